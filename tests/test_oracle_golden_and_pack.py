@@ -1,0 +1,139 @@
+"""Oracle against hand-derived blocks (tests/golden/hand_blocks.json) and the
+oracle's execution-buffer writer against an independent reader of the packed
+layout (version 1).  CPU only."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from block_planner_amd import workloads as wl
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+INT4, INT8, BF16, FP16, FP32 = 0, 1, 2, 3, 4
+PAY = (32, 64, 128, 128, 256)
+
+
+def _expand(spec, fill):
+    out = np.full(64, fill, np.float64)
+    for key, v in spec.items():
+        if key == "all":
+            out[:] = v
+        elif ".." in key:
+            a, b = (int(t) for t in key.split(".."))
+            out[a:b + 1] = v
+        else:
+            out[int(key)] = v
+    return out
+
+
+def test_hand_derived_blocks(orc):
+    data = json.load(open(os.path.join(HERE, "golden", "hand_blocks.json")))
+    for blk in data["blocks"]:
+        w = _expand(blk["entries"], 0.0).astype(np.float32)
+        f = orc.pick_block(w, force=blk["force"])
+        assert f == blk["expect_format"], blk["name"]
+        Q = 7 if f == INT4 else 127
+        s, q = orc.int_quant_block(w, Q)
+        assert hex(int(np.float32(s).view(np.uint32))) == hex(int(blk["expect_scale_hex"], 16)), blk["name"]
+        np.testing.assert_array_equal(q, _expand(blk["expect_codes"], 0).astype(np.int8), blk["name"])
+
+
+# ---------------------------------------------------------------------------
+# Independent reader of the packed layout
+# ---------------------------------------------------------------------------
+def _a256(v):
+    return (v + 255) // 256 * 256
+
+
+def read_packed(buf: np.ndarray, N: int, K: int, R: int):
+    """Decode a version-1 buffer into (fmt map, W_hat as float64)."""
+    KB, T = K // 64, (N + R - 1) // R
+    nk = T * KB + 1
+    kbidx = buf[: 5 * nk * 4].view(np.uint32).reshape(5, nk)
+    counts = [int(kbidx[f, -1]) for f in range(5)]
+    o = _a256(5 * nk * 4)
+    ids_off, sc_off, pay_off = [], [], []
+    for f in range(5):
+        ids_off.append(o); o += _a256(2 * counts[f])
+    for f in range(2):
+        sc_off.append(o); o += _a256(4 * counts[f])
+    for f in range(5):
+        pay_off.append(o); o += _a256(PAY[f] * counts[f])
+    assert o == buf.size
+    fmt = np.full((N, KB), 255, np.uint8)
+    W = np.full((N, K), np.nan)
+    for f in range(5):
+        ids = buf[ids_off[f]: ids_off[f] + 2 * counts[f]].view(np.uint16)
+        for t in range(T):
+            for kb in range(KB):
+                a, b = int(kbidx[f, t * KB + kb]), int(kbidx[f, t * KB + kb + 1])
+                prev_r = -1
+                for p in range(a, b):
+                    kb_id, r = divmod(int(ids[p]), R)
+                    assert kb_id == kb and r > prev_r     # (t, kb, r) order
+                    prev_r = r
+                    n = t * R + r
+                    assert fmt[n, kb] == 255              # each block exactly once
+                    fmt[n, kb] = f
+                    raw = buf[pay_off[f] + PAY[f] * p: pay_off[f] + PAY[f] * (p + 1)]
+                    if f in (INT4, INT8):
+                        s = float(buf[sc_off[f] + 4 * p: sc_off[f] + 4 * p + 4].view(np.float32)[0])
+                        if f == INT8:
+                            q = raw.astype(np.int64) - 128
+                        else:
+                            q = np.zeros(64, np.int64)
+                            for j in range(32):
+                                e = 32 * (j // 16) + (j % 16)
+                                q[e] = (int(raw[j]) & 15) - 8
+                                q[e + 16] = (int(raw[j]) >> 4) - 8
+                        vals = q.astype(np.float64) * s
+                    elif f == BF16:
+                        vals = (raw.view(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+                    elif f == FP16:
+                        vals = raw.view(np.float16).astype(np.float64)
+                    else:
+                        vals = raw.view(np.float32).astype(np.float64)
+                    W[n, kb * 64:(kb + 1) * 64] = vals
+    return fmt, W
+
+
+@pytest.mark.parametrize("R", [4, 16])
+def test_pack_round_trip_small_weight(orc, R):
+    """Reading the oracle's buffer back gives the plan and the dequantised
+    weights exactly; catches a wrong nibble order, a wrong code bias, a
+    misplaced region or a wrong block order."""
+    W = wl.small_weight()
+    rng = np.random.default_rng(7)
+    fmt = orc.plan(W)
+    # mix in every format so all regions are populated
+    fmt2 = fmt.copy()
+    pick = rng.random(fmt.shape) < 0.3
+    fmt2[pick] = rng.integers(0, 5, size=int(pick.sum()))
+    for f in (fmt, fmt2):
+        buf = orc.pack(W, f, R)
+        fmt_back, W_back = read_packed(buf, 256, 256, R)
+        np.testing.assert_array_equal(fmt_back, f)
+        np.testing.assert_array_equal(W_back, orc.dequant(W, f))
+
+
+def test_pack_ragged_rows(orc):
+    """N not a multiple of the row tile: the last tile has fewer rows."""
+    rng = np.random.default_rng(8)
+    W = (rng.normal(size=(37, 192)) * 0.05).astype(np.float32)
+    fmt = rng.integers(0, 5, size=(37, 3)).astype(np.uint8)
+    buf = orc.pack(W, fmt, 16)
+    fmt_back, W_back = read_packed(buf, 37, 192, 16)
+    np.testing.assert_array_equal(fmt_back, fmt)
+    np.testing.assert_array_equal(W_back, orc.dequant(W, fmt))
+
+
+def test_pack_size_closed_form(orc):
+    """bytes = aligned index table + aligned ids + aligned scales + aligned payloads."""
+    for (N, K, R, c) in [(256, 256, 16, [10, 500, 3, 1, 510]), (4096, 4096, 16, [0, 200000, 0, 0, 62144])]:
+        T, KB = (N + R - 1) // R, K // 64
+        want = _a256(5 * (T * KB + 1) * 4) + sum(_a256(2 * v) for v in c) + \
+            sum(_a256(4 * v) for v in c[:2]) + sum(_a256(p * v) for p, v in zip(PAY, c))
+        size, offs = orc.pack_layout(N, K, R, c)
+        assert size == want
+        assert all(o % 256 == 0 for o in offs)
