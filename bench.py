@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused mixed-format GEMV on the 4096-wide, depth-4 MLP.
+
+One step = one forward of the MLP (four Linear(4096, 4096) + ReLU layers, no
+bias, bfloat16 activations, batch 1) through ``ht_mlp_forward`` over packed
+execution buffers.  The weights are seeded synthetic Student-t draws (see
+``block_planner_amd.workloads.mlp_weight``), planned with the default
+thresholds and packed once before timing.
+
+Cache hygiene: one packed MLP is ~125 MB and would sit in the 256 MB
+Infinity Cache if the same copy were reused, so the timed loop rotates over
+``--copies`` independently packed copies (6 x 125 MB by default) and reads
+from HBM.  A warm-cache figure (one copy, no rotation) is reported separately.
+
+Reported value: algorithmic bytes per step / time per step, where a layer's
+algorithmic bytes are, per block, its payload + scale + one format-map byte
+(INT4 37, INT8 69, BF16/FP16 129, FP32 257), plus the input activations
+(2 bytes each) and the output (2 bytes for bfloat16 hidden layers, 4 for the
+fp32 last layer).
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, 8 TB/s
+PAY = (32, 64, 128, 128, 256)   # payload bytes per block
+SCALE = (4, 4, 0, 0, 0)
+
+
+def layer_bytes(counts, M, K, N, out_bytes):
+    w = sum(c * (p + s + 1) for c, p, s in zip(counts, PAY, SCALE))
+    return w + 2 * M * K + out_bytes * M * N
+
+
+def traffic_entry(kernel_src: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "gemv_mlp4096_m1_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+        sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+        if d.get("source_sha256") != sha:
+            return None
+        return d.get("hbm_bytes_per_launch")
+    except Exception:
+        return None
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=240)
+    ap.add_argument("--warmup", type=int, default=24)
+    ap.add_argument("--copies", type=int, default=6)
+    ap.add_argument("--cpu-steps", type=int, default=20, help="oracle MLP forwards timed for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["all", "gemv"], default="all",
+                    help="'gemv': only the per-layer GEMV loop (for counter runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus must be 1).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from block_planner_amd import api
+    from block_planner_amd import binding as B
+    from block_planner_amd import workloads as wl
+
+    B.load()   # fails loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    D, L = wl.MLP_DIM, wl.MLP_DEPTH
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    log("generating weights")
+    Ws_host = [wl.mlp_weight(l) for l in range(L)]
+    Ws = [torch.from_numpy(W).to(dev) for W in Ws_host]
+
+    def timed(fn, reps):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record(stream)
+        for i in range(reps):
+            fn(i)
+        e.record(stream)
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps / 1e3   # seconds per rep
+
+    # ---- planner ---------------------------------------------------------
+    log("planner")
+    fmts = [api.plan(W) for W in Ws]
+    torch.cuda.synchronize()
+    plan_reps = 10
+    t_plan = timed(lambda i: [B.ht_plan(Ws[l], fmts[l]) for l in range(L)], plan_reps)
+    plan_bytes = L * (4 * D * D + D * D // 64)
+    counts = [api.counts(f) for f in fmts]
+
+    # ---- packer ----------------------------------------------------------
+    log("packer")
+    copies = [[api.pack(Ws[l], fmts[l], row_tile=16, cnt=counts[l]) for l in range(L)]
+              for _ in range(max(1, args.copies))]
+    torch.cuda.synchronize()
+    scratch = [api.pack(Ws[l], fmts[l], row_tile=16, cnt=counts[l]) for l in range(L)]
+    t_pack = timed(lambda i: [B.ht_pack(Ws[l], fmts[l], 16, counts[l], scratch[l].buf) for l in range(L)], 5)
+    pack_bytes = sum(4 * D * D + D * D // 64 + sum(c * (p + s) for c, p, s in zip(counts[l], PAY, SCALE))
+                     for l in range(L))
+    del scratch
+    if args.only == "all":
+        del Ws   # inference-only: the fp32 masters are not needed any more
+        torch.cuda.empty_cache()
+
+    # ---- inputs ----------------------------------------------------------
+    def xbf(M):
+        bits = wl.to_bf16_bits(wl.mlp_activation(M))
+        return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    x1, x32 = xbf(1), xbf(32)
+    C = len(copies)
+    ws = api.workspace(max(B.ht_mlp_workspace([p.desc for p in copies[0]], 32),
+                           B.ht_linear_workspace(copies[0][0].desc, 32)), dev)
+    y1 = torch.empty((1, D), dtype=torch.float32, device=dev)
+    y32 = torch.empty((32, D), dtype=torch.float32, device=dev)
+    descs = [[p.desc for p in cp] for cp in copies]
+
+    def mlp_fn(x, y, rotate=True):
+        def f(i):
+            B.ht_mlp_forward(descs[i % C if rotate else 0], x, y, ws=ws)
+        return f
+
+    def graph_of(fn, n):
+        """Capture n calls fn(0..n-1) into one HIP graph (launches only: the
+        library records no memset or allocation)."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn(i)
+        return g
+
+    def replay_timed(g, reps, warm):
+        for _ in range(warm):
+            g.replay()
+        return timed(lambda i: g.replay(), reps)   # seconds per replay
+
+    step_bytes1 = sum(layer_bytes(counts[l], 1, D, D, 2 if l + 1 < L else 4) for l in range(L))
+    step_bytes32 = sum(layer_bytes(counts[l], 32, D, D, 2 if l + 1 < L else 4) for l in range(L))
+    G = 4 * C                              # forwards per graph
+    reps = max(1, -(-args.steps // G))
+    steps = reps * G                       # exactly this many steps are timed
+
+    # eager reference output for the replay check
+    mlp_fn(x1, y1)(0)
+    torch.cuda.synchronize()
+    y_eager = y1.clone()
+
+    # ---- roofline leg: per-launch duration of the GEMV kernel ------------
+    # G back-to-back single-layer launches per graph, replayed; events on the
+    # launch stream bracket the replays
+    log("gemv per-launch timing")
+    lin_bytes = [layer_bytes(counts[l], 1, D, D, 4) for l in range(L)]
+    glin = graph_of(lambda i: B.ht_linear_forward(descs[(i // L) % C][i % L], x1, y1, ws=ws), G)
+    t_rep = replay_timed(glin, max(1, -(-args.steps * L // G)), max(1, args.warmup // G))
+    avg_dur = t_rep / G
+    avg_lin_bytes = sum(lin_bytes) / L
+    gemv_gbs = avg_lin_bytes / avg_dur / 1e9
+    del glin
+    if args.only == "gemv":
+        print(json.dumps({"kernel": "gemv_kernel<1>", "avg_launch_us": avg_dur * 1e6,
+                          "algorithmic_bytes_per_launch": avg_lin_bytes, "GBps": gemv_gbs}))
+        return 0
+
+    # ---- timed MLP steps (the reported value) ----------------------------
+    log("mlp timed loop")
+    g1 = graph_of(mlp_fn(x1, y1), G)
+    t_step = replay_timed(g1, reps, max(1, args.warmup // G)) / G
+    torch.cuda.synchronize()
+    replay_ok = bool(torch.equal(y1, y_eager))   # every copy holds the same weights
+    value = step_bytes1 / t_step / 1e9
+
+    log("mlp batch 32, warm cache")
+    g32 = graph_of(mlp_fn(x32, y32), C)
+    t32 = replay_timed(g32, max(2, reps // 4), 1) / C
+    gw = graph_of(mlp_fn(x1, y1, rotate=False), G)
+    t_warm = replay_timed(gw, reps, 1) / G
+    del g1, g32, gw
+
+    # ---- CPU baseline: the oracle as it stands ----------------------------
+    cpu = None
+    if not args.no_cpu_baseline and args.cpu_steps > 0:
+        log("cpu baseline (oracle)")
+        import oracle
+        fm_host = [f.cpu().numpy() for f in fmts]
+        xb = wl.to_bf16_bits(wl.mlp_activation(1))
+        oracle.mlp(Ws_host, fm_host, xb)   # load + warm
+        t0 = time.perf_counter()
+        for _ in range(args.cpu_steps):
+            oracle.mlp(Ws_host, fm_host, xb)
+        t_cpu = (time.perf_counter() - t0) / args.cpu_steps
+        cpu = {"value": round(step_bytes1 / t_cpu / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{args.cpu_steps} forwards of the same 4-layer 4096 MLP at batch 1 "
+                         f"(C oracle, fp64, single thread; {t_cpu * 1e3:.1f} ms per forward; "
+                         f"host has {os.cpu_count()} logical CPUs)"}
+
+    mix = [sum(c[f] for c in counts) / sum(sum(c) for c in counts) for f in range(5)]
+    kernel_src = os.path.join(ROOT, "block_planner_amd", "csrc", "linear.hip")
+    out = {
+        "metric": "fused mixed-format GEMV GB/s (% of HBM peak) on 4096x4096 MLP; planner GB/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32-accumulate over int4/int8/bf16/fp16/fp32 weights, bf16 activations",
+        "data": "synthetic (seeded Student-t weights, N(0,1) activations)",
+        "config": {"workload": "4-layer MLP, Linear(4096,4096)+ReLU x4, no bias, batch 1, bf16 activations, "
+                               "default eps (0.08/0.01/0/0), 64-wide K-blocks, row tile 16",
+                   "global_batch": 1, "hidden": D, "layers": L, "parallelism": "none (1 GPU)",
+                   "rotating_copies": C},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(gemv_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gemv_gbs / HBM_PEAK_GBS, 4), "traffic": traffic_entry(kernel_src),
+                     "kernel": "gemv_kernel<1>", "avg_launch_us": round(avg_dur * 1e6, 3),
+                     "algorithmic_bytes_per_launch": int(avg_lin_bytes)},
+        "cpu_baseline": cpu,
+        "planner_GBps": round(plan_bytes / t_plan / 1e9, 2),
+        "planner_pct_hbm_peak": round(100 * plan_bytes / t_plan / 1e9 / HBM_PEAK_GBS, 2),
+        "packer_GBps": round(pack_bytes / t_pack / 1e9, 2),
+        "mlp_batch32_GBps": round(step_bytes32 / t32 / 1e9, 2),
+        "mlp_batch32_ms_per_step": round(t32 * 1e3, 4),
+        "mlp_batch1_warm_cache_GBps": round(step_bytes1 / t_warm / 1e9, 2),
+        "graph_replay_matches_eager": replay_ok,
+        "format_mix": {n: round(v, 5) for n, v in zip(("INT4", "INT8", "BF16", "FP16", "FP32"), mix)},
+        "packed_MB_per_mlp": round(sum(p.nbytes for p in copies[0]) / 1e6, 2),
+    }
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

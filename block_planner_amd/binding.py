@@ -1,0 +1,194 @@
+"""ctypes binding of ``libht.so`` -- argument marshalling only.
+
+Every function named ``ht_*`` here forwards to the C entry point of the same
+name declared in ``include/ht.h``; tensors are passed as raw device pointers
+(``tensor.data_ptr()``) and streams as ``hipStream_t`` handles (by default
+torch's current stream).  A non-OK status raises :class:`HTError`.
+
+The library must be built in-tree (``python -m block_planner_amd.build`` or
+``__graft_entry__.build()``); there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libht.so")
+
+HT_INT4, HT_INT8, HT_BF16, HT_FP16, HT_FP32 = range(5)
+HT_ACT_NONE, HT_ACT_RELU = 0, 1
+HT_PATH_AUTO, HT_PATH_GEMV = 0, 1
+HT_LAYOUT_VERSION = 1
+STATUS = {0: "HT_OK", 1: "HT_EINVAL", 2: "HT_ESHAPE", 3: "HT_EALIGN", 4: "HT_ESMALL", 5: "HT_EHIP"}
+
+# Every symbol include/ht.h declares.
+EXPORTS = ("ht_status_string", "ht_plan_params_default", "ht_plan", "ht_plan_counts",
+           "ht_pack_bytes", "ht_pack", "ht_linear_workspace", "ht_linear_forward",
+           "ht_mlp_workspace", "ht_mlp_forward")
+
+
+class HTError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        self.code = code
+        super().__init__(f"{fn} failed: {STATUS.get(code, code)} ({ht_status_string(code)})")
+
+
+class PlanParams(ctypes.Structure):
+    _fields_ = [("eps_int4", ctypes.c_double), ("eps_int8", ctypes.c_double),
+                ("eps_bf16", ctypes.c_double), ("eps_fp16", ctypes.c_double),
+                ("prefer_bf16", ctypes.c_int32), ("force_format", ctypes.c_int32)]
+
+
+class PackedWeight(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int64), ("K", ctypes.c_int64), ("row_tile", ctypes.c_int64),
+                ("n_tiles", ctypes.c_int64), ("counts", ctypes.c_int64 * 5),
+                ("off_kbidx", ctypes.c_uint64), ("off_ids", ctypes.c_uint64 * 5),
+                ("off_scale", ctypes.c_uint64 * 2), ("off_payload", ctypes.c_uint64 * 5),
+                ("bytes", ctypes.c_uint64), ("layout_version", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("base", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the in-tree library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it first (python -m block_planner_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, I32, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_double
+    St = ctypes.c_int
+    lib.ht_status_string.restype = ctypes.c_char_p
+    lib.ht_status_string.argtypes = [St]
+    lib.ht_plan_params_default.restype = None
+    lib.ht_plan_params_default.argtypes = [ctypes.POINTER(PlanParams)]
+    lib.ht_plan.restype = St
+    lib.ht_plan.argtypes = [P, I64, I64, I64, ctypes.POINTER(PlanParams), P, P]
+    lib.ht_plan_counts.restype = St
+    lib.ht_plan_counts.argtypes = [P, I64, I64, P, P]
+    lib.ht_pack_bytes.restype = St
+    lib.ht_pack_bytes.argtypes = [I64, I64, I64, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_size_t)]
+    lib.ht_pack.restype = St
+    lib.ht_pack.argtypes = [P, I64, I64, I64, P, I64, ctypes.POINTER(ctypes.c_int64), P, ctypes.c_size_t,
+                            ctypes.POINTER(PackedWeight), P]
+    lib.ht_linear_workspace.restype = St
+    lib.ht_linear_workspace.argtypes = [ctypes.POINTER(PackedWeight), I64, I32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.ht_linear_forward.restype = St
+    lib.ht_linear_forward.argtypes = [ctypes.POINTER(PackedWeight), P, I64, I64, P, I64, I32, I32, P,
+                                      ctypes.c_size_t, P]
+    lib.ht_mlp_workspace.restype = St
+    lib.ht_mlp_workspace.argtypes = [ctypes.POINTER(ctypes.POINTER(PackedWeight)), I32, I64,
+                                     ctypes.POINTER(ctypes.c_size_t)]
+    lib.ht_mlp_forward.restype = St
+    lib.ht_mlp_forward.argtypes = [ctypes.POINTER(ctypes.POINTER(PackedWeight)), I32, P, I64, I64, P, I64, P, P,
+                                   ctypes.c_size_t, P]
+    _lib = lib
+    return lib
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn: str, code: int) -> None:
+    if code != 0:
+        raise HTError(fn, code)
+
+
+def ht_status_string(code: int) -> str:
+    return load().ht_status_string(code).decode()
+
+
+def ht_plan_params_default() -> PlanParams:
+    p = PlanParams()
+    load().ht_plan_params_default(ctypes.byref(p))
+    return p
+
+
+def ht_plan(W, fmt_map, params: PlanParams | None = None, stream=None, N=None, K=None, ldw=None) -> None:
+    """W: fp32 [N, K] (row stride ldw); fmt_map: uint8 [N, K/64]."""
+    N = W.shape[0] if N is None else N
+    K = W.shape[1] if K is None else K
+    ldw = W.stride(0) if ldw is None else ldw
+    pp = ctypes.byref(params) if params is not None else None
+    _check("ht_plan", load().ht_plan(_ptr(W), N, K, ldw, pp, _ptr(fmt_map), _stream(stream)))
+
+
+def ht_plan_counts(fmt_map, counts5, N=None, K=None, stream=None) -> None:
+    N = fmt_map.shape[0] if N is None else N
+    K = fmt_map.shape[1] * 64 if K is None else K
+    _check("ht_plan_counts", load().ht_plan_counts(_ptr(fmt_map), N, K, _ptr(counts5), _stream(stream)))
+
+
+def ht_pack_bytes(N: int, K: int, row_tile: int, counts) -> int:
+    c = (ctypes.c_int64 * 5)(*[int(v) for v in counts])
+    out = ctypes.c_size_t(0)
+    _check("ht_pack_bytes", load().ht_pack_bytes(N, K, row_tile, c, ctypes.byref(out)))
+    return out.value
+
+
+def ht_pack(W, fmt_map, row_tile: int, counts, buf, stream=None, N=None, K=None, ldw=None,
+            buf_bytes=None) -> PackedWeight:
+    N = W.shape[0] if N is None else N
+    K = W.shape[1] if K is None else K
+    ldw = W.stride(0) if ldw is None else ldw
+    c = (ctypes.c_int64 * 5)(*[int(v) for v in counts])
+    desc = PackedWeight()
+    nbytes = buf.numel() * buf.element_size() if buf_bytes is None else buf_bytes
+    _check("ht_pack", load().ht_pack(_ptr(W), N, K, ldw, _ptr(fmt_map), row_tile, c, _ptr(buf), nbytes,
+                                     ctypes.byref(desc), _stream(stream)))
+    return desc
+
+
+def ht_linear_workspace(desc: PackedWeight, M: int, path: int = HT_PATH_AUTO) -> int:
+    out = ctypes.c_size_t(0)
+    _check("ht_linear_workspace", load().ht_linear_workspace(ctypes.byref(desc), M, path, ctypes.byref(out)))
+    return out.value
+
+
+def ht_linear_forward(desc: PackedWeight, x, y, act: int = HT_ACT_NONE, path: int = HT_PATH_AUTO, ws=None,
+                      stream=None, M=None, ldx=None, ldy=None, ws_bytes=None) -> None:
+    M = x.shape[0] if M is None else M
+    ldx = x.stride(0) if ldx is None else ldx
+    ldy = y.stride(0) if ldy is None else ldy
+    wsb = (ws.numel() * ws.element_size() if ws is not None else 0) if ws_bytes is None else ws_bytes
+    _check("ht_linear_forward", load().ht_linear_forward(ctypes.byref(desc), _ptr(x), M, ldx, _ptr(y), ldy, act,
+                                                         path, _ptr(ws), wsb, _stream(stream)))
+
+
+def _desc_array(descs):
+    arr = (ctypes.POINTER(PackedWeight) * len(descs))(*[ctypes.pointer(d) for d in descs])
+    return arr
+
+
+def ht_mlp_workspace(descs, M: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check("ht_mlp_workspace", load().ht_mlp_workspace(_desc_array(descs), len(descs), M, ctypes.byref(out)))
+    return out.value
+
+
+def ht_mlp_forward(descs, x, y, act_dump=None, ws=None, stream=None, M=None, ldx=None, ldy=None,
+                   ws_bytes=None) -> None:
+    M = x.shape[0] if M is None else M
+    ldx = x.stride(0) if ldx is None else ldx
+    ldy = y.stride(0) if ldy is None else ldy
+    wsb = (ws.numel() * ws.element_size() if ws is not None else 0) if ws_bytes is None else ws_bytes
+    _check("ht_mlp_forward", load().ht_mlp_forward(_desc_array(descs), len(descs), _ptr(x), M, ldx, _ptr(y), ldy,
+                                                   _ptr(act_dump), _ptr(ws), wsb, _stream(stream)))

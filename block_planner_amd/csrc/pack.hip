@@ -1,0 +1,339 @@
+// pack.hip -- compile a format map into execution buffers (HyperTensor 1.0.1
+// page, intro: the planner's format map "is compiled into optimized execution
+// buffers"; "Key Features": inference-only mode, which drops the fp32 master
+// weights -- after packing, the buffers are all the linear needs).
+//
+// Three kernels on the caller's stream:
+//   1. column counts: per (row tile t, K-block kb) and format, the number of
+//      rows of the tile holding that format -> kbidx[f][t*KB + kb];
+//   2. exclusive scan of each format's counts in (t, kb) order (one
+//      workgroup per format), total at kbidx[f][T*KB];
+//   3. scatter: one quad of lanes per block, in (t, kb, r) order; a block's
+//      position is kbidx[f][t*KB+kb] plus its rank among the column's rows of
+//      the same format (wave ballot).  Codes and scales are recomputed from W
+//      with the planner's exact arithmetic.  Stores are 16 bytes per lane.
+// A fourth tiny kernel zeroes the alignment padding between regions so that
+// every byte of the buffer is defined.
+#include "quant.h"
+
+namespace ht {
+
+struct PackArgs {
+    const float *W;
+    const uint8_t *fmt;
+    uint8_t *buf;
+    int64_t ldw;
+    uint32_t N, KB, R, lgR, T, nk;   // nk = T*KB + 1
+    FastDiv div_kb;
+    uint64_t off_kbidx, off_ids[5], off_scale[2], off_pay[5];
+    uint32_t counts[5];
+};
+
+__global__ __launch_bounds__(256) void pack_count_kernel(PackArgs a) {
+    const uint32_t c = blockIdx.x * 256u + threadIdx.x;   // column t*KB + kb
+    if (c >= a.T * a.KB) return;
+    const uint32_t t = fastdiv(c, a.div_kb);
+    const uint32_t kb = c - t * a.KB;
+    uint32_t cnt[5] = {0, 0, 0, 0, 0};
+    for (uint32_t r = 0; r < a.R; ++r) {
+        const uint32_t n = t * a.R + r;
+        if (n >= a.N) break;
+        const uint32_t f = a.fmt[uint64_t(n) * a.KB + kb];
+#pragma unroll
+        for (int g = 0; g < 5; ++g) cnt[g] += (f == uint32_t(g)) ? 1u : 0u;
+    }
+    uint32_t *kbidx = reinterpret_cast<uint32_t *>(a.buf + a.off_kbidx);
+#pragma unroll
+    for (int g = 0; g < 5; ++g) kbidx[uint64_t(g) * a.nk + c] = cnt[g];
+}
+
+// In-place exclusive scan of kbidx[f][0 .. L) (L = T*KB), total into [L].
+// 1024 threads, 4 entries per thread per pass, a running carry across passes.
+__global__ __launch_bounds__(1024) void pack_scan_kernel(PackArgs a) {
+    __shared__ uint32_t wsum[16];
+    __shared__ uint32_t carry_s;
+    const uint32_t f = blockIdx.x;
+    uint32_t *v = reinterpret_cast<uint32_t *>(a.buf + a.off_kbidx) + uint64_t(f) * a.nk;
+    const uint32_t L = a.T * a.KB;
+    const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (threadIdx.x == 0) carry_s = 0;
+    __syncthreads();
+    for (uint32_t base = 0; base < L; base += 4096) {
+        const uint32_t i0 = base + threadIdx.x * 4;
+        uint32_t e[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) e[j] = (i0 + j < L) ? v[i0 + j] : 0u;
+        const uint32_t local = e[0] + e[1] + e[2] + e[3];
+        // inclusive scan of `local` across the wave
+        uint32_t inc = local;
+        for (int off = 1; off < 64; off <<= 1) {
+            uint32_t o = __shfl_up(inc, off);
+            if (lane >= uint32_t(off)) inc += o;
+        }
+        if (lane == 63) wsum[wave] = inc;
+        __syncthreads();
+        uint32_t wprefix = 0;
+        for (uint32_t k = 0; k < wave; ++k) wprefix += wsum[k];
+        const uint32_t carry = carry_s;
+        uint32_t run = carry + wprefix + inc - local;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (i0 + j < L) v[i0 + j] = run;
+            run += e[j];
+        }
+        __syncthreads();
+        if (threadIdx.x == 1023) carry_s = run;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) v[L] = carry_s;
+}
+
+__global__ __launch_bounds__(256) void pack_scatter_kernel(PackArgs a) {
+    const uint32_t tid = blockIdx.x * 256u + threadIdx.x;
+    const uint32_t g = tid >> 2;                 // slot in (t, kb, r) order
+    const int part = int(threadIdx.x & 3);
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t col = g >> a.lgR;             // t*KB + kb
+    const uint32_t r = g & (a.R - 1u);
+    const uint32_t t = fastdiv(col, a.div_kb);
+    const uint32_t kb = col - t * a.KB;
+    const uint32_t n = t * a.R + r;
+    const bool valid = col < a.T * a.KB && n < a.N;
+    const uint32_t f = valid ? uint32_t(a.fmt[uint64_t(n) * a.KB + kb]) : 255u;
+
+    // rank among the column's earlier rows with the same format
+    uint64_t m[5];
+#pragma unroll
+    for (int k = 0; k < 5; ++k) m[k] = __ballot(part == 0 && f == uint32_t(k));
+    const uint32_t slot = lane >> 2;                     // slot within the wave
+    const uint32_t cstart = slot & ~(a.R - 1u);          // first slot of the column (R divides 16)
+    const uint64_t before = ((uint64_t(1) << (4 * slot)) - 1u) & ~((uint64_t(1) << (4 * cstart)) - 1u);
+    uint64_t mine = 0;
+#pragma unroll
+    for (int k = 0; k < 5; ++k) mine = (f == uint32_t(k)) ? m[k] : mine;
+    const uint32_t rank = uint32_t(__popcll(mine & before));
+
+    if (f > 4u) return;                                  // whole quad leaves together
+    const uint32_t *kbidx = reinterpret_cast<const uint32_t *>(a.buf + a.off_kbidx);
+    const uint32_t pos = kbidx[uint64_t(f) * a.nk + col] + rank;
+    if (pos >= a.counts[f]) return;                      // inconsistent counts: write nothing
+
+    float w[kPerLane];
+    const float *src = a.W + int64_t(n) * a.ldw + kb * 64u + part * 16;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const f32x4 v = ld_stream_f4(src + 4 * j);
+        w[4 * j] = v.x; w[4 * j + 1] = v.y; w[4 * j + 2] = v.z; w[4 * j + 3] = v.w;
+    }
+    if (part == 0) {
+        uint16_t id = uint16_t(kb * a.R + r);
+        *reinterpret_cast<uint16_t *>(a.buf + a.off_ids[f] + 2ull * pos) = id;
+    }
+    uint8_t *pay = a.buf + a.off_pay[f];
+    if (f <= 1u) {
+        const float Qf = f == 0u ? 7.0f : 127.0f;
+        const float amax = block_absmax(w);
+        float s = amax / Qf;
+        float q[kPerLane];
+        const uint32_t nf = block_nonfinite(w);
+        if (nf) {
+            s = (nf & 1u) ? __uint_as_float(0x7FC00000u) : __uint_as_float(0x7F800000u);
+#pragma unroll
+            for (int i = 0; i < kPerLane; ++i) q[i] = 0.0f;
+        } else {
+            lane_codes(w, s, Qf, q);
+        }
+        if (part == 0) *reinterpret_cast<float *>(a.buf + a.off_scale[f] + 4ull * pos) = s;
+        uint32_t wd[4];
+        if (f == 1u) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                wd[j] = (uint32_t(int(q[4 * j]) & 0xFF)) | (uint32_t(int(q[4 * j + 1]) & 0xFF) << 8) |
+                        (uint32_t(int(q[4 * j + 2]) & 0xFF) << 16) | (uint32_t(int(q[4 * j + 3]) & 0xFF) << 24);
+            *reinterpret_cast<uint4 *>(pay + 64ull * pos + 16 * part) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+        } else {
+            // byte i of the 16-byte half (p/2) takes entry i of this lane in
+            // its low nibble (even p) or high nibble (odd p)
+            const int sh = (part & 1) * 4;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                wd[j] = ((uint32_t(int(q[4 * j]) & 0xF)) << sh) | ((uint32_t(int(q[4 * j + 1]) & 0xF)) << (8 + sh)) |
+                        ((uint32_t(int(q[4 * j + 2]) & 0xF)) << (16 + sh)) |
+                        ((uint32_t(int(q[4 * j + 3]) & 0xF)) << (24 + sh));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) wd[j] |= dpp_u32<kDppXor1>(wd[j]);
+            if ((part & 1) == 0)
+                *reinterpret_cast<uint4 *>(pay + 32ull * pos + 16 * (part >> 1)) =
+                    make_uint4(wd[0], wd[1], wd[2], wd[3]);
+        }
+    } else if (f == 2u || f == 3u) {
+        uint32_t hv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            uint32_t lo, hi;
+            if (f == 2u) {
+                lo = f32_to_bf16_rne(w[2 * j]);
+                hi = f32_to_bf16_rne(w[2 * j + 1]);
+            } else {
+                lo = __builtin_bit_cast(uint16_t, _Float16(w[2 * j]));
+                hi = __builtin_bit_cast(uint16_t, _Float16(w[2 * j + 1]));
+            }
+            hv[j] = lo | (hi << 16);
+        }
+        uint4 *dst = reinterpret_cast<uint4 *>(pay + 128ull * pos + 32 * part);
+        dst[0] = make_uint4(hv[0], hv[1], hv[2], hv[3]);
+        dst[1] = make_uint4(hv[4], hv[5], hv[6], hv[7]);
+    } else {
+        float4 *dst = reinterpret_cast<float4 *>(pay + 256ull * pos + 64 * part);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dst[j] = make_float4(w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]);
+    }
+}
+
+struct PadArgs {
+    uint8_t *buf;
+    uint64_t start[13];
+    uint32_t len[13];
+};
+
+__global__ __launch_bounds__(256) void pack_pad_kernel(PadArgs p) {
+    const int k = blockIdx.x;
+    for (uint32_t i = threadIdx.x; i < p.len[k]; i += 256) p.buf[p.start[k] + i] = 0;
+}
+
+}  // namespace ht
+
+using namespace ht;
+
+namespace {
+
+struct Layout {
+    uint64_t kbidx, ids[5], scale[2], pay[5], end[12], total;
+    uint64_t used[12];   // bytes in use at the start of each region
+};
+
+ht_status layout_of(int64_t N, int64_t K, int64_t R, const int64_t c[5], Layout *L) {
+    if (N <= 0 || K <= 0 || K % kBlockK != 0) return HT_ESHAPE;
+    if (!(R == 1 || R == 2 || R == 4 || R == 8 || R == 16)) return HT_ESHAPE;
+    const int64_t KB = K / kBlockK;
+    if (KB * R > 65536) return HT_ESHAPE;
+    const int64_t T = (N + R - 1) / R;
+    if (T * KB + 1 > (int64_t(1) << 31)) return HT_ESHAPE;
+    int64_t tot = 0;
+    for (int f = 0; f < 5; ++f) {
+        if (c[f] < 0) return HT_EINVAL;
+        tot += c[f];
+    }
+    if (tot != N * KB) return HT_EINVAL;
+    uint64_t o = 0;
+    int k = 0;
+    L->kbidx = o; L->used[k++] = uint64_t(5) * uint64_t(T * KB + 1) * 4u; o += align256(L->used[0]);
+    for (int f = 0; f < 5; ++f) { L->ids[f] = o; L->used[k++] = 2u * uint64_t(c[f]); o += align256(2u * uint64_t(c[f])); }
+    for (int f = 0; f < 2; ++f) { L->scale[f] = o; L->used[k++] = 4u * uint64_t(c[f]); o += align256(4u * uint64_t(c[f])); }
+    for (int f = 0; f < 5; ++f) {
+        L->pay[f] = o;
+        L->used[k++] = uint64_t(pay_bytes(f)) * uint64_t(c[f]);
+        o += align256(uint64_t(pay_bytes(f)) * uint64_t(c[f]));
+    }
+    L->total = o;
+    return HT_OK;
+}
+
+}  // namespace
+
+extern "C" ht_status ht_pack_bytes(int64_t N, int64_t K, int64_t row_tile, const int64_t counts5[5],
+                                   size_t *bytes) {
+    if (!counts5 || !bytes) return HT_EINVAL;
+    Layout L;
+    ht_status st = layout_of(N, K, row_tile, counts5, &L);
+    if (st != HT_OK) return st;
+    *bytes = size_t(L.total);
+    return HT_OK;
+}
+
+extern "C" ht_status ht_pack(const float *W, int64_t N, int64_t K, int64_t ldw, const uint8_t *fmt_map,
+                             int64_t row_tile, const int64_t counts5[5], void *buf, size_t buf_bytes,
+                             ht_packed_weight *desc, ht_stream stream) {
+    if (!W || !fmt_map || !counts5 || !buf || !desc) return HT_EINVAL;
+    if (ldw < K) return HT_ESHAPE;
+    Layout L;
+    ht_status st = layout_of(N, K, row_tile, counts5, &L);
+    if (st != HT_OK) return st;
+    if ((reinterpret_cast<uintptr_t>(W) & 15u) || (ldw % 4) || (reinterpret_cast<uintptr_t>(buf) & 255u))
+        return HT_EALIGN;
+    if (buf_bytes < L.total) return HT_ESMALL;
+    const int64_t KB = K / kBlockK;
+    const int64_t R = row_tile;
+    const int64_t T = (N + R - 1) / R;
+
+    PackArgs a;
+    a.W = W;
+    a.fmt = fmt_map;
+    a.buf = static_cast<uint8_t *>(buf);
+    a.ldw = ldw;
+    a.N = uint32_t(N);
+    a.KB = uint32_t(KB);
+    a.R = uint32_t(R);
+    a.lgR = uint32_t(__builtin_ctzll(uint64_t(R)));
+    a.T = uint32_t(T);
+    a.nk = uint32_t(T * KB + 1);
+    a.div_kb = make_fastdiv(uint32_t(KB));
+    a.off_kbidx = L.kbidx;
+    for (int f = 0; f < 5; ++f) { a.off_ids[f] = L.ids[f]; a.off_pay[f] = L.pay[f]; a.counts[f] = uint32_t(counts5[f]); }
+    for (int f = 0; f < 2; ++f) a.off_scale[f] = L.scale[f];
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const uint32_t cols = uint32_t(T * KB);
+    hipLaunchKernelGGL(pack_count_kernel, dim3((cols + 255) / 256), dim3(256), 0, s, a);
+    HT_LAUNCH_CHECK();
+    hipLaunchKernelGGL(pack_scan_kernel, dim3(5), dim3(1024), 0, s, a);
+    HT_LAUNCH_CHECK();
+    const uint64_t slots = uint64_t(cols) * uint64_t(R);
+    const uint64_t grid = (slots * 4 + 255) / 256;
+    if (grid > 0xFFFFFFFFull || slots * 4 > 0xFFFFFFFFull) return HT_ESHAPE;
+    hipLaunchKernelGGL(pack_scatter_kernel, dim3(uint32_t(grid)), dim3(256), 0, s, a);
+    HT_LAUNCH_CHECK();
+
+    PadArgs p;
+    p.buf = a.buf;
+    const uint64_t starts[12] = {L.kbidx, L.ids[0], L.ids[1], L.ids[2], L.ids[3], L.ids[4],
+                                 L.scale[0], L.scale[1], L.pay[0], L.pay[1], L.pay[2], L.pay[3]};
+    // region k ends where region k+1 starts; the last (FP32 payload) ends at total
+    const uint64_t nexts[12] = {L.ids[0], L.ids[1], L.ids[2], L.ids[3], L.ids[4], L.scale[0],
+                                L.scale[1], L.pay[0], L.pay[1], L.pay[2], L.pay[3], L.pay[4]};
+    int k = 0;
+    for (int i = 0; i < 12; ++i) {
+        p.start[k] = starts[i] + L.used[i];
+        p.len[k] = uint32_t(nexts[i] - p.start[k]);
+        if (p.len[k]) ++k;
+    }
+    // FP32 payload tail
+    uint64_t used_last = uint64_t(pay_bytes(4)) * uint64_t(counts5[4]);
+    if (L.total - (L.pay[4] + used_last)) {
+        p.start[k] = L.pay[4] + used_last;
+        p.len[k] = uint32_t(L.total - p.start[k]);
+        ++k;
+    }
+    if (k) {
+        hipLaunchKernelGGL(pack_pad_kernel, dim3(k), dim3(256), 0, s, p);
+        HT_LAUNCH_CHECK();
+    }
+
+    desc->N = N;
+    desc->K = K;
+    desc->row_tile = R;
+    desc->n_tiles = T;
+    for (int f = 0; f < 5; ++f) {
+        desc->counts[f] = counts5[f];
+        desc->off_ids[f] = L.ids[f];
+        desc->off_payload[f] = L.pay[f];
+    }
+    desc->off_kbidx = L.kbidx;
+    desc->off_scale[0] = L.scale[0];
+    desc->off_scale[1] = L.scale[1];
+    desc->bytes = L.total;
+    desc->layout_version = HT_LAYOUT_VERSION;
+    desc->reserved = 0;
+    desc->base = buf;
+    return HT_OK;
+}

@@ -1,0 +1,199 @@
+/*
+ * ht.h -- C ABI of the MI355X (gfx950) per-block mixed-precision linear.
+ *
+ * The method (HyperTensor 1.0.1 project page): a precision planner measures
+ * the reconstruction error of each weight block and keeps the lowest format
+ * that stays safe ("What it does", "Key Features": per-block selection among
+ * INT4 / INT8 / FP16 / BF16 / FP32); the resulting format map is compiled
+ * into execution buffers and run by fused mixed-precision operators (intro
+ * paragraph).  The page's user calls map onto this ABI as follows:
+ *   scan_model(...)                    ("Convert model")  -> ht_plan
+ *   wrap_model_with_hypertensor(...)   ("Convert model")  -> ht_pack
+ *   HyperLinear(...).forward           ("Usage Example")  -> ht_linear_forward
+ *   BenchmarkMLP forward (Linear+ReLU) ("Usage Example")  -> ht_mlp_forward
+ *
+ * Conventions for every call
+ *   - Pointers are DEVICE pointers unless marked (host).
+ *   - Matrices are row-major; ld* is the row stride in elements.
+ *   - Calls only enqueue work on `stream` (a hipStream_t; NULL = the legacy
+ *     default stream) and never synchronise, except where stated.
+ *   - Every argument check runs on the host before anything is enqueued; a
+ *     failed check returns a status and enqueues nothing.  A failed HIP launch
+ *     returns HT_EHIP.  Nothing is printed and no exception crosses the ABI.
+ *   - The library allocates no device memory: the caller owns W, the format
+ *     map, the count array, the packed buffer, x, y and the workspace.
+ *   - Device pointers must be 16-byte aligned (HT_EALIGN otherwise), except
+ *     the format map and the count array (1 and 8 bytes).
+ *   - Calls are re-entrant.  Two calls that share a workspace must not
+ *     overlap in time (use one stream, or one workspace per stream).
+ */
+#ifndef HT_H
+#define HT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HT_BLOCK_K 64          /* K-block width: 64 consecutive entries of a row */
+#define HT_LAYOUT_VERSION 1
+
+typedef enum {
+    HT_INT4 = 0,  /* symmetric, fp32 scale max|w|/7,   codes in [-7, 7]     */
+    HT_INT8 = 1,  /* symmetric, fp32 scale max|w|/127, codes in [-127, 127] */
+    HT_BF16 = 2,  /* bfloat16, round to nearest even                        */
+    HT_FP16 = 3,  /* IEEE binary16, round to nearest even, subnormals kept  */
+    HT_FP32 = 4   /* original fp32 values                                   */
+} ht_format;
+
+typedef enum {
+    HT_OK = 0,
+    HT_EINVAL = 1,  /* NULL pointer, bad eps / force_format / path / act     */
+    HT_ESHAPE = 2,  /* N, K or M <= 0, K % 64 != 0, ld < width, layer mismatch,
+                       row tile not in {1,2,4,8,16}, (K/64)*row_tile > 65536  */
+    HT_EALIGN = 3,  /* a device pointer is not 16-byte aligned               */
+    HT_ESMALL = 4,  /* packed buffer or workspace smaller than required      */
+    HT_EHIP = 5     /* a HIP launch failed                                   */
+} ht_status;
+
+typedef void *ht_stream;    /* hipStream_t */
+
+/* Planner thresholds ("Convert model": eps_fp16 = eps_bf16 = 0.0 and
+ * prefer_bf16 = True are the scan's defaults).  A block may take format f when
+ * its relative L2 reconstruction error ||w - w_hat|| / ||w|| <= eps_f, tested
+ * in squared form in double: err2 <= (eps_f * eps_f) * nrm2, with err2 and
+ * nrm2 balanced pairwise sums over the block in natural order.  The block
+ * gets the first admissible format of INT4, INT8, then BF16, FP16 (FP16, BF16
+ * when prefer_bf16 is 0), then FP32.  A block holding NaN or Inf is FP32. */
+typedef struct {
+    double eps_int4;       /* default 0.08 */
+    double eps_int8;       /* default 0.01 */
+    double eps_bf16;       /* default 0.0  */
+    double eps_fp16;       /* default 0.0  */
+    int32_t prefer_bf16;   /* default 1    */
+    int32_t force_format;  /* -1 = plan (default); 0..4 = give every block this format */
+} ht_plan_params;
+
+/* Packed execution buffers of one weight W[N, K] (layout version 1).
+ * A host-side descriptor filled by ht_pack; valid while the buffer lives.
+ * Offsets are in bytes from `base`.  Layout:
+ *   R = row_tile, T = ceil(N / R), KB = K / 64.  Blocks are enumerated tile by
+ *   tile, K-block by K-block, row by row: (t, kb, r).  Each format keeps its
+ *   blocks in that order.  Regions (each 256-byte aligned):
+ *     kbidx    uint32 [5][T*KB + 1]: kbidx[f][t*KB + kb] = number of format-f
+ *              blocks before (t, kb); entry T*KB is the format's total.
+ *     ids_f    uint16 [count_f]: kb * R + r of each block.
+ *     scale_f  float  [count_f] for INT4 and INT8: the block's fp32 scale.
+ *     pay_f    [count_f][32 | 64 | 128 | 128 | 256 bytes]:
+ *              INT4: byte j holds element 32*(j/16) + j%16 in its low nibble
+ *                    and that element + 16 in its high nibble (4-bit two's
+ *                    complement codes);
+ *              INT8: byte i = code i (two's complement);
+ *              BF16, FP16: 16-bit patterns in element order;
+ *              FP32: the original 32-bit patterns. */
+typedef struct {
+    int64_t N, K;
+    int64_t row_tile;            /* R */
+    int64_t n_tiles;             /* T */
+    int64_t counts[5];           /* blocks per format */
+    uint64_t off_kbidx;
+    uint64_t off_ids[5];
+    uint64_t off_scale[2];       /* INT4, INT8 */
+    uint64_t off_payload[5];
+    uint64_t bytes;              /* total size of the packed buffer */
+    int32_t layout_version;      /* HT_LAYOUT_VERSION */
+    int32_t reserved;
+    void *base;                  /* device address of the packed buffer */
+} ht_packed_weight;
+
+enum { HT_ACT_NONE = 0, HT_ACT_RELU = 1 };
+enum { HT_PATH_AUTO = 0, HT_PATH_GEMV = 1 };
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *ht_status_string(ht_status s);
+
+/* Fill *p with the defaults listed in ht_plan_params. */
+void ht_plan_params_default(ht_plan_params *p);
+
+/* ht_plan -- the precision planner ("What it does": analyse each weight,
+ * assign the lowest safe precision; "Key Features": per-block selection).
+ *   W        fp32 [N, ldw], row-major; block (n, kb) = W[n, 64kb .. 64kb+63].
+ *   N, K     K % 64 == 0; ldw >= K.
+ *   p        (host) thresholds; NULL means the defaults.
+ *   fmt_map  uint8 [N, K/64] out: the format code (ht_format) of each block.
+ * Integer formats: s = fl32(max|w| / Q) (Q = 7 or 127, correctly rounded
+ * fp32 division); q_i = clamp(round_half_even(fl32(w_i / s)), -Q, Q); q = 0
+ * when s is 0 or not finite; w_hat_i = q_i * s.  BF16 / FP16: w_hat_i is w_i
+ * rounded to nearest even. */
+ht_status ht_plan(const float *W, int64_t N, int64_t K, int64_t ldw,
+                  const ht_plan_params *p, uint8_t *fmt_map, ht_stream stream);
+
+/* ht_plan_counts -- number of blocks per format in a format map.
+ *   counts5  int64 [5] out (device).  The caller copies it to the host to
+ *            size the packed buffer (the only host round trip of the path). */
+ht_status ht_plan_counts(const uint8_t *fmt_map, int64_t N, int64_t K,
+                         int64_t *counts5, ht_stream stream);
+
+/* ht_pack_bytes -- size of the packed buffer (host only, no GPU work).
+ *   row_tile in {1, 2, 4, 8, 16}; counts5 (host) from ht_plan_counts. */
+ht_status ht_pack_bytes(int64_t N, int64_t K, int64_t row_tile,
+                        const int64_t counts5[5], size_t *bytes);
+
+/* ht_pack -- compile a plan into execution buffers (intro paragraph: the
+ * format map "is compiled into optimized execution buffers").
+ *   W, N, K, ldw  as for ht_plan (W is only read; the caller may free it
+ *                 afterwards: the buffers hold everything the linear needs,
+ *                 the page's inference-only mode).
+ *   fmt_map       the plan (any valid codes 0..4 are accepted).
+ *   counts5       (host) the plan's per-format counts.
+ *   buf           device buffer of buf_bytes >= ht_pack_bytes(...), 256-byte
+ *                 aligned; every byte of it is written.
+ *   desc          (host) out: the descriptor of the packed weight.
+ * Codes and scales are recomputed from W exactly as ht_plan defines them. */
+ht_status ht_pack(const float *W, int64_t N, int64_t K, int64_t ldw,
+                  const uint8_t *fmt_map, int64_t row_tile, const int64_t counts5[5],
+                  void *buf, size_t buf_bytes, ht_packed_weight *desc, ht_stream stream);
+
+/* ht_linear_workspace -- workspace bytes ht_linear_forward needs for M rows. */
+ht_status ht_linear_workspace(const ht_packed_weight *w, int64_t M, int32_t path,
+                              size_t *bytes);
+
+/* ht_linear_forward -- the fused mixed-format linear y = x . W_hat^T
+ * ("Key Features": drop-in HyperLinear for nn.Linear, no bias).
+ *   w      (host) descriptor from ht_pack.
+ *   x      bfloat16 bit patterns [M, ldx], ldx >= K.
+ *   y      fp32 [M, ldy] out, ldy >= N: y[m, n] = act(sum_k x[m,k] * w_hat[n,k]),
+ *          accumulated in fp32; integer blocks apply their scale after the
+ *          block's 64-term partial sum.  The result is bitwise reproducible
+ *          run to run (fixed-order reductions, no atomics on data).
+ *   act    HT_ACT_NONE or HT_ACT_RELU.
+ *   path   HT_PATH_AUTO or HT_PATH_GEMV.
+ *   ws     workspace of ws_bytes >= ht_linear_workspace(w, M, path). */
+ht_status ht_linear_forward(const ht_packed_weight *w, const uint16_t *x, int64_t M,
+                            int64_t ldx, float *y, int64_t ldy, int32_t act, int32_t path,
+                            void *ws, size_t ws_bytes, ht_stream stream);
+
+/* ht_mlp_workspace -- workspace bytes ht_mlp_forward needs. */
+ht_status ht_mlp_workspace(const ht_packed_weight *const *layers, int32_t n_layers,
+                           int64_t M, size_t *bytes);
+
+/* ht_mlp_forward -- the page's BenchmarkMLP ("Usage Example": HyperLinear then
+ * ReLU, repeated; no bias):  h_0 = x;  h_l = bf16_rne(relu(h_{l-1} . W_l^T))
+ * for l < L;  y = relu(h_{L-1} . W_L^T) in fp32.
+ *   layers    (host) array of n_layers descriptors; layer l's K must equal
+ *             layer l-1's N.
+ *   x         bfloat16 [M, ldx];  y fp32 [M, ldy] (ldy >= last layer's N).
+ *   act_dump  nullable; if set, bfloat16 [n_layers-1][M][N_l] receives every
+ *             intermediate h_l (each layer's slab is M * N_l elements, slabs
+ *             packed back to back); the layers then read their input from it.
+ *   ws        workspace of ws_bytes >= ht_mlp_workspace(...). */
+ht_status ht_mlp_forward(const ht_packed_weight *const *layers, int32_t n_layers,
+                         const uint16_t *x, int64_t M, int64_t ldx, float *y, int64_t ldy,
+                         uint16_t *act_dump, void *ws, size_t ws_bytes, ht_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HT_H */

@@ -136,6 +136,7 @@ void oracle_int_quant_block(const float *w, int Q, float *s_out, int8_t *q)
         if (isnan(amax)) break;
     }
     float s = amax / (float)Q;                      /* fp32, correctly rounded */
+    if (isnan(s)) s = NAN;                          /* one canonical quiet NaN */
     *s_out = s;
     if (s == 0.0f || !isfinite(s)) {
         for (int i = 0; i < OR_BLOCK; ++i) q[i] = 0;
@@ -339,8 +340,9 @@ void oracle_relu_bf16(const double *z, int64_t count, uint16_t *h)
 /*    scale_f float [c_f] for f = INT4, INT8: the fp32 scale                  */
 /*    pay_f  [c_f][bytes_f] for f = 0..4:                                     */
 /*       INT4 32 B: byte j holds element e = 32*(j/16) + (j%16) in its low    */
-/*            nibble and element e + 16 in its high nibble, each as q + 8;    */
-/*       INT8 64 B: byte i = q_i + 128;                                       */
+/*            nibble and element e + 16 in its high nibble, each as the      */
+/*            4-bit two's complement of q;                                   */
+/*       INT8 64 B: byte i = q_i as an 8-bit two's complement;                */
 /*       BF16 / FP16 128 B: the 16-bit patterns, little endian, in order;     */
 /*       FP32 256 B: the original fp32 bit patterns.                          */
 /* ------------------------------------------------------------------------ */
@@ -393,11 +395,11 @@ void oracle_pack(const float *W, int64_t N, int64_t K, int64_t ldw, const uint8_
                     oracle_int_quant_block(w, f == OR_INT4 ? 7 : 127, &s, q);
                     memcpy(buf + offs[6 + f] + 4 * p, &s, 4);
                     if (f == OR_INT8) {
-                        for (int i = 0; i < OR_BLOCK; ++i) dst[i] = (uint8_t)(q[i] + 128);
+                        for (int i = 0; i < OR_BLOCK; ++i) dst[i] = (uint8_t)q[i];
                     } else {
                         for (int j = 0; j < 32; ++j) {
                             int e = 32 * (j / 16) + (j % 16);
-                            dst[j] = (uint8_t)((q[e] + 8) | ((q[e + 16] + 8) << 4));
+                            dst[j] = (uint8_t)((q[e] & 15) | ((q[e + 16] & 15) << 4));
                         }
                     }
                 } else if (f == OR_BF16) {

@@ -1,0 +1,138 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol the header
+declares, and its host-side checks reject bad arguments before any launch
+(only invalid calls are made here, so nothing reaches the HIP runtime)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_planner_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_symbols():
+    text = open(os.path.join(ROOT, "include", "ht.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ht_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.load()
+    syms = header_symbols()
+    assert len(syms) >= 10
+    for s in syms:
+        assert hasattr(lib, s), s
+    assert set(syms) == set(B.EXPORTS)
+
+
+def test_status_strings_and_defaults():
+    assert B.ht_status_string(0) == "ok"
+    for c in range(1, 6):
+        assert B.ht_status_string(c) not in ("ok", "unknown status")
+    assert B.ht_status_string(99) == "unknown status"
+    p = B.ht_plan_params_default()
+    assert (p.eps_int4, p.eps_int8, p.eps_bf16, p.eps_fp16, p.prefer_bf16, p.force_format) == \
+        (0.08, 0.01, 0.0, 0.0, 1, -1)
+
+
+def test_pack_bytes_matches_layout(orc):
+    for (N, K, R, c) in [(256, 256, 16, [10, 500, 3, 1, 510]), (37, 192, 16, [20, 20, 20, 20, 31]),
+                         (4096, 4096, 16, [163, 195780, 0, 0, 66201]), (256, 2048, 1, [0, 8192, 0, 0, 0]),
+                         (5632, 2048, 8, [0, 0, 0, 0, 5632 * 32])]:
+        assert B.ht_pack_bytes(N, K, R, c) == orc.pack_layout(N, K, R, c)[0]
+
+
+@pytest.mark.parametrize("args,code", [
+    ((256, 100, 16, [0, 0, 0, 0, 0]), 2),          # K % 64
+    ((256, 256, 3, [0, 1024, 0, 0, 0]), 2),        # row tile not a power of two <= 16
+    ((256, 256, 32, [0, 1024, 0, 0, 0]), 2),
+    ((256, 256, 16, [0, 1000, 0, 0, 0]), 1),       # counts do not sum to N*K/64
+    ((256, 256, 16, [-1, 1025, 0, 0, 0]), 1),
+    ((0, 256, 16, [0, 0, 0, 0, 0]), 2),
+    ((16, 64 * 5000, 16, [0, 80000, 0, 0, 0]), 2), # K/64 * R > 65536 (16-bit block ids)
+])
+def test_pack_bytes_rejects(args, code):
+    with pytest.raises(B.HTError) as e:
+        B.ht_pack_bytes(*args)
+    assert e.value.code == code
+
+
+def _plan_raw(W, N, K, ldw, params, fmt):
+    lib = B.load()
+    pp = ctypes.byref(params) if params is not None else None
+    return lib.ht_plan(W, N, K, ldw, pp, fmt, None)
+
+
+def test_plan_argument_checks():
+    good = 0x10000
+    assert _plan_raw(None, 4, 64, 64, None, good) == 1
+    assert _plan_raw(good, 4, 64, 64, None, None) == 1
+    assert _plan_raw(good, 0, 64, 64, None, good) == 2
+    assert _plan_raw(good, 4, 65, 65, None, good) == 2
+    assert _plan_raw(good, 4, 128, 64, None, good) == 2          # ldw < K
+    assert _plan_raw(good + 4, 4, 64, 64, None, good) == 3       # W misaligned
+    assert _plan_raw(good, 4, 64, 66, None, good) == 3           # ldw not a multiple of 4
+    for bad in (-0.1, float("nan"), float("inf")):
+        p = B.ht_plan_params_default()
+        p.eps_int8 = bad
+        assert _plan_raw(good, 4, 64, 64, p, good) == 1
+    p = B.ht_plan_params_default()
+    p.force_format = 5
+    assert _plan_raw(good, 4, 64, 64, p, good) == 1
+    p.force_format = -2
+    assert _plan_raw(good, 4, 64, 64, p, good) == 1
+
+
+def test_plan_counts_argument_checks():
+    lib = B.load()
+    assert lib.ht_plan_counts(None, 4, 64, 0x10000, None) == 1
+    assert lib.ht_plan_counts(0x10000, 4, 64, None, None) == 1
+    assert lib.ht_plan_counts(0x10000, 4, 60, 0x10000, None) == 2
+    assert lib.ht_plan_counts(0x10000, 4, 64, 0x10004, None) == 3
+
+
+def _desc(N=256, K=256, R=16, base=0x100000):
+    d = B.PackedWeight()
+    d.N, d.K, d.row_tile, d.n_tiles = N, K, R, (N + R - 1) // R
+    d.layout_version = 1
+    d.base = base
+    return d
+
+
+def test_linear_argument_checks():
+    lib = B.load()
+    d = _desc()
+    x, y = 0x200000, 0x300000
+    f = lib.ht_linear_forward
+    assert f(None, x, 1, 256, y, 256, 0, 0, None, 0, None) == 1
+    bad = _desc()
+    bad.layout_version = 7
+    assert f(ctypes.byref(bad), x, 1, 256, y, 256, 0, 0, None, 0, None) == 1
+    assert f(ctypes.byref(d), None, 1, 256, y, 256, 0, 0, None, 0, None) == 1
+    assert f(ctypes.byref(d), x, 1, 256, y, 256, 2, 0, None, 0, None) == 1      # act
+    assert f(ctypes.byref(d), x, 1, 256, y, 256, 0, 9, None, 0, None) == 1      # path
+    assert f(ctypes.byref(d), x, 0, 256, y, 256, 0, 0, None, 0, None) == 2      # M
+    assert f(ctypes.byref(d), x, 1, 128, y, 256, 0, 0, None, 0, None) == 2      # ldx < K
+    assert f(ctypes.byref(d), x, 1, 256, y, 100, 0, 0, None, 0, None) == 2      # ldy < N
+    assert f(ctypes.byref(d), x + 2, 1, 256, y, 256, 0, 0, None, 0, None) == 3  # x misaligned
+    assert f(ctypes.byref(d), x, 1, 260, y, 256, 0, 0, None, 0, None) == 3      # ldx % 8
+    big = _desc(N=256, K=64 * 1024, R=16)
+    need = B.ht_linear_workspace(big, 1)
+    assert need > 0                                                            # needs a K-split
+    assert f(ctypes.byref(big), x, 1, 64 * 1024, y, 256, 0, 0, None, 0, None) == 4
+
+
+def test_mlp_argument_checks():
+    lib = B.load()
+    a, b = _desc(256, 256), _desc(128, 512)
+    arr = (ctypes.POINTER(B.PackedWeight) * 2)(ctypes.pointer(a), ctypes.pointer(b))
+    out = ctypes.c_size_t(0)
+    assert lib.ht_mlp_workspace(arr, 2, 1, ctypes.byref(out)) == 2            # K of layer 1 != N of layer 0
+    c = _desc(128, 256)
+    arr = (ctypes.POINTER(B.PackedWeight) * 2)(ctypes.pointer(a), ctypes.pointer(c))
+    assert lib.ht_mlp_workspace(arr, 2, 1, ctypes.byref(out)) == 0
+    assert out.value > 0
+    assert lib.ht_mlp_forward(arr, 2, 0x200000, 1, 256, 0x300000, 128, None, None, 0, None) == 4
+    assert lib.ht_mlp_forward(arr, 0, 0x200000, 1, 256, 0x300000, 128, None, None, 0, None) == 1

@@ -1,0 +1,337 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars: format maps, codes, scales and packed bytes bit-exact; linear outputs
+within max|y_gpu - y_oracle| <= 1e-3 * max|y_oracle| with identical bfloat16
+activations on both sides (oracle in fp64).
+"""
+import numpy as np
+import pytest
+import torch
+
+from block_planner_amd import api
+from block_planner_amd import binding as B
+from block_planner_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+INT4, INT8, BF16, FP16, FP32 = 0, 1, 2, 3, 4
+TOL = 1e-3
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def gpu(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev())
+
+
+def gpu_plan(W, **kw):
+    fmt = api.plan(gpu(W), **kw)
+    torch.cuda.synchronize()
+    return fmt.cpu().numpy()
+
+
+def bf16_gpu(xbits):
+    return gpu(xbits.view(np.int16)).view(torch.bfloat16)
+
+
+def check_close(y_gpu, y_or, what=""):
+    y_gpu = np.asarray(y_gpu, np.float64)
+    err = np.max(np.abs(y_gpu - y_or))
+    ref = np.max(np.abs(y_or))
+    assert np.all(np.isfinite(y_gpu)), what
+    assert err <= TOL * ref, f"{what}: max|dy| = {err:.3e} > {TOL} * {ref:.3e}"
+    return err / max(ref, 1e-300)
+
+
+def edge_matrix(rows=32, per_row=4, seed=0):
+    E = wl.edge_blocks(seed)
+    rng = np.random.default_rng(seed + 5)
+    idx = rng.integers(0, E.shape[0], size=(rows, per_row))
+    idx[0, :] = np.arange(per_row) % E.shape[0]
+    W = E[idx].reshape(rows, per_row * 64)
+    return np.ascontiguousarray(W.astype(np.float32))
+
+
+def finite_rows(W):
+    return np.all(np.isfinite(W.reshape(W.shape[0], -1, 64)), axis=-1)
+
+
+# ---------------------------------------------------------------------------
+# Planner
+# ---------------------------------------------------------------------------
+def test_plan_small_weight(orc):
+    W = wl.small_weight()
+    np.testing.assert_array_equal(gpu_plan(W), orc.plan(W))
+
+
+@pytest.mark.parametrize("kw", [
+    {}, {"prefer_bf16": False}, {"eps_int4": 0.0, "eps_int8": 0.0},
+    {"eps_bf16": 0.004, "eps_fp16": 0.0005}, {"eps_bf16": 0.01, "eps_fp16": 0.01, "prefer_bf16": False},
+    {"eps_int4": 0.16}, {"force_format": 0}, {"force_format": 1}, {"force_format": 4},
+])
+def test_plan_edge_blocks(orc, kw):
+    W = edge_matrix()
+    oracle_kw = dict(kw)
+    force = oracle_kw.pop("force_format", -1)
+    np.testing.assert_array_equal(gpu_plan(W, **kw), orc.plan(W, force=force, **oracle_kw))
+
+
+@pytest.mark.parametrize("shape", [(1, 64), (3, 192), (37, 320), (17, 128), (130, 64 * 88)])
+def test_plan_shapes(orc, shape):
+    rng = np.random.default_rng(shape[0] * 1000 + shape[1])
+    W = (rng.standard_t(3, size=shape) * 0.02).astype(np.float32)
+    W.reshape(-1)[rng.choice(W.size, size=max(1, W.size // 200), replace=False)] *= 40
+    np.testing.assert_array_equal(gpu_plan(W), orc.plan(W))
+
+
+def test_plan_row_stride(orc):
+    """ldw > K: the planner reads W[n, :K] of a wider array."""
+    Wide = wl.small_weight(seed=3, n=64, k=384)
+    W = gpu(Wide)[:, 64:320]
+    fmt = api.plan(W)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(fmt.cpu().numpy(), orc.plan(np.ascontiguousarray(Wide[:, 64:320])))
+
+
+@pytest.mark.parametrize("eps4", [0.04, 0.08, 0.16])
+def test_plan_mlp_layer(orc, eps4):
+    W = wl.mlp_weight(0, dim=4096)[:1024]
+    np.testing.assert_array_equal(gpu_plan(W, eps_int4=eps4), orc.plan(W, eps_int4=eps4))
+
+
+def test_plan_counts(orc):
+    W = edge_matrix(rows=50)
+    fmt = api.plan(gpu(W))
+    c = api.counts(fmt)
+    assert c == list(np.bincount(fmt.cpu().numpy().ravel(), minlength=5))
+
+
+# ---------------------------------------------------------------------------
+# Packer (codes, scales and the whole buffer, byte for byte)
+# ---------------------------------------------------------------------------
+def gpu_pack_bytes(W, fmt, R):
+    pw = api.pack(gpu(W), gpu(fmt), row_tile=R)
+    torch.cuda.synchronize()
+    return pw.buf.cpu().numpy(), pw
+
+
+@pytest.mark.parametrize("R", [1, 4, 8, 16])
+def test_pack_small_weight(orc, R):
+    W = wl.small_weight()
+    fmt = orc.plan(W)
+    got, _ = gpu_pack_bytes(W, fmt, R)
+    np.testing.assert_array_equal(got, orc.pack(W, fmt, R))
+
+
+@pytest.mark.parametrize("force", [INT4, INT8, BF16, FP16, FP32])
+def test_pack_forced_formats(orc, force):
+    """Every block in one format: all codes and scales of that format."""
+    W = wl.small_weight(seed=1)
+    fmt = orc.plan(W, force=force)
+    got, _ = gpu_pack_bytes(W, fmt, 16)
+    np.testing.assert_array_equal(got, orc.pack(W, fmt, 16))
+
+
+def test_pack_mixed_random_formats_ragged(orc):
+    rng = np.random.default_rng(9)
+    W = (rng.normal(size=(37, 320)) * 0.05).astype(np.float32)
+    fmt = rng.integers(0, 5, size=(37, 5)).astype(np.uint8)
+    for R in (4, 16):
+        got, _ = gpu_pack_bytes(W, fmt, R)
+        np.testing.assert_array_equal(got, orc.pack(W, fmt, R))
+
+
+@pytest.mark.parametrize("force", [INT4, INT8, FP32])
+def test_pack_edge_blocks(orc, force):
+    """Subnormal, huge, tie, NaN and Inf blocks: scales (including the
+    canonical NaN / Inf scale) and codes bit-exact."""
+    W = edge_matrix()
+    fmt = orc.plan(W, force=force)
+    got, _ = gpu_pack_bytes(W, fmt, 8)
+    np.testing.assert_array_equal(got, orc.pack(W, fmt, 8))
+
+
+@pytest.mark.parametrize("force", [BF16, FP16])
+def test_pack_edge_blocks_16bit(orc, force):
+    W = edge_matrix()
+    keep = np.all(finite_rows(W), axis=1)
+    W = np.ascontiguousarray(W[keep])
+    fmt = orc.plan(W, force=force)
+    got, _ = gpu_pack_bytes(W, fmt, 8)
+    np.testing.assert_array_equal(got, orc.pack(W, fmt, 8))
+
+
+def test_pack_mlp_layer(orc):
+    W = wl.mlp_weight(2, dim=4096)[:512]
+    fmt = orc.plan(W)
+    got, _ = gpu_pack_bytes(W, fmt, 16)
+    np.testing.assert_array_equal(got, orc.pack(W, fmt, 16))
+
+
+# ---------------------------------------------------------------------------
+# Linear
+# ---------------------------------------------------------------------------
+def run_linear(W, fmt, xbits, R=16, act=0, ldx_pad=0, ldy_pad=0):
+    pw = api.pack(gpu(W), gpu(fmt), row_tile=R)
+    M, K = xbits.shape
+    xs = torch.zeros((M, K + ldx_pad), dtype=torch.bfloat16, device=dev())
+    xs[:, :K] = bf16_gpu(xbits)
+    ys = torch.full((M, W.shape[0] + ldy_pad), 7.0, dtype=torch.float32, device=dev())
+    x_v, y_v = xs[:, :K], ys[:, :W.shape[0]]
+    api.linear(pw, x_v, act=act, out=y_v)
+    torch.cuda.synchronize()
+    if ldy_pad:
+        assert torch.all(ys[:, W.shape[0]:] == 7.0)   # padding untouched
+    return y_v.cpu().numpy()
+
+
+@pytest.mark.parametrize("M", [1, 2, 5, 8, 13])
+def test_linear_small_weight(orc, M):
+    W = wl.small_weight()
+    fmt = orc.plan(W)
+    x = wl.to_bf16_bits(wl.small_activation(m=M))
+    check_close(run_linear(W, fmt, x), orc.linear(W, fmt, x), f"M={M}")
+
+
+@pytest.mark.parametrize("R", [1, 4, 16])
+def test_linear_all_formats(orc, R):
+    rng = np.random.default_rng(17)
+    W = (rng.normal(size=(200, 512)) * 0.05).astype(np.float32)
+    fmt = rng.integers(0, 5, size=(200, 8)).astype(np.uint8)
+    x = wl.to_bf16_bits(rng.normal(size=(3, 512)).astype(np.float32))
+    check_close(run_linear(W, fmt, x, R=R), orc.linear(W, fmt, x), f"R={R}")
+
+
+@pytest.mark.parametrize("force", [INT4, INT8, BF16, FP16, FP32])
+def test_linear_single_format(orc, force):
+    W = wl.small_weight(seed=4)
+    fmt = orc.plan(W, force=force)
+    x = wl.to_bf16_bits(wl.small_activation(m=2))
+    check_close(run_linear(W, fmt, x), orc.linear(W, fmt, x), f"force={force}")
+
+
+def test_linear_relu_strides_ragged(orc):
+    rng = np.random.default_rng(18)
+    W = (rng.normal(size=(37, 192)) * 0.1).astype(np.float32)
+    fmt = orc.plan(W, eps_int4=0.2)
+    x = wl.to_bf16_bits(rng.normal(size=(4, 192)).astype(np.float32))
+    y = run_linear(W, fmt, x, act=1, ldx_pad=64, ldy_pad=5)
+    check_close(y, np.maximum(orc.linear(W, fmt, x), 0), "relu/strides")
+
+
+def test_linear_single_block(orc):
+    W = (np.arange(64, dtype=np.float32) - 31.5)[None, :] / 64
+    fmt = orc.plan(W)
+    x = wl.to_bf16_bits(np.ones((1, 64), np.float32))
+    check_close(run_linear(W, fmt, x), orc.linear(W, fmt, x), "1x64")
+
+
+def test_linear_long_k_split(orc):
+    """K = 14336 (the 8B-shaped down projection width): the launch splits K
+    and a second kernel adds the splits in order."""
+    shp = wl.LinearShape("down", 96, 14336)
+    W = wl.llama8b_weight(0, shp)
+    fmt = orc.plan(W)
+    pw = api.pack(gpu(W), gpu(fmt))
+    assert B.ht_linear_workspace(pw.desc, 1) > 0
+    for M in (1, 4):
+        x = wl.to_bf16_bits(wl.activation("llama8b", M, 14336))
+        check_close(run_linear(W, fmt, x), orc.linear(W, fmt, x), f"K=14336 M={M}")
+
+
+def test_linear_deterministic():
+    W = wl.mlp_weight(1, dim=4096)[:2048]
+    Wg = gpu(W)
+    fmt = api.plan(Wg)
+    pw = api.pack(Wg, fmt)
+    x = bf16_gpu(wl.to_bf16_bits(wl.mlp_activation(3)))
+    y1 = api.linear(pw, x).clone()
+    y2 = api.linear(pw, x).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
+# ---------------------------------------------------------------------------
+# The 4096-wide, depth-4 MLP at the benchmark's launch configuration
+# ---------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def mlp4096(orc):
+    Ws = [wl.mlp_weight(l) for l in range(wl.MLP_DEPTH)]
+    fmts = [orc.plan(W) for W in Ws]
+    pws = []
+    for W, f in zip(Ws, fmts):
+        Wg = gpu(W)
+        fg = api.plan(Wg)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(fg.cpu().numpy(), f)   # planner parity at full size
+        pws.append(api.pack(Wg, fg, row_tile=16))
+        del Wg
+    return Ws, fmts, pws
+
+
+@pytest.mark.parametrize("M", [1, 32])
+def test_mlp_teacher_forced(orc, mlp4096, M):
+    Ws, fmts, pws = mlp4096
+    x = wl.to_bf16_bits(wl.mlp_activation(M))
+    y, dumps = api.mlp(pws, bf16_gpu(x), dump=True)
+    torch.cuda.synchronize()
+    h_in = x
+    for l in range(wl.MLP_DEPTH):
+        z = orc.linear(Ws[l], fmts[l], h_in)
+        if l + 1 < wl.MLP_DEPTH:
+            h_gpu = dumps[l].cpu().view(torch.int16).numpy().view(np.uint16)
+            hv = wl.bf16_bits_to_f32(h_gpu).astype(np.float64)
+            r = np.maximum(z, 0)
+            # bf16 output: tolerance plus half a bf16 ulp of the value
+            err = np.abs(hv - r) - np.abs(r) * 2.0 ** -8
+            assert np.max(err) <= TOL * np.max(r), f"layer {l}"
+            h_in = h_gpu
+        else:
+            check_close(y.cpu().numpy(), np.maximum(z, 0), f"last layer M={M}")
+
+
+def test_mlp_end_to_end_info(orc, mlp4096):
+    """End to end without teacher forcing (rounding differences of the bf16
+    activations compound over layers): reported with a looser bound."""
+    Ws, fmts, pws = mlp4096
+    x = wl.to_bf16_bits(wl.mlp_activation(1))
+    y = api.mlp(pws, bf16_gpu(x))
+    torch.cuda.synchronize()
+    y_or, _ = orc.mlp(Ws, fmts, x)
+    err = np.max(np.abs(y.cpu().numpy() - y_or)) / np.max(np.abs(y_or))
+    print(f"MLP end-to-end relative max error {err:.3e}")
+    assert err < 2e-2
+
+
+# ---------------------------------------------------------------------------
+# Transformer-shaped layers at full size (sampled outputs)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg,name", [("tinyllama", "k"), ("tinyllama", "down"), ("llama8b", "gate"),
+                                      ("llama8b", "v")])
+def test_full_size_layers_sampled(orc, cfg, name):
+    shapes = wl.tinyllama_shapes() if cfg == "tinyllama" else wl.llama8b_shapes()
+    shp = [s for s in shapes if s.name == name][0]
+    W = (wl.tinyllama_weight if cfg == "tinyllama" else wl.llama8b_weight)(0, shp)
+    fmt_or = orc.plan(W)
+    Wg = gpu(W)
+    fmt = api.plan(Wg)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(fmt.cpu().numpy(), fmt_or)
+    pw = api.pack(Wg, fmt)
+    x1 = wl.to_bf16_bits(wl.activation(cfg, 1, shp.k))
+    y1 = api.linear(pw, bf16_gpu(x1))
+    torch.cuda.synchronize()
+    check_close(y1.cpu().numpy(), orc.linear(W, fmt_or, x1), f"{cfg}.{name} M=1")
+    M = 16
+    x = wl.to_bf16_bits(wl.activation(cfg, M, shp.k))
+    y = api.linear(pw, bf16_gpu(x))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    mi = rng.integers(0, M, size=128)
+    ni = rng.integers(0, shp.n, size=128)
+    ys = orc.linear_sampled(W, fmt_or, x, mi, ni)
+    # scale: the largest sampled oracle value (a lower bound of max|y|, so
+    # the bound is at least as strict as the full-output one)
+    assert np.max(np.abs(y.cpu().numpy()[mi, ni] - ys)) <= TOL * np.max(np.abs(ys)), (cfg, name, M)

@@ -80,13 +80,14 @@ def read_packed(buf: np.ndarray, N: int, K: int, R: int):
                     if f in (INT4, INT8):
                         s = float(buf[sc_off[f] + 4 * p: sc_off[f] + 4 * p + 4].view(np.float32)[0])
                         if f == INT8:
-                            q = raw.astype(np.int64) - 128
+                            q = raw.view(np.int8).astype(np.int64)
                         else:
                             q = np.zeros(64, np.int64)
                             for j in range(32):
                                 e = 32 * (j // 16) + (j % 16)
-                                q[e] = (int(raw[j]) & 15) - 8
-                                q[e + 16] = (int(raw[j]) >> 4) - 8
+                                lo, hi = int(raw[j]) & 15, int(raw[j]) >> 4
+                                q[e] = lo - 16 if lo >= 8 else lo
+                                q[e + 16] = hi - 16 if hi >= 8 else hi
                         vals = q.astype(np.float64) * s
                     elif f == BF16:
                         vals = (raw.view(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
