@@ -41,9 +41,9 @@ struct LinArgs {
 __host__ __device__ constexpr uint32_t bpc_of(int f) { return f == 0 ? 32u : f == 1 ? 16u : f == 4 ? 4u : 8u; }
 __device__ constexpr int lpb_of(int f) { return f == 0 ? 2 : f == 1 ? 4 : f == 4 ? 16 : 8; }
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 16;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kUnroll = 4;   // chunks in flight per wave
+constexpr int kUnroll = 8;   // chunks in flight per wave (a 16-row, 4096-wide tile is one batch)
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
@@ -163,30 +163,118 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(LinArgs a) {
     float *xs = lds;                       // [M][nkb*64]
     float *P = lds + M * xstride;          // [M][R][nkb+1]
 
-    // this workgroup's range of each format's blocks
+    // this workgroup's range of each format's blocks (10 independent scalar
+    // loads, then the per-format chunk counts)
     const uint32_t *kbidx = reinterpret_cast<const uint32_t *>(a.base + a.off_kbidx);
+    const uint64_t col0 = uint64_t(t) * a.KB + kb0, col1 = uint64_t(t) * a.KB + kb1;
     uint32_t lo[5], hi[5], nch[5];
+#pragma unroll
+    for (int f = 0; f < 5; ++f) {
+        hi[f] = kbidx[uint64_t(f) * a.nk + col1];
+        lo[f] = kbidx[uint64_t(f) * a.nk + col0];
+    }
     uint32_t C = 0;
 #pragma unroll
     for (int f = 0; f < 5; ++f) {
-        uint32_t h = min(kbidx[uint64_t(f) * a.nk + t * a.KB + kb1], a.counts[f]);
-        uint32_t l = min(kbidx[uint64_t(f) * a.nk + t * a.KB + kb0], h);
-        lo[f] = l;
-        hi[f] = h;
-        nch[f] = (h - l + bpc_of(f) - 1) / bpc_of(f);
+        hi[f] = min(hi[f], a.counts[f]);
+        lo[f] = min(lo[f], hi[f]);
+        nch[f] = (hi[f] - lo[f] + bpc_of(f) - 1) / bpc_of(f);
         C += nch[f];
     }
+    // per-format base pointers, resolved with static indices (kept in
+    // scalar registers; a run-time index into the argument arrays would make
+    // the compiler fetch them with vector loads and serialise every chunk)
+    const uint8_t *pay_b[5];
+    const uint16_t *id_b[5];
+#pragma unroll
+    for (int f = 0; f < 5; ++f) {
+        pay_b[f] = a.base + a.off_pay[f];
+        id_b[f] = reinterpret_cast<const uint16_t *>(a.base + a.off_ids[f]);
+    }
+    const float *sc_b0 = reinterpret_cast<const float *>(a.base + a.off_scale[0]);
+    const float *sc_b1 = reinterpret_cast<const float *>(a.base + a.off_scale[1]);
 
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t wave = threadIdx.x >> 6;
 
-    // stage x[:, 64kb0 .. 64kb1) as fp32
-    {
-        const uint32_t per_row = nkb * 8;   // 8 bf16 per 16-byte load
-        for (uint32_t i = threadIdx.x; i < M * per_row; i += kThreads) {
-            const uint32_t m = i / per_row, j = i - m * per_row;
-            const uint4 v = *reinterpret_cast<const uint4 *>(a.x + int64_t(m) * a.ldx + kb0 * 64 + j * 8);
-            float4 *d = reinterpret_cast<float4 *>(xs + m * xstride + j * 8);
+    // one batch: kUnroll chunks per wave, 16 payload bytes + id + scale per lane
+    uint4 pay[kUnroll];
+    float sc[kUnroll];
+    uint32_t ids[kUnroll];
+    int fm[kUnroll];
+    bool vl[kUnroll];
+    // Loads are issued without branches (straight-line code lets the
+    // compiler wait for the x loads alone): a slot without a chunk reads the
+    // first 256 bytes of the buffer, and a lane past the end of its format's
+    // range re-reads the range's last block; neither lane stores a result.
+    const float *dummy_f = reinterpret_cast<const float *>(a.base);
+    auto load_batch = [&](uint32_t c0) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint32_t c = c0 + u * kWaves;
+            // wave-uniform: format and chunk index within the format
+            int f = 5;
+            uint32_t ci = c, base_blk = 0, hb = 1, bpc = 1, pb = 0;
+            const uint8_t *pp = a.base;
+            const uint16_t *ip = reinterpret_cast<const uint16_t *>(a.base);
+            const float *sp = dummy_f;
+            int lg = 4;
+#pragma unroll
+            for (int g = 0; g < 5; ++g) {
+                if (f == 5) {
+                    if (ci < nch[g]) {
+                        f = g;
+                        base_blk = lo[g];
+                        hb = hi[g];
+                        bpc = bpc_of(g);
+                        pb = uint32_t(pay_bytes(g));
+                        pp = pay_b[g];
+                        ip = id_b[g];
+                        sp = g == 0 ? sc_b0 : g == 1 ? sc_b1 : dummy_f;
+                        lg = g == 0 ? 1 : g == 1 ? 2 : g == 4 ? 4 : 3;
+                    } else {
+                        ci -= nch[g];
+                    }
+                }
+            }
+            uint32_t blk = base_blk + ci * bpc + (lane >> lg);
+            vl[u] = f < 5 && blk < hb;
+            blk = f < 5 ? min(blk, hb - 1u) : 0u;
+            const uint32_t sblk = f < 2 ? blk : 0u;
+            fm[u] = f;
+            const u32x4 pv = ld_stream_u4(pp + uint64_t(blk) * pb + (lane & ((1u << lg) - 1u)) * 16u);
+            pay[u] = make_uint4(pv.x, pv.y, pv.z, pv.w);
+            ids[u] = ip[blk];
+            const float sv = sp[sblk];
+            sc[u] = f < 2 ? sv : 1.0f;   // float formats carry no scale
+        }
+    };
+
+    // x for these K-blocks: at most two 16-byte loads per thread (the host
+    // keeps M * nkb * 64 * 4 bytes of x within 64 KiB of LDS).  They are
+    // issued before the weight loads, so converting them into LDS waits only
+    // for themselves.
+    const uint32_t per_row = nkb * 8;   // 8 bf16 per 16-byte load
+    uint4 xr[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const uint32_t i = threadIdx.x + j * kThreads;
+        if (i < M * per_row) {
+            const uint32_t m = i / per_row, jj = i - m * per_row;
+            xr[j] = *reinterpret_cast<const uint4 *>(a.x + int64_t(m) * a.ldx + kb0 * 64 + jj * 8);
+        }
+    }
+
+    // the first batch of weights is in flight while x goes into LDS
+    load_batch(wave);
+
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const uint32_t i = threadIdx.x + j * kThreads;
+        if (i < M * per_row) {
+            const uint32_t m = i / per_row, jj = i - m * per_row;
+            const uint4 v = xr[j];
+            float4 *d = reinterpret_cast<float4 *>(xs + m * xstride + jj * 8);
             d[0] = make_float4(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y));
             d[1] = make_float4(bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w));
         }
@@ -194,42 +282,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(LinArgs a) {
     __syncthreads();
 
     for (uint32_t c0 = wave; c0 < C; c0 += kWaves * kUnroll) {
-        uint4 pay[kUnroll];
-        float sc[kUnroll];
-        uint32_t ids[kUnroll];
-        int fm[kUnroll];
-        bool vl[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const uint32_t c = c0 + u * kWaves;
-            int f = 5;
-            uint32_t ci = c;
-#pragma unroll
-            for (int g = 0; g < 5; ++g) {
-                if (f == 5) {
-                    if (ci < nch[g]) f = g;
-                    else ci -= nch[g];
-                }
-            }
-            fm[u] = f;
-            pay[u] = make_uint4(0, 0, 0, 0);
-            sc[u] = 1.0f;
-            ids[u] = 0;
-            vl[u] = false;
-            if (f < 5) {
-                const int lpb = f == 0 ? 2 : f == 1 ? 4 : f == 4 ? 16 : 8;
-                const int lg = f == 0 ? 1 : f == 1 ? 2 : f == 4 ? 4 : 3;
-                const uint32_t blk = lo[f] + ci * bpc_of(f) + (lane >> lg);
-                vl[u] = blk < hi[f];
-                if (vl[u]) {
-                    const uint8_t *p = a.base + a.off_pay[f] + uint64_t(blk) * pay_bytes(f) + (lane & (lpb - 1)) * 16;
-                    const u32x4 pv = ld_stream_u4(p);
-                    pay[u] = make_uint4(pv.x, pv.y, pv.z, pv.w);
-                    ids[u] = reinterpret_cast<const uint16_t *>(a.base + a.off_ids[f])[blk];
-                    if (f < 2) sc[u] = reinterpret_cast<const float *>(a.base + a.off_scale[f])[blk];
-                }
-            }
-        }
+        if (c0 != wave) load_batch(c0);
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             switch (fm[u]) {
