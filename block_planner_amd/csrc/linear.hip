@@ -195,7 +195,9 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(LinArgs a) {
     const float *sc_b1 = reinterpret_cast<const float *>(a.base + a.off_scale[1]);
 
     const uint32_t lane = threadIdx.x & 63;
-    const uint32_t wave = threadIdx.x >> 6;
+    // wave index as a scalar: everything derived from it (chunk -> format
+    // decode, base pointers) then stays in scalar registers
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
     // one batch: kUnroll chunks per wave, 16 payload bytes + id + scale per lane
     uint4 pay[kUnroll];
@@ -281,8 +283,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(LinArgs a) {
     }
     __syncthreads();
 
-    for (uint32_t c0 = wave; c0 < C; c0 += kWaves * kUnroll) {
-        if (c0 != wave) load_batch(c0);
+    auto compute_batch = [&]() {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             switch (fm[u]) {
@@ -294,6 +295,14 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(LinArgs a) {
             default: break;
             }
         }
+    };
+    // The first batch is consumed in straight-line code after its loads, so
+    // each chunk waits only for its own data and the arithmetic on early
+    // chunks overlaps the arrival of later ones.
+    compute_batch();
+    for (uint32_t c0 = wave + kWaves * kUnroll; c0 < C; c0 += kWaves * kUnroll) {
+        load_batch(c0);
+        compute_batch();
     }
     __syncthreads();
 
