@@ -87,18 +87,25 @@ def linear(pw: PackedLinear, x: torch.Tensor, act: int = B.HT_ACT_NONE, out: tor
     return y
 
 
+def mlp_workspace(layers: list, M: int, device, stream=None) -> torch.Tensor:
+    """An initialised workspace for mlp() over these layers at batch M."""
+    ws = workspace(B.ht_mlp_workspace([pw.desc for pw in layers], M), device)
+    B.ht_workspace_init(ws, stream=stream)
+    return ws
+
+
 def mlp(layers: list, x: torch.Tensor, dump: bool = False, out: torch.Tensor | None = None,
-        ws: torch.Tensor | None = None, stream=None):
+        ws: torch.Tensor | None = None, path: int = B.HT_PATH_AUTO, stream=None):
     M = x.shape[0]
     descs = [pw.desc for pw in layers]
     y = torch.empty((M, layers[-1].N), dtype=torch.float32, device=x.device) if out is None else out
     if ws is None:
-        ws = workspace(B.ht_mlp_workspace(descs, M), x.device)
+        ws = mlp_workspace(layers, M, x.device, stream=stream)
     act_dump = None
     if dump:
         tot = sum(M * pw.N for pw in layers[:-1])
         act_dump = torch.empty(max(tot, 8), dtype=torch.bfloat16, device=x.device)
-    B.ht_mlp_forward(descs, x, y, act_dump=act_dump, ws=ws, stream=stream)
+    B.ht_mlp_forward(descs, x, y, act_dump=act_dump, path=path, ws=ws, stream=stream)
     if dump:
         slabs, off = [], 0
         for pw in layers[:-1]:

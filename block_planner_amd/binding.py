@@ -18,14 +18,14 @@ LIB_PATH = os.path.join(HERE, "libht.so")
 
 HT_INT4, HT_INT8, HT_BF16, HT_FP16, HT_FP32 = range(5)
 HT_ACT_NONE, HT_ACT_RELU = 0, 1
-HT_PATH_AUTO, HT_PATH_GEMV = 0, 1
+HT_PATH_AUTO, HT_PATH_GEMV, HT_PATH_FUSED = 0, 1, 2
 HT_LAYOUT_VERSION = 1
 STATUS = {0: "HT_OK", 1: "HT_EINVAL", 2: "HT_ESHAPE", 3: "HT_EALIGN", 4: "HT_ESMALL", 5: "HT_EHIP"}
 
 # Every symbol include/ht.h declares.
 EXPORTS = ("ht_status_string", "ht_plan_params_default", "ht_plan", "ht_plan_counts",
            "ht_pack_bytes", "ht_pack", "ht_linear_workspace", "ht_linear_forward",
-           "ht_mlp_workspace", "ht_mlp_forward")
+           "ht_mlp_workspace", "ht_workspace_init", "ht_mlp_forward")
 
 
 class HTError(RuntimeError):
@@ -83,9 +83,11 @@ def load() -> ctypes.CDLL:
     lib.ht_mlp_workspace.restype = St
     lib.ht_mlp_workspace.argtypes = [ctypes.POINTER(ctypes.POINTER(PackedWeight)), I32, I64,
                                      ctypes.POINTER(ctypes.c_size_t)]
+    lib.ht_workspace_init.restype = St
+    lib.ht_workspace_init.argtypes = [P, ctypes.c_size_t, P]
     lib.ht_mlp_forward.restype = St
-    lib.ht_mlp_forward.argtypes = [ctypes.POINTER(ctypes.POINTER(PackedWeight)), I32, P, I64, I64, P, I64, P, P,
-                                   ctypes.c_size_t, P]
+    lib.ht_mlp_forward.argtypes = [ctypes.POINTER(ctypes.POINTER(PackedWeight)), I32, P, I64, I64, P, I64, P, I32,
+                                   P, ctypes.c_size_t, P]
     _lib = lib
     return lib
 
@@ -184,11 +186,17 @@ def ht_mlp_workspace(descs, M: int) -> int:
     return out.value
 
 
-def ht_mlp_forward(descs, x, y, act_dump=None, ws=None, stream=None, M=None, ldx=None, ldy=None,
-                   ws_bytes=None) -> None:
+def ht_workspace_init(ws, stream=None, ws_bytes=None) -> None:
+    wsb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check("ht_workspace_init", load().ht_workspace_init(_ptr(ws), wsb, _stream(stream)))
+
+
+def ht_mlp_forward(descs, x, y, act_dump=None, path: int = HT_PATH_AUTO, ws=None, stream=None, M=None, ldx=None,
+                   ldy=None, ws_bytes=None, desc_array=None) -> None:
     M = x.shape[0] if M is None else M
     ldx = x.stride(0) if ldx is None else ldx
     ldy = y.stride(0) if ldy is None else ldy
     wsb = (ws.numel() * ws.element_size() if ws is not None else 0) if ws_bytes is None else ws_bytes
-    _check("ht_mlp_forward", load().ht_mlp_forward(_desc_array(descs), len(descs), _ptr(x), M, ldx, _ptr(y), ldy,
-                                                   _ptr(act_dump), _ptr(ws), wsb, _stream(stream)))
+    arr = _desc_array(descs) if desc_array is None else desc_array
+    _check("ht_mlp_forward", load().ht_mlp_forward(arr, len(descs), _ptr(x), M, ldx, _ptr(y), ldy,
+                                                   _ptr(act_dump), path, _ptr(ws), wsb, _stream(stream)))

@@ -1,0 +1,21 @@
+// linear_host.h -- host helpers of the single-layer linear, shared with the
+// MLP entry points.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "../../include/ht.h"
+
+namespace ht {
+
+// A descriptor the kernels can use (layout version, shape, row tile).
+bool desc_ok(const ht_packed_weight *w);
+
+// Workspace bytes of one linear over M rows (the K-split partial sums).
+size_t linear_ws(const ht_packed_weight *w, int64_t M);
+
+// Enqueue one linear: y = act(x . W_hat^T), fp32 y or bfloat16 ybf (one of
+// them non-null).  Arguments are assumed checked.
+ht_status run_linear(const ht_packed_weight *w, const uint16_t *x, int64_t M, int64_t ldx, float *y,
+                     uint16_t *ybf, int64_t ldy, int act, void *ws, hipStream_t s);
+
+}  // namespace ht

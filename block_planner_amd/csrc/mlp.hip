@@ -1,0 +1,476 @@
+// mlp.hip -- the page's BenchmarkMLP forward ("Usage Example": HyperLinear
+// layers each followed by ReLU) over packed execution buffers.
+//
+// Fused path: one persistent launch runs every layer.  Workgroup g owns row
+// tile g of each layer (the grid is the largest layer's tile count, and all
+// workgroups are resident together).  15 of its 16 wavefronts stream the
+// tile's weight chunks: each walks one sequence of chunks across all layers
+// in groups of 8 register slots and refills slot u, as soon as it has been
+// consumed, with the chunk one group ahead -- so layer l+1's weights are in
+// flight while layer l finishes.  The 16th wavefront moves activations; it
+// holds no weight loads, so waiting for activations never waits for weights.
+//
+// Activation exchange without a barrier or cache flushes: a hidden layer's
+// outputs are ReLU values, so the sign bit of each bfloat16 is free.  Four
+// values are published with one 64-bit atomic store, their four sign bits
+// holding a 4-bit call tag (the workspace keeps a call counter; tags cycle
+// through 1..15, so a zero-initialised word never matches).  The activation
+// wavefront of every workgroup reads the whole layer with 64-bit atomic
+// loads and re-reads any word whose tag is not yet the current one.  Every
+// word is written exactly once per call, so a matching tag means the word
+// holds this call's values (single-copy atomicity of the 64-bit access).
+// The wait is bounded (~50 ms); if it ever expires, a flag word in the
+// workspace is set and that call's output is invalid, but the launch still
+// terminates.
+//
+// Per-layer path: one single-layer launch per layer (linear.hip), used when
+// the fused launch does not fit (layer count, batch, LDS, residency, tiles).
+#include "gemv_common.h"
+#include "linear_host.h"
+
+namespace ht {
+
+constexpr int kMaxLayers = 8;
+constexpr int kMaxFusedM = 4;
+constexpr uint32_t kSpinLimit = 1u << 21;   // x ~64 clocks per poll: ~50 ms
+constexpr uint32_t kSyncBytes = 256;        // [0] call counter, [2] expired-wait flag
+constexpr uint32_t kLoadWaves = kWaves - 1; // waves streaming weights; the last one moves activations
+constexpr uint32_t kXWords = 16;            // activation words read per lane per round
+
+struct MlpArgs {
+    LayerDev layer[kMaxLayers];
+    uint64_t *hw[kMaxLayers];     // tagged activation words of hidden layer l: [M][N_l / 4]
+    uint16_t *hd[kMaxLayers];     // optional plain bfloat16 copy of hidden layer l: [M][N_l]
+    const uint16_t *x;
+    int64_t ldx;
+    float *y;
+    int64_t ldy;
+    uint32_t *sync;
+    uint32_t n_layers;
+    uint32_t xcap;                // fp32 entries per row of the x region (max K)
+    uint32_t pcap;                // P row stride (max K/64 + 1)
+    uint32_t rmax;                // max row tile
+};
+
+// Groups of kUnroll chunks this wave walks in a layer with C chunks for its
+// tile (at least one, possibly all-empty, so every wave stays in step).
+__device__ __forceinline__ uint32_t wave_groups(uint32_t C, uint32_t wave) {
+    const uint32_t J = C > wave ? (C - wave + kLoadWaves - 1) / kLoadWaves : 0u;
+    const uint32_t g = (J + kUnroll - 1) / kUnroll;
+    return g ? g : 1u;
+}
+
+// Chunk loader state for layer l of this workgroup's tile (from the LDS copy
+// of the tile's block ranges).
+__device__ __forceinline__ ChunkSrc layer_src(const MlpArgs &a, const uint32_t *meta, uint32_t l) {
+    uint32_t lo[5], hi[5];
+#pragma unroll
+    for (int f = 0; f < 5; ++f) {
+        lo[f] = __builtin_amdgcn_readfirstlane(meta[l * 10 + f * 2 + 0]);
+        hi[f] = __builtin_amdgcn_readfirstlane(meta[l * 10 + f * 2 + 1]);
+    }
+    return chunk_src(a.layer[l], lo, hi);
+}
+
+// Layer 0's input (bfloat16 [M][K], row stride ld) -> LDS fp32 [M][xcap].
+template <int M>
+__device__ __forceinline__ void stage_input(const uint16_t *x, int64_t ld, uint32_t K, float *xs, uint32_t xstride,
+                                            uint32_t lane) {
+    const uint32_t per_row = K / 8, total = M * per_row;
+    for (uint32_t base = 0; base < total; base += 64 * 8) {
+        uint4 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t i = base + j * 64 + lane;
+            if (i < total) {
+                const uint32_t m = i / per_row, jj = i - m * per_row;
+                v[j] = *reinterpret_cast<const uint4 *>(x + int64_t(m) * ld + jj * 8);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t i = base + j * 64 + lane;
+            if (i < total) {
+                const uint32_t m = i / per_row, jj = i - m * per_row;
+                float4 *d = reinterpret_cast<float4 *>(xs + m * xstride + jj * 8);
+                d[0] = make_float4(bf16_lo(v[j].x), bf16_hi(v[j].x), bf16_lo(v[j].y), bf16_hi(v[j].y));
+                d[1] = make_float4(bf16_lo(v[j].z), bf16_hi(v[j].z), bf16_lo(v[j].w), bf16_hi(v[j].w));
+            }
+        }
+    }
+}
+
+// The tag of a call: bit j of (counter mod 15) + 1 goes to the sign bit of
+// value j of every word.
+__device__ __forceinline__ uint64_t tag_bits(uint32_t counter) {
+    const uint32_t tag = counter % 15u + 1u;
+    return (uint64_t(tag & 1u) << 15) | (uint64_t((tag >> 1) & 1u) << 31) | (uint64_t((tag >> 2) & 1u) << 47) |
+           (uint64_t((tag >> 3) & 1u) << 63);
+}
+
+// A word is current when its four sign bits spell this call's tag.
+__device__ __forceinline__ bool word_ready(uint64_t w, uint64_t tagmask) {
+    return (w & 0x8000800080008000ull) == tagmask;
+}
+
+// Hidden layer's activations (tagged words [M][N/4]) -> LDS fp32 [M][xcap].
+// Rounds of kXWords 64-bit atomic loads per lane, re-reading stale words.
+template <int M>
+__device__ __forceinline__ void gather_hidden(const uint64_t *words, uint32_t N, uint64_t tagmask, float *xs,
+                                              uint32_t xstride, uint32_t lane, uint32_t *sync) {
+    const uint32_t per_row = N / 4, total = M * per_row;
+    for (uint32_t base = 0; base < total; base += 64 * kXWords) {
+        uint64_t v[kXWords];
+#pragma unroll
+        for (uint32_t j = 0; j < kXWords; ++j) {
+            const uint32_t i = base + j * 64 + lane;
+            v[j] = i < total ? __hip_atomic_load(words + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : tagmask;
+        }
+        uint32_t n = 0;
+        for (;;) {
+            bool ok = true;
+#pragma unroll
+            for (uint32_t j = 0; j < kXWords; ++j) ok = ok && word_ready(v[j], tagmask);
+            if (__all(ok)) break;
+            if (++n > kSpinLimit) {
+                if (lane == 0) __hip_atomic_store(sync + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+            for (uint32_t j = 0; j < kXWords; ++j) {
+                const uint32_t i = base + j * 64 + lane;
+                if (i < total && !word_ready(v[j], tagmask))
+                    v[j] = __hip_atomic_load(words + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+#pragma unroll
+        for (uint32_t j = 0; j < kXWords; ++j) {
+            const uint32_t i = base + j * 64 + lane;
+            if (i < total) {
+                const uint32_t m = i / per_row, q = i - m * per_row;
+                const uint64_t w = v[j] & ~0x8000800080008000ull;
+                const uint32_t lo = uint32_t(w), hi = uint32_t(w >> 32);
+                *reinterpret_cast<float4 *>(xs + m * xstride + q * 4) =
+                    make_float4(bf16_lo(lo), bf16_hi(lo), bf16_lo(hi), bf16_hi(hi));
+            }
+        }
+    }
+}
+
+template <int M>
+__global__ __launch_bounds__(kThreads) void mlp_fused_kernel(MlpArgs a) {
+    extern __shared__ float lds[];
+    uint32_t *meta = reinterpret_cast<uint32_t *>(lds);   // [layer][format][lo, hi]: 80 words
+    float *hrow = lds + 128;                              // this tile's row results [M][rmax] (<= 64)
+    float *xs = lds + 192;                                // [M][xcap]
+    float *P = xs + M * a.xcap;                           // [M][rmax][pcap]
+    const uint32_t t = blockIdx.x;
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t L = a.n_layers;
+    const bool xwave = wave == kLoadWaves;
+    // the call counter is read before any word of this call can be written;
+    // workgroup 0 advances it after the last layer
+    const uint32_t epoch =
+        __builtin_amdgcn_readfirstlane(__hip_atomic_load(a.sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    const uint64_t tagmask = tag_bits(epoch);
+
+    // block ranges of this tile in every layer -> LDS (10 values per layer)
+    if (threadIdx.x < 10 * L) {
+        const uint32_t l = threadIdx.x / 10, f = (threadIdx.x % 10) >> 1, end = threadIdx.x & 1;
+        const LayerDev &w = a.layer[l];
+        uint32_t v = 0;
+        if (t < w.T) {
+            const uint32_t *kbidx = reinterpret_cast<const uint32_t *>(w.base + w.off_kbidx);
+            v = kbidx[uint64_t(f) * w.nk + uint64_t(t) * w.KB + (end ? w.KB : 0u)];
+        }
+        meta[threadIdx.x] = v;
+    }
+    if (xwave) stage_input<M>(a.x, a.ldx, a.layer[0].KB * 64, xs, a.xcap, lane);
+    __syncthreads();
+
+    // Layer tail, run by every wave: fixed-order row sums, ReLU, then either
+    // y (last layer) or this tile's rows published as tagged words.
+    auto layer_tail = [&](uint32_t l) {
+        const LayerDev &w = a.layer[l];
+        const uint32_t R = w.R;
+        const bool last = l + 1 == L;
+        reduce_rows<M>(P, a.pcap, R, w.KB, wave, lane, [&](uint32_t m, uint32_t r, float v) {
+            const uint32_t n = t * R + r;
+            v = v > 0.0f ? v : 0.0f;                      // ReLU; +0 for zero, negative and NaN
+            if (last) {
+                if (n < w.N) a.y[int64_t(m) * a.ldy + n] = v;
+            } else {
+                hrow[m * R + r] = v;
+                if (a.hd[l] && n < w.N) a.hd[l][uint64_t(m) * w.N + n] = f32_to_bf16_rne(v);
+            }
+        });
+        if (last) return;
+        __syncthreads();
+        // publish: four rows per 64-bit atomic store, the tag in the sign bits
+        const uint32_t qpt = R / 4;
+        if (threadIdx.x < M * qpt) {
+            const uint32_t m = threadIdx.x / qpt, q = threadIdx.x - m * qpt;
+            const uint32_t n0 = t * R + 4 * q;
+            if (n0 < w.N) {
+                const float *h = hrow + m * R + 4 * q;
+                const uint64_t word = uint64_t(f32_to_bf16_rne(h[0])) | (uint64_t(f32_to_bf16_rne(h[1])) << 16) |
+                                      (uint64_t(f32_to_bf16_rne(h[2])) << 32) |
+                                      (uint64_t(f32_to_bf16_rne(h[3])) << 48);
+                __hip_atomic_store(a.hw[l] + uint64_t(m) * (w.N / 4) + n0 / 4, word | tagmask, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    };
+
+    // The two roles run separate loops with the same sequence of workgroup
+    // barriers (per layer: after the chunks, after the row sums, after the
+    // next layer's x is in LDS), so their registers never overlap.
+    if (xwave) {
+        for (uint32_t l = 0; l < L; ++l) {
+            __syncthreads();
+            layer_tail(l);
+            if (l + 1 < L) {
+                gather_hidden<M>(a.hw[l], a.layer[l].N, tagmask, xs, a.xcap, lane, a.sync);
+                __syncthreads();
+            }
+        }
+    } else {
+        // Loader: walk this wave's chunks of every layer in groups of kUnroll
+        // slots; slot u is refilled right after it is consumed, with the same
+        // slot of the next group (possibly the next layer's).
+        uint32_t ll = 0, gl = 0;             // layer and group to load next
+        ChunkSrc src = layer_src(a, meta, 0);
+        uint32_t gcount = wave_groups(n_chunks(src), wave);
+        auto advance_loader = [&]() {
+            if (++gl == gcount) {
+                gl = 0;
+                if (ll + 1 < L) {
+                    ++ll;
+                    src = layer_src(a, meta, ll);
+                    gcount = wave_groups(n_chunks(src), wave);
+                } else {
+                    gcount = ~0u;            // past the last layer: every further slot is empty
+                    gl = 1u << 24;
+                }
+            }
+        };
+        Slot sl[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) sl[u] = load_chunk(src, wave + kLoadWaves * (gl * kUnroll + u), lane);
+        advance_loader();
+        for (uint32_t l = 0; l < L; ++l) {
+            const LayerDev &w = a.layer[l];
+            const uint32_t KB = w.KB, R = w.R, lgR = w.lgR;
+            const uint32_t groups = wave_groups(n_chunks(layer_src(a, meta, l)), wave);
+            for (uint32_t g = 0; g < groups; ++g) {
+                const uint32_t lbase = wave + kLoadWaves * (gl * kUnroll);
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+                    consume<M>(sl[u], lane, xs, a.xcap, P, a.pcap, 0u, KB, R, lgR);
+                    sl[u] = load_chunk(src, lbase + kLoadWaves * u, lane);
+                }
+                advance_loader();
+            }
+            __syncthreads();
+            layer_tail(l);
+            if (l + 1 < L) __syncthreads();
+        }
+    }
+    if (t == 0 && threadIdx.x == 0)
+        __hip_atomic_store(a.sync, epoch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint32_t *p, uint64_t n) {
+    for (uint64_t i = uint64_t(blockIdx.x) * 256u + threadIdx.x; i < n; i += uint64_t(gridDim.x) * 256u) p[i] = 0u;
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+namespace {
+
+struct MlpPlan {
+    size_t part = 0, act = 0;   // bytes: split partials, one activation buffer
+    size_t words = 0;           // bytes of tagged activation words (all hidden layers)
+    bool fused = false;
+    uint32_t grid = 0, lds = 0, xcap = 0, pcap = 0, rmax = 0;
+};
+
+template <int M>
+bool fused_fits(uint32_t grid, uint32_t lds) {
+    // all workgroups must be resident at once: occupancy x compute units
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return false;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&mlp_fused_kernel<M>),
+                                                     kThreads, lds) != hipSuccess)
+        return false;
+    return uint64_t(per_cu) * uint64_t(cus) >= grid;
+}
+
+bool fused_fits_m(int64_t M, uint32_t grid, uint32_t lds) {
+    switch (M) {
+    case 1: return fused_fits<1>(grid, lds);
+    case 2: return fused_fits<2>(grid, lds);
+    case 3: return fused_fits<3>(grid, lds);
+    case 4: return fused_fits<4>(grid, lds);
+    default: return false;
+    }
+}
+
+// Shapes and buffer sizes; `probe_device` also checks residency (a HIP call).
+ht_status mlp_plan(const ht_packed_weight *const *layers, int32_t L, int64_t M, bool probe_device, MlpPlan *pl) {
+    if (!layers || L <= 0) return HT_EINVAL;
+    if (M <= 0) return HT_ESHAPE;
+    uint32_t kmax = 0, kbmax = 0, rmax = 0, tmax = 0;
+    bool fusable = L <= kMaxLayers && M <= kMaxFusedM;
+    for (int32_t l = 0; l < L; ++l) {
+        const ht_packed_weight *w = layers[l];
+        if (!desc_ok(w)) return HT_EINVAL;
+        if (l && w->K != layers[l - 1]->N) return HT_ESHAPE;
+        const size_t p = linear_ws(w, M);
+        pl->part = p > pl->part ? p : pl->part;
+        const size_t h = align256(size_t(M) * size_t(w->N) * 2u);
+        pl->act = h > pl->act ? h : pl->act;
+        if (l + 1 < L) pl->words += align256(size_t(M) * size_t(w->N) * 2u);
+        kmax = uint32_t(w->K) > kmax ? uint32_t(w->K) : kmax;
+        kbmax = uint32_t(w->K / 64) > kbmax ? uint32_t(w->K / 64) : kbmax;
+        rmax = uint32_t(w->row_tile) > rmax ? uint32_t(w->row_tile) : rmax;
+        tmax = uint32_t(w->n_tiles) > tmax ? uint32_t(w->n_tiles) : tmax;
+        if (w->row_tile < 4) fusable = false;              // four rows per activation word
+    }
+    if (uint64_t(M) * rmax > 64) fusable = false;           // LDS row buffer
+    pl->xcap = kmax;
+    pl->pcap = kbmax + 1;
+    pl->rmax = rmax;
+    pl->grid = tmax;
+    pl->lds = 768u + uint32_t(M) * kmax * 4u + uint32_t(M) * rmax * (kbmax + 1u) * 4u;
+    if (pl->lds > 64u * 1024u) fusable = false;
+    pl->fused = fusable && (!probe_device || fused_fits_m(M, pl->grid, pl->lds));
+    return HT_OK;
+}
+
+size_t mlp_ws_bytes(const MlpPlan &pl) { return kSyncBytes + pl.words + align256(pl.part) + 2 * pl.act; }
+
+template <int M>
+void launch_fused(const MlpArgs &a, uint32_t grid, uint32_t lds, hipStream_t s) {
+    hipLaunchKernelGGL(mlp_fused_kernel<M>, dim3(grid), dim3(kThreads), lds, s, a);
+}
+
+bool al16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+}  // namespace ht
+
+using namespace ht;
+
+extern "C" ht_status ht_mlp_workspace(const ht_packed_weight *const *layers, int32_t n_layers, int64_t M,
+                                      size_t *bytes) {
+    if (!bytes) return HT_EINVAL;
+    MlpPlan pl;
+    ht_status st = mlp_plan(layers, n_layers, M, false, &pl);
+    if (st != HT_OK) return st;
+    *bytes = mlp_ws_bytes(pl);
+    return HT_OK;
+}
+
+extern "C" ht_status ht_workspace_init(void *ws, size_t ws_bytes, ht_stream stream) {
+    if (!ws) return HT_EINVAL;
+    if (!al16(ws) || (ws_bytes % 4u)) return HT_EALIGN;
+    const uint64_t n = ws_bytes / 4u;
+    if (!n) return HT_OK;
+    const uint64_t want = (n + 255) / 256;
+    const uint32_t grid = uint32_t(want < 4096 ? want : 4096);
+    hipLaunchKernelGGL(zero_fill_kernel, dim3(grid), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
+                       static_cast<uint32_t *>(ws), n);
+    HT_LAUNCH_CHECK();
+    return HT_OK;
+}
+
+extern "C" ht_status ht_mlp_forward(const ht_packed_weight *const *layers, int32_t n_layers, const uint16_t *x,
+                                    int64_t M, int64_t ldx, float *y, int64_t ldy, uint16_t *act_dump, int32_t path,
+                                    void *ws, size_t ws_bytes, ht_stream stream) {
+    if (!layers || n_layers <= 0 || !x || !y) return HT_EINVAL;
+    if (path != HT_PATH_AUTO && path != HT_PATH_GEMV && path != HT_PATH_FUSED) return HT_EINVAL;
+    MlpPlan pl;
+    ht_status st = mlp_plan(layers, n_layers, M, false, &pl);
+    if (st != HT_OK) return st;
+    if (ldx < layers[0]->K || ldy < layers[n_layers - 1]->N) return HT_ESHAPE;
+    if (!ws || ws_bytes < mlp_ws_bytes(pl)) return HT_ESMALL;
+    if (!al16(x) || !al16(y) || !al16(ws) || (ldx % 8) || (act_dump && !al16(act_dump))) return HT_EALIGN;
+    for (int32_t l = 0; l < n_layers; ++l) {
+        if (!al16(layers[l]->base)) return HT_EALIGN;
+        if (l + 1 < n_layers && (layers[l]->N % 8)) return HT_EALIGN;
+    }
+    if (path == HT_PATH_FUSED && !pl.fused) return HT_EINVAL;
+    bool fused = pl.fused && path != HT_PATH_GEMV;
+    if (fused) {
+        MlpPlan probe;
+        if (mlp_plan(layers, n_layers, M, true, &probe) != HT_OK || !probe.fused) {
+            if (path == HT_PATH_FUSED) return HT_EINVAL;
+            fused = false;
+        }
+    }
+
+    uint8_t *wsb = static_cast<uint8_t *>(ws);
+    uint8_t *words = wsb + kSyncBytes;
+    uint8_t *part = words + pl.words;
+    uint16_t *ping[2] = {reinterpret_cast<uint16_t *>(part + align256(pl.part)),
+                         reinterpret_cast<uint16_t *>(part + align256(pl.part) + pl.act)};
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+    if (fused) {
+        MlpArgs a;
+        size_t woff = 0, dump_off = 0;
+        for (int32_t l = 0; l < n_layers; ++l) {
+            a.layer[l] = layer_dev(layers[l]);
+            a.hw[l] = nullptr;
+            a.hd[l] = nullptr;
+            if (l + 1 < n_layers) {
+                a.hw[l] = reinterpret_cast<uint64_t *>(words + woff);
+                woff += align256(size_t(M) * size_t(layers[l]->N) * 2u);
+                if (act_dump) a.hd[l] = act_dump + dump_off;
+                dump_off += size_t(M) * size_t(layers[l]->N);
+            }
+        }
+        a.x = x;
+        a.ldx = ldx;
+        a.y = y;
+        a.ldy = ldy;
+        a.sync = reinterpret_cast<uint32_t *>(wsb);
+        a.n_layers = uint32_t(n_layers);
+        a.xcap = pl.xcap;
+        a.pcap = pl.pcap;
+        a.rmax = pl.rmax;
+        switch (M) {
+        case 1: launch_fused<1>(a, pl.grid, pl.lds, s); break;
+        case 2: launch_fused<2>(a, pl.grid, pl.lds, s); break;
+        case 3: launch_fused<3>(a, pl.grid, pl.lds, s); break;
+        default: launch_fused<4>(a, pl.grid, pl.lds, s); break;
+        }
+        HT_LAUNCH_CHECK();
+        return HT_OK;
+    }
+
+    const uint16_t *in = x;
+    int64_t ld_in = ldx;
+    size_t dump_off = 0;
+    for (int32_t l = 0; l < n_layers; ++l) {
+        const ht_packed_weight *w = layers[l];
+        if (l + 1 < n_layers) {
+            uint16_t *out = act_dump ? act_dump + dump_off : ping[l & 1];
+            dump_off += size_t(M) * size_t(w->N);
+            st = run_linear(w, in, M, ld_in, nullptr, out, w->N, HT_ACT_RELU, part, s);
+            if (st != HT_OK) return st;
+            in = out;
+            ld_in = w->N;
+        } else {
+            st = run_linear(w, in, M, ld_in, y, nullptr, ldy, HT_ACT_RELU, part, s);
+            if (st != HT_OK) return st;
+        }
+    }
+    return HT_OK;
+}

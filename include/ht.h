@@ -109,7 +109,11 @@ typedef struct {
 } ht_packed_weight;
 
 enum { HT_ACT_NONE = 0, HT_ACT_RELU = 1 };
-enum { HT_PATH_AUTO = 0, HT_PATH_GEMV = 1 };
+enum {
+    HT_PATH_AUTO = 0,   /* let the library choose                                  */
+    HT_PATH_GEMV = 1,   /* one fused GEMV launch per layer                          */
+    HT_PATH_FUSED = 2   /* ht_mlp_forward only: all layers in one persistent launch */
+};
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char *ht_status_string(ht_status s);
@@ -175,23 +179,45 @@ ht_status ht_linear_forward(const ht_packed_weight *w, const uint16_t *x, int64_
                             int64_t ldx, float *y, int64_t ldy, int32_t act, int32_t path,
                             void *ws, size_t ws_bytes, ht_stream stream);
 
-/* ht_mlp_workspace -- workspace bytes ht_mlp_forward needs. */
+/* ht_mlp_workspace -- workspace bytes ht_mlp_forward needs for M rows. */
 ht_status ht_mlp_workspace(const ht_packed_weight *const *layers, int32_t n_layers,
                            int64_t M, size_t *bytes);
 
+/* ht_workspace_init -- zero-fill a workspace (a fill kernel on `stream`, so it
+ * may be captured in a graph).  ht_mlp_forward needs it once per workspace
+ * and configuration: the workspace holds a call counter and the tagged
+ * activation words of the single-launch path, which every call leaves
+ * consistent for the next call with the same layers and M. */
+ht_status ht_workspace_init(void *ws, size_t ws_bytes, ht_stream stream);
+
 /* ht_mlp_forward -- the page's BenchmarkMLP ("Usage Example": HyperLinear then
  * ReLU, repeated; no bias):  h_0 = x;  h_l = bf16_rne(relu(h_{l-1} . W_l^T))
- * for l < L;  y = relu(h_{L-1} . W_L^T) in fp32.
+ * for l < L;  y = relu(h_{L-1} . W_L^T) in fp32.  Each layer computes exactly
+ * what ht_linear_forward computes (the same fixed-order sums), whichever path
+ * runs.
  *   layers    (host) array of n_layers descriptors; layer l's K must equal
- *             layer l-1's N.
+ *             layer l-1's N; hidden widths must be multiples of 8.
  *   x         bfloat16 [M, ldx];  y fp32 [M, ldy] (ldy >= last layer's N).
  *   act_dump  nullable; if set, bfloat16 [n_layers-1][M][N_l] receives every
  *             intermediate h_l (each layer's slab is M * N_l elements, slabs
  *             packed back to back); the layers then read their input from it.
- *   ws        workspace of ws_bytes >= ht_mlp_workspace(...). */
+ *   path      HT_PATH_AUTO: one persistent launch for all layers when it fits
+ *             (n_layers <= 8, M <= 4, M*K of every layer <= 16384, LDS, and
+ *             every workgroup resident at once), else one launch per layer;
+ *             HT_PATH_GEMV: one launch per layer; HT_PATH_FUSED: the single
+ *             launch or HT_EINVAL if it does not fit.
+ *   ws        workspace of ws_bytes >= ht_mlp_workspace(...), initialised with
+ *             ht_workspace_init before its first use and again whenever it is
+ *             used with other layers or another M.  The single launch passes
+ *             activations between workgroups through tagged words in it; a
+ *             wait for a word is bounded (about 50 ms): if one ever expires,
+ *             the 32-bit word at byte offset 8 of ws becomes nonzero and that
+ *             call's output is invalid (the launch still terminates).
+ * ReLU maps zero, negative values and NaN to +0. */
 ht_status ht_mlp_forward(const ht_packed_weight *const *layers, int32_t n_layers,
                          const uint16_t *x, int64_t M, int64_t ldx, float *y, int64_t ldy,
-                         uint16_t *act_dump, void *ws, size_t ws_bytes, ht_stream stream);
+                         uint16_t *act_dump, int32_t path, void *ws, size_t ws_bytes,
+                         ht_stream stream);
 
 #ifdef __cplusplus
 }

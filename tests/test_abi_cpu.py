@@ -134,5 +134,8 @@ def test_mlp_argument_checks():
     arr = (ctypes.POINTER(B.PackedWeight) * 2)(ctypes.pointer(a), ctypes.pointer(c))
     assert lib.ht_mlp_workspace(arr, 2, 1, ctypes.byref(out)) == 0
     assert out.value > 0
-    assert lib.ht_mlp_forward(arr, 2, 0x200000, 1, 256, 0x300000, 128, None, None, 0, None) == 4
-    assert lib.ht_mlp_forward(arr, 0, 0x200000, 1, 256, 0x300000, 128, None, None, 0, None) == 1
+    assert lib.ht_mlp_forward(arr, 2, 0x200000, 1, 256, 0x300000, 128, None, 0, None, 0, None) == 4
+    assert lib.ht_mlp_forward(arr, 2, 0x200000, 1, 256, 0x300000, 128, None, 7, 0x400000, 1 << 20, None) == 1
+    assert lib.ht_mlp_forward(arr, 0, 0x200000, 1, 256, 0x300000, 128, None, 0, None, 0, None) == 1
+    assert lib.ht_workspace_init(None, 256, None) == 1
+    assert lib.ht_workspace_init(0x400004, 256, None) == 3

@@ -271,12 +271,15 @@ def mlp4096(orc):
     return Ws, fmts, pws
 
 
-@pytest.mark.parametrize("M", [1, 32])
-def test_mlp_teacher_forced(orc, mlp4096, M):
+@pytest.mark.parametrize("M,path", [(1, B.HT_PATH_AUTO), (1, B.HT_PATH_GEMV), (2, B.HT_PATH_FUSED),
+                                    (4, B.HT_PATH_AUTO), (32, B.HT_PATH_AUTO)])
+def test_mlp_teacher_forced(orc, mlp4096, M, path):
     Ws, fmts, pws = mlp4096
     x = wl.to_bf16_bits(wl.mlp_activation(M))
-    y, dumps = api.mlp(pws, bf16_gpu(x), dump=True)
+    ws = api.mlp_workspace(pws, M, dev())
+    y, dumps = api.mlp(pws, bf16_gpu(x), dump=True, ws=ws, path=path)
     torch.cuda.synchronize()
+    assert int(ws[8:12].view(torch.int32).item()) == 0       # no barrier wait expired
     h_in = x
     for l in range(wl.MLP_DEPTH):
         z = orc.linear(Ws[l], fmts[l], h_in)
@@ -290,6 +293,54 @@ def test_mlp_teacher_forced(orc, mlp4096, M):
             h_in = h_gpu
         else:
             check_close(y.cpu().numpy(), np.maximum(z, 0), f"last layer M={M}")
+
+
+@pytest.mark.parametrize("M", [1, 2])
+def test_mlp_fused_equals_per_layer(mlp4096, M):
+    """The single persistent launch computes exactly what one launch per
+    layer computes (same block partials, same fixed-order row sums), and is
+    bitwise reproducible over repeated calls on one workspace."""
+    _, _, pws = mlp4096
+    x = bf16_gpu(wl.to_bf16_bits(wl.mlp_activation(M, seed=3)))
+    ws = api.mlp_workspace(pws, M, dev())
+    y_ref = api.mlp(pws, x, ws=ws, path=B.HT_PATH_GEMV).clone()
+    for _ in range(3):
+        y = api.mlp(pws, x, ws=ws, path=B.HT_PATH_FUSED)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref)
+    assert int(ws[8:12].view(torch.int32).item()) == 0
+
+
+def test_mlp_fused_ragged_layers(orc):
+    """Layers of different widths (tiles per layer differ; workgroups without
+    a tile in a layer only take part in its barrier), ragged last tile."""
+    rng = np.random.default_rng(71)
+    dims = [512, 1024, 256, 200]   # 64, 16 and 13 row tiles; the last one ragged
+    Ws = [(rng.standard_t(4, size=(dims[i + 1], dims[i])) * 0.03).astype(np.float32) for i in range(3)]
+    fmts = [orc.plan(W) for W in Ws]
+    pws = [api.pack(gpu(W), gpu(f)) for W, f in zip(Ws, fmts)]
+    x = wl.to_bf16_bits(rng.normal(size=(2, 512)).astype(np.float32))
+    ws = api.mlp_workspace(pws, 2, dev())
+    y_f, d_f = api.mlp(pws, bf16_gpu(x), dump=True, ws=ws, path=B.HT_PATH_FUSED)
+    y_g, d_g = api.mlp(pws, bf16_gpu(x), dump=True, ws=ws, path=B.HT_PATH_GEMV)
+    torch.cuda.synchronize()
+    assert torch.equal(y_f, y_g)
+    for a_, b_ in zip(d_f, d_g):
+        assert torch.equal(a_, b_)
+    h1 = d_f[-1].cpu().view(torch.int16).numpy().view(np.uint16)
+    check_close(y_f.cpu().numpy(), np.maximum(orc.linear(Ws[-1], fmts[-1], h1), 0), "last layer")
+    assert int(ws[8:12].view(torch.int32).item()) == 0
+
+
+def test_mlp_fused_refuses_what_does_not_fit(mlp4096):
+    """M = 4 at width 4096 needs 64 KiB of LDS for x alone: HT_PATH_FUSED
+    reports HT_EINVAL and HT_PATH_AUTO runs one launch per layer."""
+    _, _, pws = mlp4096
+    x = bf16_gpu(wl.to_bf16_bits(wl.mlp_activation(4)))
+    ws = api.mlp_workspace(pws, 4, dev())
+    with pytest.raises(B.HTError) as e:
+        api.mlp(pws, x, ws=ws, path=B.HT_PATH_FUSED)
+    assert e.value.code == 1
 
 
 def test_mlp_end_to_end_info(orc, mlp4096):
