@@ -5,10 +5,13 @@
 // tile g of each layer (the grid is the largest layer's tile count, and all
 // workgroups are resident together).  15 of its 16 wavefronts stream the
 // tile's weight chunks: each walks one sequence of chunks across all layers
-// in groups of 8 register slots and refills slot u, as soon as it has been
-// consumed, with the chunk one group ahead -- so layer l+1's weights are in
-// flight while layer l finishes.  The 16th wavefront moves activations; it
-// holds no weight loads, so waiting for activations never waits for weights.
+// (interleaved with the other waves, so every wave gets a mix of formats) in
+// groups of two register slots, and refills slot u, as soon as it has been
+// consumed, with the chunk one group ahead, possibly the next layer's.  A
+// short window keeps each wave's requests flowing steadily; on the measured
+// part, deeper windows (4 or 8 slots) streamed more slowly.  The 16th
+// wavefront stages the first layer's input and joins the row sums and the
+// activation exchange.
 //
 // Activation exchange without a barrier or cache flushes: a hidden layer's
 // outputs are ReLU values, so the sign bit of each bfloat16 is free.  Four
@@ -19,9 +22,10 @@
 // loads and re-reads any word whose tag is not yet the current one.  Every
 // word is written exactly once per call, so a matching tag means the word
 // holds this call's values (single-copy atomicity of the 64-bit access).
-// The wait is bounded (~50 ms); if it ever expires, a flag word in the
-// workspace is set and that call's output is invalid, but the launch still
-// terminates.
+// All 16 wavefronts take part in reading a layer (one word per lane per
+// round for the 4096-wide MLP at batch 1).  The wait is bounded (~50 ms); if
+// it ever expires, a flag word in the workspace is set and that call's output
+// is invalid, but the launch still terminates.
 //
 // Per-layer path: one single-layer launch per layer (linear.hip), used when
 // the fused launch does not fit (layer count, batch, LDS, residency, tiles).
@@ -34,8 +38,8 @@ constexpr int kMaxLayers = 8;
 constexpr int kMaxFusedM = 4;
 constexpr uint32_t kSpinLimit = 1u << 21;   // x ~64 clocks per poll: ~50 ms
 constexpr uint32_t kSyncBytes = 256;        // [0] call counter, [2] expired-wait flag
-constexpr uint32_t kLoadWaves = kWaves - 1; // waves streaming weights; the last one moves activations
-constexpr uint32_t kXWords = 16;            // activation words read per lane per round
+constexpr uint32_t kLoadWaves = kWaves - 1; // waves streaming weights; the last one stages the input
+constexpr int kSlots = 2;                   // chunks in flight per loading wave
 
 struct MlpArgs {
     LayerDev layer[kMaxLayers];
@@ -56,7 +60,7 @@ struct MlpArgs {
 // tile (at least one, possibly all-empty, so every wave stays in step).
 __device__ __forceinline__ uint32_t wave_groups(uint32_t C, uint32_t wave) {
     const uint32_t J = C > wave ? (C - wave + kLoadWaves - 1) / kLoadWaves : 0u;
-    const uint32_t g = (J + kUnroll - 1) / kUnroll;
+    const uint32_t g = (J + kSlots - 1) / kSlots;
     return g ? g : 1u;
 }
 
@@ -114,46 +118,30 @@ __device__ __forceinline__ bool word_ready(uint64_t w, uint64_t tagmask) {
 }
 
 // Hidden layer's activations (tagged words [M][N/4]) -> LDS fp32 [M][xcap].
-// Rounds of kXWords 64-bit atomic loads per lane, re-reading stale words.
+// Wave w reads words w*64 + lane, (w + 16)*64 + lane, ... with 64-bit atomic
+// loads and re-reads a word until its tag is current.
 template <int M>
 __device__ __forceinline__ void gather_hidden(const uint64_t *words, uint32_t N, uint64_t tagmask, float *xs,
-                                              uint32_t xstride, uint32_t lane, uint32_t *sync) {
+                                              uint32_t xstride, uint32_t lane, uint32_t wave, uint32_t *sync) {
     const uint32_t per_row = N / 4, total = M * per_row;
-    for (uint32_t base = 0; base < total; base += 64 * kXWords) {
-        uint64_t v[kXWords];
-#pragma unroll
-        for (uint32_t j = 0; j < kXWords; ++j) {
-            const uint32_t i = base + j * 64 + lane;
-            v[j] = i < total ? __hip_atomic_load(words + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : tagmask;
-        }
+    for (uint32_t i = wave * 64 + lane; i - lane < total; i += kWaves * 64) {   // i - lane is wave-uniform
+        uint64_t v = i < total ? __hip_atomic_load(words + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : tagmask;
         uint32_t n = 0;
-        for (;;) {
-            bool ok = true;
-#pragma unroll
-            for (uint32_t j = 0; j < kXWords; ++j) ok = ok && word_ready(v[j], tagmask);
-            if (__all(ok)) break;
+        while (!__all(word_ready(v, tagmask))) {
             if (++n > kSpinLimit) {
                 if (lane == 0) __hip_atomic_store(sync + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 break;
             }
             __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-            for (uint32_t j = 0; j < kXWords; ++j) {
-                const uint32_t i = base + j * 64 + lane;
-                if (i < total && !word_ready(v[j], tagmask))
-                    v[j] = __hip_atomic_load(words + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+            if (i < total && !word_ready(v, tagmask))
+                v = __hip_atomic_load(words + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-#pragma unroll
-        for (uint32_t j = 0; j < kXWords; ++j) {
-            const uint32_t i = base + j * 64 + lane;
-            if (i < total) {
-                const uint32_t m = i / per_row, q = i - m * per_row;
-                const uint64_t w = v[j] & ~0x8000800080008000ull;
-                const uint32_t lo = uint32_t(w), hi = uint32_t(w >> 32);
-                *reinterpret_cast<float4 *>(xs + m * xstride + q * 4) =
-                    make_float4(bf16_lo(lo), bf16_hi(lo), bf16_lo(hi), bf16_hi(hi));
-            }
+        if (i < total) {
+            const uint32_t m = i / per_row, q = i - m * per_row;
+            const uint64_t w = v & ~0x8000800080008000ull;
+            const uint32_t lo = uint32_t(w), hi = uint32_t(w >> 32);
+            *reinterpret_cast<float4 *>(xs + m * xstride + q * 4) =
+                make_float4(bf16_lo(lo), bf16_hi(lo), bf16_lo(hi), bf16_hi(hi));
         }
     }
 }
@@ -232,12 +220,12 @@ __global__ __launch_bounds__(kThreads) void mlp_fused_kernel(MlpArgs a) {
             __syncthreads();
             layer_tail(l);
             if (l + 1 < L) {
-                gather_hidden<M>(a.hw[l], a.layer[l].N, tagmask, xs, a.xcap, lane, a.sync);
+                gather_hidden<M>(a.hw[l], a.layer[l].N, tagmask, xs, a.xcap, lane, wave, a.sync);
                 __syncthreads();
             }
         }
     } else {
-        // Loader: walk this wave's chunks of every layer in groups of kUnroll
+        // Loader: walk this wave's chunks of every layer in groups of kSlots
         // slots; slot u is refilled right after it is consumed, with the same
         // slot of the next group (possibly the next layer's).
         uint32_t ll = 0, gl = 0;             // layer and group to load next
@@ -256,18 +244,18 @@ __global__ __launch_bounds__(kThreads) void mlp_fused_kernel(MlpArgs a) {
                 }
             }
         };
-        Slot sl[kUnroll];
+        Slot sl[kSlots];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) sl[u] = load_chunk(src, wave + kLoadWaves * (gl * kUnroll + u), lane);
+        for (int u = 0; u < kSlots; ++u) sl[u] = load_chunk(src, wave + kLoadWaves * (gl * kSlots + u), lane);
         advance_loader();
         for (uint32_t l = 0; l < L; ++l) {
             const LayerDev &w = a.layer[l];
             const uint32_t KB = w.KB, R = w.R, lgR = w.lgR;
             const uint32_t groups = wave_groups(n_chunks(layer_src(a, meta, l)), wave);
             for (uint32_t g = 0; g < groups; ++g) {
-                const uint32_t lbase = wave + kLoadWaves * (gl * kUnroll);
+                const uint32_t lbase = wave + kLoadWaves * (gl * kSlots);
 #pragma unroll
-                for (int u = 0; u < kUnroll; ++u) {
+                for (int u = 0; u < kSlots; ++u) {
                     consume<M>(sl[u], lane, xs, a.xcap, P, a.pcap, 0u, KB, R, lgR);
                     sl[u] = load_chunk(src, lbase + kLoadWaves * u, lane);
                 }
@@ -275,7 +263,10 @@ __global__ __launch_bounds__(kThreads) void mlp_fused_kernel(MlpArgs a) {
             }
             __syncthreads();
             layer_tail(l);
-            if (l + 1 < L) __syncthreads();
+            if (l + 1 < L) {
+                gather_hidden<M>(a.hw[l], a.layer[l].N, tagmask, xs, a.xcap, lane, wave, a.sync);
+                __syncthreads();
+            }
         }
     }
     if (t == 0 && threadIdx.x == 0)
