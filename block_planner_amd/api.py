@@ -78,12 +78,12 @@ def workspace(nbytes: int, device) -> torch.Tensor | None:
 
 
 def linear(pw: PackedLinear, x: torch.Tensor, act: int = B.HT_ACT_NONE, out: torch.Tensor | None = None,
-           ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+           ws: torch.Tensor | None = None, path: int = B.HT_PATH_AUTO, stream=None) -> torch.Tensor:
     M = x.shape[0]
     y = torch.empty((M, pw.N), dtype=torch.float32, device=x.device) if out is None else out
     if ws is None:
-        ws = workspace(B.ht_linear_workspace(pw.desc, M), x.device)
-    B.ht_linear_forward(pw.desc, x, y, act=act, ws=ws, stream=stream)
+        ws = workspace(B.ht_linear_workspace(pw.desc, M, path), x.device)
+    B.ht_linear_forward(pw.desc, x, y, act=act, path=path, ws=ws, stream=stream)
     return y
 
 

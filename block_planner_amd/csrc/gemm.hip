@@ -1,0 +1,358 @@
+// gemm.hip -- the mixed-format linear for many rows of x (prefill):
+// y[m, n] = sum over K-blocks kb of  blk(m, n, kb)  with fp32 accumulation,
+// where an integer block contributes s * (sum_i q_i * x[m, 64kb+i]) and a
+// float block sum_i w_i * x[m, 64kb+i] (HyperTensor 1.0.1 page: "fused
+// mixed-precision operators" run the plan; "Key Features": HyperLinear).
+//
+// A workgroup owns a 32*MS x 64 tile of y and walks K one 64-wide block at a
+// time.  Per step it dequantises the tile's 64 weight blocks (one per output
+// column) into LDS as bfloat16:
+//   INT4 / INT8   the codes themselves (|q| <= 127 is exact in bfloat16);
+//                 the block's scale multiplies the 64-term partial afterwards;
+//   BF16          the values;
+//   FP16 / FP32   two planes, hi = w with the low 16 bits cleared and
+//                 lo = bf16(w - hi) (exact for FP16; 16 significant bits for
+//                 FP32), scale 1.
+// The partial of each step comes from bf16 MFMAs (v_mfma_f32_16x16x32_bf16)
+// with a fresh accumulator; the lo plane is multiplied only for 16-column
+// groups that hold an FP16 or FP32 block in that step.  Then every output
+// element adds scale[n] * partial[m, n] in fp32, in K order.
+//
+// Pipelining: two LDS stages.  While the MFMAs run on stage kb, the loads of
+// step kb+1 (x tile and packed blocks) are in flight in registers; they are
+// dequantised into the other stage after the MFMAs, then one barrier.
+#include "gemv_common.h"
+#include "linear_host.h"
+
+namespace ht {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr uint32_t kGemmBN = 64;          // output columns (weight rows) per workgroup
+constexpr uint32_t kGemmThreads = 256;    // 4 waves in a 2 x 2 arrangement
+constexpr uint32_t kLdsRow = 72;          // bfloat16 per LDS row: 64 + 8 of padding
+
+struct GemmArgs {
+    LayerDev w;
+    const uint16_t *x;
+    int64_t ldx;
+    float *y;
+    int64_t ldy;
+    uint32_t M;
+    int act;
+};
+
+// One pipeline stage in LDS.
+template <int MS>
+struct GemmStage {
+    uint16_t xs[32 * MS][kLdsRow];     // x tile, bfloat16
+    uint16_t whi[kGemmBN][kLdsRow];    // weight planes, bfloat16, row = output column
+    uint16_t wlo[kGemmBN][kLdsRow];
+    float scale[kGemmBN];
+    uint32_t need_lo[4];               // per 16-column group
+};
+
+template <int MS>
+constexpr uint32_t gemm_lds_bytes() { return 2u * uint32_t(sizeof(GemmStage<MS>)); }
+
+// The packed block (or its absence) one thread dequantises in a step: block
+// quarter `part` (16 of the 64 entries) of output column n.
+struct BlockLoad {
+    uint4 p[4];        // payload bytes of this quarter (8 / 16 / 32 / 32 / 64 bytes by format)
+    float sc;
+    uint32_t r;        // row within the tile (from the block id)
+    int f;             // format, or 5 for "no block": the column is zero in this step
+};
+
+__device__ __forceinline__ uint16_t bf16_trunc_bits(float v) {
+    const uint32_t u = __float_as_uint(v);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;   // NaN stays NaN
+    return uint16_t(u >> 16);
+}
+
+// hi / lo planes of a float entry; lo is 0 when hi is not finite.
+__device__ __forceinline__ void split_hi_lo(float w, uint16_t &hi, uint16_t &lo) {
+    hi = bf16_trunc_bits(w);
+    const float h = __uint_as_float(uint32_t(hi) << 16);
+    lo = (__float_as_uint(h) & 0x7f800000u) == 0x7f800000u ? uint16_t(0) : f32_to_bf16_rne(w - h);
+}
+
+// Signed 4-bit field k of v.
+__device__ __forceinline__ int q4(uint32_t v, int k) { return int32_t(v << (28 - 4 * k)) >> 28; }
+__device__ __forceinline__ uint16_t bf16_of_int(int q) { return uint16_t(__float_as_uint(float(q)) >> 16); }
+
+template <int MS>
+__global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
+    extern __shared__ __align__(16) unsigned char gemm_lds[];
+    GemmStage<MS> *stage = reinterpret_cast<GemmStage<MS> *>(gemm_lds);
+    constexpr uint32_t BM = 32 * MS;
+    const LayerDev &w = a.w;
+    const uint32_t tid = threadIdx.x, lane = tid & 63;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t wm = wave >> 1, wn = wave & 1;          // wave tile: rows [wm*16*MS, +16*MS), cols [wn*32, +32)
+    const uint32_t n0 = blockIdx.x * kGemmBN, m0 = blockIdx.y * BM;
+    const uint32_t KB = w.KB, R = w.R;
+
+    // ---- dequantisation role: thread -> (column block gb, quarter part) ----
+    const uint32_t gb = tid >> 2, part = tid & 3;
+    const uint32_t tile = n0 / R + gb / R, bi = gb % R;    // tile of the column, block slot within it
+    const bool tile_ok = tile < w.T;
+    const uint32_t *kbidx = reinterpret_cast<const uint32_t *>(w.base + w.off_kbidx);
+    uint32_t cur[5];                                        // kbidx[f][tile*KB + kb] for the step being loaded
+#pragma unroll
+    for (int f = 0; f < 5; ++f) cur[f] = tile_ok ? kbidx[uint64_t(f) * w.nk + uint64_t(tile) * KB] : 0u;
+
+    auto load_block = [&](uint32_t kb) -> BlockLoad {
+        BlockLoad b;
+        b.f = 5;
+        b.r = bi;
+        b.sc = 1.0f;
+        uint32_t nxt[5];
+#pragma unroll
+        for (int f = 0; f < 5; ++f)
+            nxt[f] = tile_ok ? kbidx[uint64_t(f) * w.nk + uint64_t(tile) * KB + kb + 1] : 0u;
+        uint32_t cum = 0, blk = 0;
+#pragma unroll
+        for (int f = 0; f < 5; ++f) {
+            const uint32_t c = nxt[f] - cur[f];
+            if (b.f == 5 && bi < cum + c) {
+                b.f = f;
+                blk = cur[f] + (bi - cum);
+            }
+            cum += c;
+        }
+#pragma unroll
+        for (int f = 0; f < 5; ++f) cur[f] = nxt[f];
+        b.p[0] = b.p[1] = b.p[2] = b.p[3] = make_uint4(0, 0, 0, 0);
+        if (b.f < 5) {
+            b.r = reinterpret_cast<const uint16_t *>(w.base + w.off_ids[b.f])[blk] & (R - 1u);
+            const uint8_t *pay = w.base + w.off_pay[b.f] + uint64_t(blk) * uint32_t(pay_bytes(b.f));
+            switch (b.f) {
+            case 0: {   // quarter p: bytes [8p, 8p+8)
+                const uint2 v = *reinterpret_cast<const uint2 *>(pay + 8 * part);
+                b.p[0] = make_uint4(v.x, v.y, 0, 0);
+                b.sc = reinterpret_cast<const float *>(w.base + w.off_scale[0])[blk];
+                break;
+            }
+            case 1:
+                b.p[0] = *reinterpret_cast<const uint4 *>(pay + 16 * part);
+                b.sc = reinterpret_cast<const float *>(w.base + w.off_scale[1])[blk];
+                break;
+            case 2:
+            case 3:
+                b.p[0] = *reinterpret_cast<const uint4 *>(pay + 32 * part);
+                b.p[1] = *reinterpret_cast<const uint4 *>(pay + 32 * part + 16);
+                break;
+            default:
+#pragma unroll
+                for (int j = 0; j < 4; ++j) b.p[j] = *reinterpret_cast<const uint4 *>(pay + 64 * part + 16 * j);
+                break;
+            }
+        }
+        return b;
+    };
+
+    // Dequantise into stage st: entries [16*part, 16*part + 16) of column gb
+    // (INT4 quarters cover two runs of 8, see the nibble order of the layout).
+    auto store_block = [&](const BlockLoad &b, GemmStage<MS> &st) {
+        const uint32_t col = (gb / R) * R + b.r;               // column within the workgroup's 64
+        uint16_t hi[16], lo[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) lo[i] = 0;
+        const uint32_t u[16] = {b.p[0].x, b.p[0].y, b.p[0].z, b.p[0].w, b.p[1].x, b.p[1].y, b.p[1].z, b.p[1].w,
+                                b.p[2].x, b.p[2].y, b.p[2].z, b.p[2].w, b.p[3].x, b.p[3].y, b.p[3].z, b.p[3].w};
+        uint32_t k0 = 16 * part, k1 = k0 + 8;                  // where the two runs of 8 go
+        switch (b.f) {
+        case 0:
+            // bytes j = 8p..8p+7: low nibble -> entry 32*(j/16) + j%16, high -> +16
+            k0 = 32 * (part >> 1) + 8 * (part & 1);
+            k1 = k0 + 16;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t byte = (u[i >> 2] >> (8 * (i & 3))) & 0xffu;
+                hi[i] = bf16_of_int(q4(byte, 0));
+                hi[8 + i] = bf16_of_int(q4(byte, 1));
+            }
+            break;
+        case 1:
+#pragma unroll
+            for (int i = 0; i < 16; ++i) hi[i] = bf16_of_int(int8_t(u[i >> 2] >> (8 * (i & 3))));
+            break;
+        case 2:
+#pragma unroll
+            for (int i = 0; i < 16; ++i) hi[i] = uint16_t(u[i >> 1] >> (16 * (i & 1)));
+            break;
+        case 3:
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                split_hi_lo(float(__builtin_bit_cast(_Float16, uint16_t(u[i >> 1] >> (16 * (i & 1))))), hi[i], lo[i]);
+            break;
+        case 4:
+#pragma unroll
+            for (int i = 0; i < 16; ++i) split_hi_lo(__uint_as_float(u[i]), hi[i], lo[i]);
+            break;
+        default:
+#pragma unroll
+            for (int i = 0; i < 16; ++i) hi[i] = 0;
+            break;
+        }
+        uint4 *dh0 = reinterpret_cast<uint4 *>(&st.whi[col][k0]);
+        uint4 *dh1 = reinterpret_cast<uint4 *>(&st.whi[col][k1]);
+        uint4 *dl0 = reinterpret_cast<uint4 *>(&st.wlo[col][k0]);
+        uint4 *dl1 = reinterpret_cast<uint4 *>(&st.wlo[col][k1]);
+        auto pk = [](const uint16_t *h) {
+            return make_uint4(h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16), h[4] | (uint32_t(h[5]) << 16),
+                              h[6] | (uint32_t(h[7]) << 16));
+        };
+        *dh0 = pk(hi);
+        *dh1 = pk(hi + 8);
+        *dl0 = pk(lo);
+        *dl1 = pk(lo + 8);
+        if (part == 0) st.scale[col] = b.sc;
+        // a 16-column group is one wave's 16 column blocks: does any need the lo plane?
+        const bool flt = b.f == 3 || b.f == 4;
+        const bool any = __any(flt);
+        if (lane == 0) st.need_lo[wave] = any ? 1u : 0u;
+    };
+
+    // ---- x tile: BM rows x 64 entries, 16 bytes per load ----
+    constexpr uint32_t kXLoads = BM * 8 / kGemmThreads;     // = MS
+    auto load_x = [&](uint32_t kb, uint4 (&xv)[kXLoads]) {
+#pragma unroll
+        for (uint32_t j = 0; j < kXLoads; ++j) {
+            const uint32_t idx = tid + kGemmThreads * j, row = idx >> 3, seg = idx & 7;
+            const uint32_t m = m0 + row;
+            xv[j] = m < a.M ? *reinterpret_cast<const uint4 *>(a.x + int64_t(m) * a.ldx + kb * 64 + seg * 8)
+                            : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto store_x = [&](const uint4 (&xv)[kXLoads], GemmStage<MS> &st) {
+#pragma unroll
+        for (uint32_t j = 0; j < kXLoads; ++j) {
+            const uint32_t idx = tid + kGemmThreads * j, row = idx >> 3, seg = idx & 7;
+            *reinterpret_cast<uint4 *>(&st.xs[row][seg * 8]) = xv[j];
+        }
+    };
+
+    f32x4 acc[MS][2];
+#pragma unroll
+    for (int i = 0; i < MS; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    {   // prologue: step 0 into stage 0
+        uint4 xv[kXLoads];
+        load_x(0, xv);
+        const BlockLoad b = load_block(0);
+        store_x(xv, stage[0]);
+        store_block(b, stage[0]);
+    }
+    __syncthreads();
+
+    const uint32_t lr = lane & 15, lk = (lane >> 4) * 8;    // MFMA operand row / first k of this lane
+    for (uint32_t kb = 0; kb < KB; ++kb) {
+        GemmStage<MS> &st = stage[kb & 1];
+        const bool more = kb + 1 < KB;
+        uint4 xv[kXLoads];
+        BlockLoad b;
+        if (more) {
+            load_x(kb + 1, xv);
+            b = load_block(kb + 1);
+        }
+        // MFMAs on this stage
+        bf16x8 A[MS][2];
+#pragma unroll
+        for (int i = 0; i < MS; ++i)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                A[i][h] = *reinterpret_cast<const bf16x8 *>(&st.xs[wm * 16 * MS + 16 * i + lr][32 * h + lk]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t c0 = wn * 32 + 16 * j;
+            const bf16x8 Bh0 = *reinterpret_cast<const bf16x8 *>(&st.whi[c0 + lr][lk]);
+            const bf16x8 Bh1 = *reinterpret_cast<const bf16x8 *>(&st.whi[c0 + lr][32 + lk]);
+            const float sc = st.scale[c0 + lr];
+            const bool lo = __builtin_amdgcn_readfirstlane(st.need_lo[c0 >> 4]) != 0u;
+            bf16x8 Bl0, Bl1;
+            if (lo) {
+                Bl0 = *reinterpret_cast<const bf16x8 *>(&st.wlo[c0 + lr][lk]);
+                Bl1 = *reinterpret_cast<const bf16x8 *>(&st.wlo[c0 + lr][32 + lk]);
+            }
+#pragma unroll
+            for (int i = 0; i < MS; ++i) {
+                f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][0], Bh0, (f32x4{0.f, 0.f, 0.f, 0.f}), 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][1], Bh1, c, 0, 0, 0);
+                if (lo) {
+                    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][0], Bl0, c, 0, 0, 0);
+                    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][1], Bl1, c, 0, 0, 0);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(sc, c[e], acc[i][j][e]);
+            }
+        }
+        if (more) {
+            GemmStage<MS> &nx = stage[(kb + 1) & 1];
+            store_x(xv, nx);
+            store_block(b, nx);
+        }
+        __syncthreads();
+    }
+
+    // ---- output: lane holds column lr, rows 4*(lane/16) + e of each 16x16 tile ----
+#pragma unroll
+    for (int i = 0; i < MS; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t n = n0 + wn * 32 + 16 * j + lr;
+            if (n >= w.N) continue;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t m = m0 + wm * 16 * MS + 16 * i + 4 * (lane >> 4) + e;
+                float v = acc[i][j][e];
+                if (a.act == HT_ACT_RELU) v = v > 0.0f ? v : 0.0f;   // +0 for zero, negative and NaN
+                if (m < a.M) a.y[int64_t(m) * a.ldy + n] = v;
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+namespace {
+
+template <int MS>
+void launch_gemm(const GemmArgs &a, hipStream_t s) {
+    static bool attr = false;   // dynamic LDS above 64 KiB must be allowed once per kernel
+    if (!attr) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_kernel<MS>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(gemm_lds_bytes<MS>()));
+        attr = true;
+    }
+    const dim3 grid((a.w.N + kGemmBN - 1) / kGemmBN, (a.M + 32 * MS - 1) / (32 * MS));
+    hipLaunchKernelGGL(gemm_kernel<MS>, grid, dim3(kGemmThreads), gemm_lds_bytes<MS>(), s, a);
+}
+
+}  // namespace
+
+ht_status run_gemm(const ht_packed_weight *w, const uint16_t *x, int64_t M, int64_t ldx, float *y, int64_t ldy,
+                   int act, hipStream_t s) {
+    GemmArgs a;
+    a.w = layer_dev(w);
+    a.x = x;
+    a.ldx = ldx;
+    a.y = y;
+    a.ldy = ldy;
+    a.act = act;
+    // row tiles of at most 65535 x-row tiles per launch (grid y limit)
+    for (int64_t m0 = 0; m0 < M; m0 += 65535 * 32) {
+        const int64_t Mt = M - m0 < 65535 * 32 ? M - m0 : 65535 * 32;
+        a.x = x + m0 * ldx;
+        a.y = y + m0 * ldy;
+        a.M = uint32_t(Mt);
+        if (Mt >= 128) launch_gemm<4>(a, s);
+        else if (Mt >= 64) launch_gemm<2>(a, s);
+        else launch_gemm<1>(a, s);
+        HT_LAUNCH_CHECK();
+    }
+    return HT_OK;
+}
+
+}  // namespace ht

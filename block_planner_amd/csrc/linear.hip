@@ -224,11 +224,14 @@ using namespace ht;
 
 static bool al16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+static bool path_ok(int32_t path) { return path == HT_PATH_AUTO || path == HT_PATH_GEMV || path == HT_PATH_GEMM; }
+
 extern "C" ht_status ht_linear_workspace(const ht_packed_weight *w, int64_t M, int32_t path, size_t *bytes) {
     if (!bytes || !desc_ok(w)) return HT_EINVAL;
     if (M <= 0) return HT_ESHAPE;
-    if (path != HT_PATH_AUTO && path != HT_PATH_GEMV) return HT_EINVAL;
-    *bytes = linear_ws(w, M);
+    if (!path_ok(path)) return HT_EINVAL;
+    if (path == HT_PATH_AUTO) path = auto_linear_path(M);
+    *bytes = path == HT_PATH_GEMM ? 0 : linear_ws(w, M);
     return HT_OK;
 }
 
@@ -237,9 +240,11 @@ extern "C" ht_status ht_linear_forward(const ht_packed_weight *w, const uint16_t
                                        size_t ws_bytes, ht_stream stream) {
     if (!desc_ok(w) || !x || !y) return HT_EINVAL;
     if (act != HT_ACT_NONE && act != HT_ACT_RELU) return HT_EINVAL;
-    if (path != HT_PATH_AUTO && path != HT_PATH_GEMV) return HT_EINVAL;
+    if (!path_ok(path)) return HT_EINVAL;
     if (M <= 0 || ldx < w->K || ldy < w->N) return HT_ESHAPE;
     if (!al16(x) || !al16(y) || (ldx % 8) || !al16(w->base)) return HT_EALIGN;
+    if (path == HT_PATH_AUTO) path = auto_linear_path(M);
+    if (path == HT_PATH_GEMM) return run_gemm(w, x, M, ldx, y, ldy, act, reinterpret_cast<hipStream_t>(stream));
     const size_t need = linear_ws(w, M);
     if (need && (!ws || ws_bytes < need)) return HT_ESMALL;
     if (ws && !al16(ws)) return HT_EALIGN;

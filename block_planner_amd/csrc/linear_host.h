@@ -18,4 +18,11 @@ size_t linear_ws(const ht_packed_weight *w, int64_t M);
 ht_status run_linear(const ht_packed_weight *w, const uint16_t *x, int64_t M, int64_t ldx, float *y,
                      uint16_t *ybf, int64_t ldy, int act, void *ws, hipStream_t s);
 
+// Enqueue one linear on the MFMA path (fp32 y).  Arguments are assumed checked.
+ht_status run_gemm(const ht_packed_weight *w, const uint16_t *x, int64_t M, int64_t ldx, float *y, int64_t ldy,
+                   int act, hipStream_t s);
+
+// The path HT_PATH_AUTO resolves to for one linear over M rows.
+inline int32_t auto_linear_path(int64_t M) { return M >= 64 ? HT_PATH_GEMM : HT_PATH_GEMV; }
+
 }  // namespace ht

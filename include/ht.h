@@ -112,7 +112,8 @@ enum { HT_ACT_NONE = 0, HT_ACT_RELU = 1 };
 enum {
     HT_PATH_AUTO = 0,   /* let the library choose                                  */
     HT_PATH_GEMV = 1,   /* one fused GEMV launch per layer                          */
-    HT_PATH_FUSED = 2   /* ht_mlp_forward only: all layers in one persistent launch */
+    HT_PATH_FUSED = 2,  /* ht_mlp_forward only: all layers in one persistent launch */
+    HT_PATH_GEMM = 3    /* ht_linear_forward only: LDS dequantisation + bf16 MFMA   */
 };
 
 /* Human-readable name of a status code (static storage; never NULL). */
@@ -160,7 +161,8 @@ ht_status ht_pack(const float *W, int64_t N, int64_t K, int64_t ldw,
                   const uint8_t *fmt_map, int64_t row_tile, const int64_t counts5[5],
                   void *buf, size_t buf_bytes, ht_packed_weight *desc, ht_stream stream);
 
-/* ht_linear_workspace -- workspace bytes ht_linear_forward needs for M rows. */
+/* ht_linear_workspace -- workspace bytes ht_linear_forward needs for M rows
+ * on `path` (HT_PATH_AUTO, HT_PATH_GEMV or HT_PATH_GEMM). */
 ht_status ht_linear_workspace(const ht_packed_weight *w, int64_t M, int32_t path,
                               size_t *bytes);
 
@@ -173,8 +175,15 @@ ht_status ht_linear_workspace(const ht_packed_weight *w, int64_t M, int32_t path
  *          block's 64-term partial sum.  The result is bitwise reproducible
  *          run to run (fixed-order reductions, no atomics on data).
  *   act    HT_ACT_NONE or HT_ACT_RELU.
- *   path   HT_PATH_AUTO or HT_PATH_GEMV.
- *   ws     workspace of ws_bytes >= ht_linear_workspace(w, M, path). */
+ *   path   HT_PATH_GEMV: register dequantisation, 8 rows of x per launch
+ *          (for decode, M of a few rows);
+ *          HT_PATH_GEMM: blocks dequantised into LDS as bfloat16 (integer
+ *          codes exactly; FP16 and FP32 entries as a hi + lo pair, exact for
+ *          FP16 and to 16 significant bits for FP32) and multiplied with
+ *          bf16 MFMA, fp32 accumulation (for prefill, many rows);
+ *          HT_PATH_AUTO: GEMM when M >= 64, else GEMV.
+ *   ws     workspace of ws_bytes >= ht_linear_workspace(w, M, path) (the
+ *          GEMM path needs none). */
 ht_status ht_linear_forward(const ht_packed_weight *w, const uint16_t *x, int64_t M,
                             int64_t ldx, float *y, int64_t ldy, int32_t act, int32_t path,
                             void *ws, size_t ws_bytes, ht_stream stream);

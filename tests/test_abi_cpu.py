@@ -122,6 +122,13 @@ def test_linear_argument_checks():
     need = B.ht_linear_workspace(big, 1)
     assert need > 0                                                            # needs a K-split
     assert f(ctypes.byref(big), x, 1, 64 * 1024, y, 256, 0, 0, None, 0, None) == 4
+    # the MFMA path needs no workspace; AUTO takes it from 64 rows on
+    assert B.ht_linear_workspace(big, 1, B.HT_PATH_GEMM) == 0
+    assert B.ht_linear_workspace(big, 64, B.HT_PATH_AUTO) == 0
+    assert B.ht_linear_workspace(big, 63, B.HT_PATH_AUTO) > 0
+    with pytest.raises(B.HTError):
+        B.ht_linear_workspace(big, 1, B.HT_PATH_FUSED)                        # MLP-only path
+    assert f(ctypes.byref(d), x, 1, 256, y, 256, 0, B.HT_PATH_FUSED, None, 0, None) == 1
 
 
 def test_mlp_argument_checks():
