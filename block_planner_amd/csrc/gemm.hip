@@ -12,7 +12,7 @@
 //   BF16          the values;
 //   FP16 / FP32   two planes, hi = w with the low 16 bits cleared and
 //                 lo = bf16(w - hi) (exact for FP16; 16 significant bits for
-//                 FP32), scale 1.
+//                 FP32), scale 1; a non-finite entry gives a NaN column.
 // The partial of each step comes from bf16 MFMAs (v_mfma_f32_16x16x32_bf16)
 // with a fresh accumulator; the lo plane is multiplied only for 16-column
 // groups that hold an FP16 or FP32 block in that step.  Then every output
@@ -27,6 +27,7 @@
 namespace ht {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr uint32_t kGemmBN = 64;          // output columns (weight rows) per workgroup
 constexpr uint32_t kGemmThreads = 256;    // 4 waves in a 2 x 2 arrangement
@@ -64,23 +65,6 @@ struct BlockLoad {
     int f;             // format, or 5 for "no block": the column is zero in this step
 };
 
-__device__ __forceinline__ uint16_t bf16_trunc_bits(float v) {
-    const uint32_t u = __float_as_uint(v);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;   // NaN stays NaN
-    return uint16_t(u >> 16);
-}
-
-// hi / lo planes of a float entry; lo is 0 when hi is not finite.
-__device__ __forceinline__ void split_hi_lo(float w, uint16_t &hi, uint16_t &lo) {
-    hi = bf16_trunc_bits(w);
-    const float h = __uint_as_float(uint32_t(hi) << 16);
-    lo = (__float_as_uint(h) & 0x7f800000u) == 0x7f800000u ? uint16_t(0) : f32_to_bf16_rne(w - h);
-}
-
-// Signed 4-bit field k of v.
-__device__ __forceinline__ int q4(uint32_t v, int k) { return int32_t(v << (28 - 4 * k)) >> 28; }
-__device__ __forceinline__ uint16_t bf16_of_int(int q) { return uint16_t(__float_as_uint(float(q)) >> 16); }
-
 template <int MS>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
     extern __shared__ __align__(16) unsigned char gemm_lds[];
@@ -98,31 +82,36 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
     const uint32_t tile = n0 / R + gb / R, bi = gb % R;    // tile of the column, block slot within it
     const bool tile_ok = tile < w.T;
     const uint32_t *kbidx = reinterpret_cast<const uint32_t *>(w.base + w.off_kbidx);
-    uint32_t cur[5];                                        // kbidx[f][tile*KB + kb] for the step being loaded
+    // kbidx[f][tile*KB + kb] for the step about to be loaded (ka) and the one
+    // after it (kn): the index loads run two steps ahead of their use, so a
+    // step's block loads need one memory round trip, not two.
+    auto kbidx_at = [&](uint32_t kb, uint32_t (&v)[5]) {
 #pragma unroll
-    for (int f = 0; f < 5; ++f) cur[f] = tile_ok ? kbidx[uint64_t(f) * w.nk + uint64_t(tile) * KB] : 0u;
+        for (int f = 0; f < 5; ++f)
+            v[f] = tile_ok && kb <= KB ? kbidx[uint64_t(f) * w.nk + uint64_t(tile) * KB + kb] : 0u;
+    };
+    uint32_t ka[5], kn[5];
+    kbidx_at(0, ka);
+    kbidx_at(1, kn);
 
     auto load_block = [&](uint32_t kb) -> BlockLoad {
         BlockLoad b;
         b.f = 5;
         b.r = bi;
         b.sc = 1.0f;
-        uint32_t nxt[5];
-#pragma unroll
-        for (int f = 0; f < 5; ++f)
-            nxt[f] = tile_ok ? kbidx[uint64_t(f) * w.nk + uint64_t(tile) * KB + kb + 1] : 0u;
         uint32_t cum = 0, blk = 0;
 #pragma unroll
         for (int f = 0; f < 5; ++f) {
-            const uint32_t c = nxt[f] - cur[f];
+            const uint32_t c = kn[f] - ka[f];
             if (b.f == 5 && bi < cum + c) {
                 b.f = f;
-                blk = cur[f] + (bi - cum);
+                blk = ka[f] + (bi - cum);
             }
             cum += c;
         }
 #pragma unroll
-        for (int f = 0; f < 5; ++f) cur[f] = nxt[f];
+        for (int f = 0; f < 5; ++f) ka[f] = kn[f];
+        kbidx_at(kb + 2, kn);
         b.p[0] = b.p[1] = b.p[2] = b.p[3] = make_uint4(0, 0, 0, 0);
         if (b.f < 5) {
             b.r = reinterpret_cast<const uint16_t *>(w.base + w.off_ids[b.f])[blk] & (R - 1u);
@@ -154,65 +143,84 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
 
     // Dequantise into stage st: entries [16*part, 16*part + 16) of column gb
     // (INT4 quarters cover two runs of 8, see the nibble order of the layout).
+    // Entries are produced as packed bfloat16 pairs: integers via an exact
+    // fp32 conversion whose upper half is the bfloat16 (v_perm packs two),
+    // floats as hi = upper half (truncation) and lo = bf16_rne(w - hi)
+    // (v_cvt_pk_bf16_f32).  A non-finite FP16/FP32 entry makes lo NaN, so its
+    // output column is NaN.
     auto store_block = [&](const BlockLoad &b, GemmStage<MS> &st) {
         const uint32_t col = (gb / R) * R + b.r;               // column within the workgroup's 64
-        uint16_t hi[16], lo[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) lo[i] = 0;
+        const bool flt = b.f == 3 || b.f == 4;
+        const bool any_lo = __any(flt);                         // this wave's 16 columns need the lo plane
         const uint32_t u[16] = {b.p[0].x, b.p[0].y, b.p[0].z, b.p[0].w, b.p[1].x, b.p[1].y, b.p[1].z, b.p[1].w,
                                 b.p[2].x, b.p[2].y, b.p[2].z, b.p[2].w, b.p[3].x, b.p[3].y, b.p[3].z, b.p[3].w};
+        uint32_t hp[8], lp[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) lp[i] = 0u;
         uint32_t k0 = 16 * part, k1 = k0 + 8;                  // where the two runs of 8 go
+        auto nib = [](uint32_t v, uint32_t at) { return int32_t(v << (28u - at)) >> 28; };   // signed 4-bit field
+        auto pair_hi = [](float f0, float f1) {                 // upper halves of two fp32 -> one word
+            return __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+        };
+        auto pair_lo = [](float f0, float f1) {                 // bf16_rne(f - trunc(f)) of two fp32
+            const float r0 = f0 - __uint_as_float(__float_as_uint(f0) & 0xffff0000u);
+            const float r1 = f1 - __uint_as_float(__float_as_uint(f1) & 0xffff0000u);
+            const bf16x2 v = {(__bf16)r0, (__bf16)r1};
+            return __builtin_bit_cast(uint32_t, v);
+        };
         switch (b.f) {
         case 0:
-            // bytes j = 8p..8p+7: low nibble -> entry 32*(j/16) + j%16, high -> +16
+            // bytes 8p .. 8p+7: low nibble -> entry 32*(p/2) + 8*(p%2) + i, high nibble -> that + 16
             k0 = 32 * (part >> 1) + 8 * (part & 1);
             k1 = k0 + 16;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t byte = (u[i >> 2] >> (8 * (i & 3))) & 0xffu;
-                hi[i] = bf16_of_int(q4(byte, 0));
-                hi[8 + i] = bf16_of_int(q4(byte, 1));
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t wd = u[i >> 1], sh = 16 * (i & 1);
+                hp[i] = pair_hi(float(nib(wd, sh)), float(nib(wd, sh + 8)));
+                hp[4 + i] = pair_hi(float(nib(wd, sh + 4)), float(nib(wd, sh + 12)));
             }
             break;
         case 1:
 #pragma unroll
-            for (int i = 0; i < 16; ++i) hi[i] = bf16_of_int(int8_t(u[i >> 2] >> (8 * (i & 3))));
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t wd = u[i >> 1], sh = 16 * (i & 1);
+                hp[i] = pair_hi(float(int8_t(wd >> sh)), float(int8_t(wd >> (sh + 8))));
+            }
             break;
         case 2:
 #pragma unroll
-            for (int i = 0; i < 16; ++i) hi[i] = uint16_t(u[i >> 1] >> (16 * (i & 1)));
+            for (int i = 0; i < 8; ++i) hp[i] = u[i];
             break;
         case 3:
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-                split_hi_lo(float(__builtin_bit_cast(_Float16, uint16_t(u[i >> 1] >> (16 * (i & 1))))), hi[i], lo[i]);
+            for (int i = 0; i < 8; ++i) {
+                const float f0 = float(__builtin_bit_cast(_Float16, uint16_t(u[i])));
+                const float f1 = float(__builtin_bit_cast(_Float16, uint16_t(u[i] >> 16)));
+                hp[i] = pair_hi(f0, f1);
+                lp[i] = pair_lo(f0, f1);
+            }
             break;
         case 4:
 #pragma unroll
-            for (int i = 0; i < 16; ++i) split_hi_lo(__uint_as_float(u[i]), hi[i], lo[i]);
+            for (int i = 0; i < 8; ++i) {
+                const float f0 = __uint_as_float(u[2 * i]), f1 = __uint_as_float(u[2 * i + 1]);
+                hp[i] = pair_hi(f0, f1);
+                lp[i] = pair_lo(f0, f1);
+            }
             break;
         default:
 #pragma unroll
-            for (int i = 0; i < 16; ++i) hi[i] = 0;
+            for (int i = 0; i < 8; ++i) hp[i] = 0u;
             break;
         }
-        uint4 *dh0 = reinterpret_cast<uint4 *>(&st.whi[col][k0]);
-        uint4 *dh1 = reinterpret_cast<uint4 *>(&st.whi[col][k1]);
-        uint4 *dl0 = reinterpret_cast<uint4 *>(&st.wlo[col][k0]);
-        uint4 *dl1 = reinterpret_cast<uint4 *>(&st.wlo[col][k1]);
-        auto pk = [](const uint16_t *h) {
-            return make_uint4(h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16), h[4] | (uint32_t(h[5]) << 16),
-                              h[6] | (uint32_t(h[7]) << 16));
-        };
-        *dh0 = pk(hi);
-        *dh1 = pk(hi + 8);
-        *dl0 = pk(lo);
-        *dl1 = pk(lo + 8);
+        *reinterpret_cast<uint4 *>(&st.whi[col][k0]) = make_uint4(hp[0], hp[1], hp[2], hp[3]);
+        *reinterpret_cast<uint4 *>(&st.whi[col][k1]) = make_uint4(hp[4], hp[5], hp[6], hp[7]);
+        if (any_lo) {
+            *reinterpret_cast<uint4 *>(&st.wlo[col][k0]) = make_uint4(lp[0], lp[1], lp[2], lp[3]);
+            *reinterpret_cast<uint4 *>(&st.wlo[col][k1]) = make_uint4(lp[4], lp[5], lp[6], lp[7]);
+        }
         if (part == 0) st.scale[col] = b.sc;
-        // a 16-column group is one wave's 16 column blocks: does any need the lo plane?
-        const bool flt = b.f == 3 || b.f == 4;
-        const bool any = __any(flt);
-        if (lane == 0) st.need_lo[wave] = any ? 1u : 0u;
+        if (lane == 0) st.need_lo[wave] = any_lo ? 1u : 0u;
     };
 
     // ---- x tile: BM rows x 64 entries, 16 bytes per load ----
