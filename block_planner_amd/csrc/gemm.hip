@@ -61,7 +61,8 @@ constexpr uint32_t gemm_lds_bytes() { return 2u * uint32_t(sizeof(GemmStage<MS>)
 struct BlockLoad {
     uint4 p[4];        // payload bytes of this quarter (8 / 16 / 32 / 32 / 64 bytes by format)
     float sc;
-    uint32_t r;        // row within the tile (from the block id)
+    uint32_t id2;      // the 4 bytes holding the block id (kb * R + r), as loaded
+    uint32_t hi16;     // which half of id2 is the id
     int f;             // format, or 5 for "no block": the column is zero in this step
 };
 
@@ -97,7 +98,6 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
     auto load_block = [&](uint32_t kb) -> BlockLoad {
         BlockLoad b;
         b.f = 5;
-        b.r = bi;
         b.sc = 1.0f;
         uint32_t cum = 0, blk = 0;
 #pragma unroll
@@ -112,32 +112,35 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int f = 0; f < 5; ++f) ka[f] = kn[f];
         kbidx_at(kb + 2, kn);
-        b.p[0] = b.p[1] = b.p[2] = b.p[3] = make_uint4(0, 0, 0, 0);
-        if (b.f < 5) {
-            b.r = reinterpret_cast<const uint16_t *>(w.base + w.off_ids[b.f])[blk] & (R - 1u);
-            const uint8_t *pay = w.base + w.off_pay[b.f] + uint64_t(blk) * uint32_t(pay_bytes(b.f));
-            switch (b.f) {
-            case 0: {   // quarter p: bytes [8p, 8p+8)
-                const uint2 v = *reinterpret_cast<const uint2 *>(pay + 8 * part);
-                b.p[0] = make_uint4(v.x, v.y, 0, 0);
-                b.sc = reinterpret_cast<const float *>(w.base + w.off_scale[0])[blk];
-                break;
-            }
-            case 1:
-                b.p[0] = *reinterpret_cast<const uint4 *>(pay + 16 * part);
-                b.sc = reinterpret_cast<const float *>(w.base + w.off_scale[1])[blk];
-                break;
-            case 2:
-            case 3:
-                b.p[0] = *reinterpret_cast<const uint4 *>(pay + 32 * part);
-                b.p[1] = *reinterpret_cast<const uint4 *>(pay + 32 * part + 16);
-                break;
-            default:
+        // Branch-free loads (so no load waits for another): four 16-byte loads
+        // at addresses chosen per format, repeating the last one where the
+        // quarter is shorter; a missing block reads the buffer's first bytes.
+        // INT4's 8-byte quarter p comes with its neighbour in a 16-byte load
+        // at 16 * (p / 2); the dequantisation picks its half.
+        const bool has = b.f < 5;
+        const int f = has ? b.f : 0;
+        uint64_t po = 0, io = 0, so = 0;
+        uint32_t qb = 0, nl = 1;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) b.p[j] = *reinterpret_cast<const uint4 *>(pay + 64 * part + 16 * j);
-                break;
+        for (int g = 0; g < 5; ++g) {
+            if (f == g) {
+                po = w.off_pay[g] + uint64_t(blk) * uint32_t(pay_bytes(g));
+                io = w.off_ids[g] + ((2ull * blk) & ~3ull);
+                so = g < 2 ? w.off_scale[g] + 4ull * blk : 0ull;
+                qb = g == 0 ? 16u * (part >> 1) : uint32_t(pay_bytes(g) / 4) * part;
+                nl = g < 2 ? 1u : g == 4 ? 4u : 2u;
             }
         }
+        if (!has) po = io = so = 0;
+        const uint8_t *pq = w.base + po + qb;
+#pragma unroll
+        for (uint32_t j = 0; j < 4; ++j) {
+            const uint32_t jj = j < nl ? j : nl - 1u;
+            b.p[j] = *reinterpret_cast<const uint4 *>(pq + 16u * jj);
+        }
+        b.id2 = *reinterpret_cast<const uint32_t *>(w.base + io);
+        b.hi16 = blk & 1u;
+        b.sc = *reinterpret_cast<const float *>(w.base + so);   // meaningful for INT4 / INT8 only
         return b;
     };
 
@@ -149,7 +152,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
     // (v_cvt_pk_bf16_f32).  A non-finite FP16/FP32 entry makes lo NaN, so its
     // output column is NaN.
     auto store_block = [&](const BlockLoad &b, GemmStage<MS> &st) {
-        const uint32_t col = (gb / R) * R + b.r;               // column within the workgroup's 64
+        const uint32_t id = b.hi16 ? b.id2 >> 16 : b.id2;
+        const uint32_t col = (gb / R) * R + (b.f < 5 ? (id & (R - 1u)) : bi);   // column within the workgroup's 64
         const bool flt = b.f == 3 || b.f == 4;
         const bool any_lo = __any(flt);                         // this wave's 16 columns need the lo plane
         const uint32_t u[16] = {b.p[0].x, b.p[0].y, b.p[0].z, b.p[0].w, b.p[1].x, b.p[1].y, b.p[1].z, b.p[1].w,
@@ -170,12 +174,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
         };
         switch (b.f) {
         case 0:
-            // bytes 8p .. 8p+7: low nibble -> entry 32*(p/2) + 8*(p%2) + i, high nibble -> that + 16
+            // bytes 8p .. 8p+7 (words 2*(p&1), +1 of the 16-byte load): low nibble
+            // -> entry 32*(p/2) + 8*(p%2) + i, high nibble -> that + 16
             k0 = 32 * (part >> 1) + 8 * (part & 1);
             k1 = k0 + 16;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const uint32_t wd = u[i >> 1], sh = 16 * (i & 1);
+                const uint32_t wd = (part & 1) ? u[2 + (i >> 1)] : u[i >> 1], sh = 16 * (i & 1);
                 hp[i] = pair_hi(float(nib(wd, sh)), float(nib(wd, sh + 8)));
                 hp[4 + i] = pair_hi(float(nib(wd, sh + 4)), float(nib(wd, sh + 12)));
             }
@@ -219,7 +224,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
             *reinterpret_cast<uint4 *>(&st.wlo[col][k0]) = make_uint4(lp[0], lp[1], lp[2], lp[3]);
             *reinterpret_cast<uint4 *>(&st.wlo[col][k1]) = make_uint4(lp[4], lp[5], lp[6], lp[7]);
         }
-        if (part == 0) st.scale[col] = b.sc;
+        if (part == 0) st.scale[col] = b.f < 2 ? b.sc : 1.0f;
         if (lane == 0) st.need_lo[wave] = any_lo ? 1u : 0u;
     };
 
@@ -229,16 +234,15 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (uint32_t j = 0; j < kXLoads; ++j) {
             const uint32_t idx = tid + kGemmThreads * j, row = idx >> 3, seg = idx & 7;
-            const uint32_t m = m0 + row;
-            xv[j] = m < a.M ? *reinterpret_cast<const uint4 *>(a.x + int64_t(m) * a.ldx + kb * 64 + seg * 8)
-                            : make_uint4(0, 0, 0, 0);
+            const uint32_t m = min(m0 + row, a.M - 1u);   // rows past M read row M-1; zeroed when stored
+            xv[j] = *reinterpret_cast<const uint4 *>(a.x + int64_t(m) * a.ldx + kb * 64 + seg * 8);
         }
     };
     auto store_x = [&](const uint4 (&xv)[kXLoads], GemmStage<MS> &st) {
 #pragma unroll
         for (uint32_t j = 0; j < kXLoads; ++j) {
             const uint32_t idx = tid + kGemmThreads * j, row = idx >> 3, seg = idx & 7;
-            *reinterpret_cast<uint4 *>(&st.xs[row][seg * 8]) = xv[j];
+            *reinterpret_cast<uint4 *>(&st.xs[row][seg * 8]) = m0 + row < a.M ? xv[j] : make_uint4(0, 0, 0, 0);
         }
     };
 
@@ -248,8 +252,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
 
     {   // prologue: step 0 into stage 0
         uint4 xv[kXLoads];
-        load_x(0, xv);
         const BlockLoad b = load_block(0);
+        load_x(0, xv);
         store_x(xv, stage[0]);
         store_block(b, stage[0]);
     }
@@ -261,9 +265,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
         const bool more = kb + 1 < KB;
         uint4 xv[kXLoads];
         BlockLoad b;
-        if (more) {
-            load_x(kb + 1, xv);
+        if (more) {   // block loads first: nothing in them waits, so they never wait for x's loads
             b = load_block(kb + 1);
+            load_x(kb + 1, xv);
         }
         // MFMAs on this stage
         bf16x8 A[MS][2];
@@ -279,22 +283,29 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
             const bf16x8 Bh1 = *reinterpret_cast<const bf16x8 *>(&st.whi[c0 + lr][32 + lk]);
             const float sc = st.scale[c0 + lr];
             const bool lo = __builtin_amdgcn_readfirstlane(st.need_lo[c0 >> 4]) != 0u;
-            bf16x8 Bl0, Bl1;
+            // independent MFMA chains per 16-row group, straight-line for each case
+            f32x4 c[MS];
             if (lo) {
-                Bl0 = *reinterpret_cast<const bf16x8 *>(&st.wlo[c0 + lr][lk]);
-                Bl1 = *reinterpret_cast<const bf16x8 *>(&st.wlo[c0 + lr][32 + lk]);
-            }
+                const bf16x8 Bl0 = *reinterpret_cast<const bf16x8 *>(&st.wlo[c0 + lr][lk]);
+                const bf16x8 Bl1 = *reinterpret_cast<const bf16x8 *>(&st.wlo[c0 + lr][32 + lk]);
 #pragma unroll
-            for (int i = 0; i < MS; ++i) {
-                f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][0], Bh0, (f32x4{0.f, 0.f, 0.f, 0.f}), 0, 0, 0);
-                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][1], Bh1, c, 0, 0, 0);
-                if (lo) {
-                    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][0], Bl0, c, 0, 0, 0);
-                    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][1], Bl1, c, 0, 0, 0);
+                for (int i = 0; i < MS; ++i) {
+                    c[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][0], Bh0, (f32x4{0.f, 0.f, 0.f, 0.f}), 0, 0, 0);
+                    c[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][1], Bh1, c[i], 0, 0, 0);
+                    c[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][0], Bl0, c[i], 0, 0, 0);
+                    c[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][1], Bl1, c[i], 0, 0, 0);
                 }
+            } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(sc, c[e], acc[i][j][e]);
+                for (int i = 0; i < MS; ++i) {
+                    c[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][0], Bh0, (f32x4{0.f, 0.f, 0.f, 0.f}), 0, 0, 0);
+                    c[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][1], Bh1, c[i], 0, 0, 0);
+                }
             }
+#pragma unroll
+            for (int i = 0; i < MS; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(sc, c[i][e], acc[i][j][e]);
         }
         if (more) {
             GemmStage<MS> &nx = stage[(kb + 1) & 1];
