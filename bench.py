@@ -18,6 +18,10 @@ algorithmic bytes are, per block, its payload + scale + one format-map byte
 (2 bytes each) and the output (2 bytes for bfloat16 hidden layers, 4 for the
 fp32 last layer).
 
+Also reported (not the headline value): planner and packer GB/s, the
+single-layer GEMV, the per-layer MLP path, batch 32, a warm-cache figure, and
+the prefill GEMM (MFMA path, M = 2048, Llama-8B-shaped layers) in TFLOP/s.
+
 Prints ONE JSON line.
 """
 from __future__ import annotations
@@ -77,8 +81,9 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=6)
     ap.add_argument("--cpu-steps", type=int, default=20, help="oracle MLP forwards timed for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "gemv", "mlp"], default="all",
-                    help="'gemv' / 'mlp': only that timing leg (for counter runs)")
+    ap.add_argument("--only", choices=["all", "gemv", "mlp", "gemm"], default="all",
+                    help="'gemv' / 'mlp' / 'gemm': only that timing leg (for counter runs)")
+    ap.add_argument("--no-gemm", action="store_true", help="skip the prefill GEMM leg")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -102,10 +107,6 @@ def main() -> int:
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
-    log("generating weights")
-    Ws_host = [wl.mlp_weight(l) for l in range(L)]
-    Ws = [torch.from_numpy(W).to(dev) for W in Ws_host]
-
     def timed(fn, reps):
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -115,6 +116,42 @@ def main() -> int:
         e.record(stream)
         torch.cuda.synchronize()
         return s.elapsed_time(e) / reps / 1e3   # seconds per rep
+
+    def gemm_leg():
+        """Prefill: ht_linear_forward on the MFMA path at M = 2048 over
+        Llama-8B-shaped layers (q: 4096x4096, gate: 14336x4096, down:
+        4096x14336), seeded synthetic weights planned with the default
+        thresholds.  Reported: TFLOP/s of 2*M*N*K and the fraction of the
+        2.5 PFLOP/s dense bf16 MFMA peak."""
+        out = {}
+        M = 2048
+        for name in ("q", "gate", "down"):
+            shp = [t for t in wl.llama8b_shapes() if t.name == name][0]
+            W = torch.from_numpy(wl.llama8b_weight(0, shp)).to(dev)
+            fmt = api.plan(W)
+            pw = api.pack(W, fmt)
+            del W
+            xb = torch.from_numpy(wl.to_bf16_bits(wl.activation("llama8b", M, shp.k)).view(np.int16)).to(dev)
+            xg = xb.view(torch.bfloat16)
+            yg = torch.empty((M, shp.n), dtype=torch.float32, device=dev)
+            for _ in range(2):
+                api.linear(pw, xg, out=yg, path=B.HT_PATH_GEMM)
+            reps = 10
+            t = timed(lambda i: api.linear(pw, xg, out=yg, path=B.HT_PATH_GEMM), reps)
+            fl = 2.0 * M * shp.n * shp.k
+            out[name] = {"M": M, "N": shp.n, "K": shp.k, "us": round(t * 1e6, 1),
+                         "TFLOPs": round(fl / t / 1e12, 1), "mfma_frac": round(fl / t / 2.5e15, 4)}
+            del pw, xb, yg
+            torch.cuda.empty_cache()
+        return {"kernel": "gemm_kernel<4>", "peak_TFLOPs": 2500.0, "shapes": out}
+
+    if args.only == "gemm":
+        print(json.dumps(gemm_leg()))
+        return 0
+
+    log("generating weights")
+    Ws_host = [wl.mlp_weight(l) for l in range(L)]
+    Ws = [torch.from_numpy(W).to(dev) for W in Ws_host]
 
     # ---- planner ---------------------------------------------------------
     log("planner")
@@ -228,6 +265,7 @@ def main() -> int:
                           "copy_calibration": "torch.neg on 2**26 fp32 (268435456 B read + written), 3 launches"}))
         return 0
 
+    packed_mb = sum(p.nbytes for p in copies[0]) / 1e6
     log("mlp per-layer path, batch 32, warm cache")
     gp = graph_of(mlp_fn(x1, y1, path=B.HT_PATH_GEMV), G)
     t_perlayer = replay_timed(gp, reps, 1) / G
@@ -236,6 +274,13 @@ def main() -> int:
     gw = graph_of(mlp_fn(x1, y1, rotate=False), G)
     t_warm = replay_timed(gw, reps, 1) / G
     del gp, g32, gw
+
+    gemm = None
+    if not args.no_gemm:
+        log("prefill gemm (Llama-8B shapes, M = 2048)")
+        del copies, arrays, descs
+        torch.cuda.empty_cache()
+        gemm = gemm_leg()
 
     # ---- CPU baseline: the oracle as it stands ----------------------------
     cpu = None
@@ -291,7 +336,8 @@ def main() -> int:
         "graph_replay_matches_eager": replay_ok,
         "grid_barrier_ok": sync_ok,
         "format_mix": {n: round(v, 5) for n, v in zip(("INT4", "INT8", "BF16", "FP16", "FP32"), mix)},
-        "packed_MB_per_mlp": round(sum(p.nbytes for p in copies[0]) / 1e6, 2),
+        "packed_MB_per_mlp": round(packed_mb, 2),
+        "prefill_gemm": gemm,
     }
     print(json.dumps(out))
     return 0
