@@ -157,15 +157,6 @@ __device__ __forceinline__ void do_chunk(uint4 v, float scale, uint32_t id, bool
 }
 
 
-// Scalar per-layer state of a chunk loader: the tile's block range of each
-// format and the per-format region offsets from the buffer base (all
-// wave-uniform; 32-bit offsets keep the scalar register footprint small).
-struct ChunkSrc {
-    uint32_t lo[5], hi[5], nch[5];
-    uint32_t pay[5], ids[5], sc[2];
-    const uint8_t *base;    // the packed buffer; its first 256 bytes are always readable
-};
-
 // Per-lane data of one loaded chunk.
 struct Slot {
     uint4 pay;
@@ -175,52 +166,86 @@ struct Slot {
     bool v;    // this lane's block exists
 };
 
-// Load chunk c (wave-uniform) of a tile.  Branch-free in the loads: a slot
-// without a chunk reads the first 256 bytes of the buffer, and a lane past
-// the end of its format's range re-reads the range's last block; neither
-// lane stores a result.  Straight-line loads let the compiler count
-// outstanding loads exactly and wait for each chunk's own data only.
-__device__ __forceinline__ Slot load_chunk(const ChunkSrc &s, uint32_t c, uint32_t lane) {
-    int f = 5;
-    uint32_t ci = c, base_blk = 0, hb = 1, bpc = 1, pb = 0, po = 0, io = 0, so = 0;
-    int lg = 4;
+// Wave-uniform walk over one tile's chunks in format order (all format-0
+// chunks, then format 1, ...): this wave takes global chunk indices first,
+// first + step, first + 2*step, ...  The current format's constants are kept
+// in scalars and refreshed only when the walk crosses into another format, so
+// a chunk costs a handful of scalar instructions.
+struct ChunkWalker {
+    uint32_t lo[5], hi[5], nch[5], pay[5], ids[5], sc[2];
+    const uint8_t *base;
+    uint32_t step;
+    int f;                       // current format; 5 once the tile is exhausted
+    uint32_t ci;                 // chunk index within format f
+    // constants of format f (a harmless dummy once f == 5)
+    uint32_t c_lo, c_hi, c_nch, c_bpc, c_pb, c_po, c_io, c_so, c_lg;
+};
+
+__device__ __forceinline__ void walker_cache(ChunkWalker &w) {
+    while (w.f < 5) {   // skip exhausted (or empty) formats
+        uint32_t n = 0;
+#pragma unroll
+        for (int g = 0; g < 5; ++g)
+            if (w.f == g) n = w.nch[g];
+        if (w.ci < n) break;
+        w.ci -= n;
+        ++w.f;
+    }
+    w.c_lo = 0; w.c_hi = 1; w.c_nch = 0xFFFFFFFFu; w.c_bpc = 0; w.c_pb = 0;
+    w.c_po = 0; w.c_io = 0; w.c_so = 0; w.c_lg = 4;
 #pragma unroll
     for (int g = 0; g < 5; ++g) {
-        if (f == 5) {
-            if (ci < s.nch[g]) {
-                f = g;
-                base_blk = s.lo[g];
-                hb = s.hi[g];
-                bpc = bpc_of(g);
-                pb = uint32_t(pay_bytes(g));
-                po = s.pay[g];
-                io = s.ids[g];
-                so = g < 2 ? s.sc[g] : 0u;
-                lg = g == 0 ? 1 : g == 1 ? 2 : g == 4 ? 4 : 3;
-            } else {
-                ci -= s.nch[g];
-            }
+        if (w.f == g) {
+            w.c_lo = w.lo[g];
+            w.c_hi = w.hi[g];
+            w.c_nch = w.nch[g];
+            w.c_bpc = bpc_of(g);
+            w.c_pb = uint32_t(pay_bytes(g));
+            w.c_po = w.pay[g];
+            w.c_io = w.ids[g];
+            w.c_so = g < 2 ? w.sc[g] : 0u;
+            w.c_lg = g == 0 ? 1u : g == 1 ? 2u : g == 4 ? 4u : 3u;
         }
     }
+}
+
+__device__ __forceinline__ void walker_start(ChunkWalker &w, uint32_t first, uint32_t step) {
+    w.step = step;
+    w.f = 0;
+    w.ci = first;
+    walker_cache(w);
+}
+
+__device__ __forceinline__ void walker_advance(ChunkWalker &w) {
+    w.ci += w.step;
+    if (w.ci >= w.c_nch) walker_cache(w);
+}
+
+// Load the walker's current chunk.  Branch-free in the loads: past the end a
+// slot reads the first 256 bytes of the buffer, and a lane past the end of
+// its format's range re-reads the range's last block; neither lane stores a
+// result.  Straight-line loads let the compiler count outstanding loads
+// exactly and wait for each chunk's own data only.
+__device__ __forceinline__ Slot walker_load(const ChunkWalker &w, uint32_t lane) {
     Slot r;
-    uint32_t blk = base_blk + ci * bpc + (lane >> lg);
-    r.v = f < 5 && blk < hb;
-    blk = f < 5 ? min(blk, hb - 1u) : 0u;
-    const uint32_t sblk = f < 2 ? blk : 0u;
-    r.f = f;
+    uint32_t blk = w.c_lo + w.ci * w.c_bpc + (lane >> w.c_lg);
+    r.v = w.f < 5 && blk < w.c_hi;
+    blk = min(blk, w.c_hi - 1u);
+    const uint32_t sblk = w.f < 2 ? blk : 0u;
+    r.f = w.f;
     // the loaded values are used as they are (no arithmetic here), so the
     // wait for each slot's data lands at its first use
-    const u32x4 pv = ld_stream_u4(s.base + po + uint64_t(blk) * pb + (lane & ((1u << lg) - 1u)) * 16u);
+    const u32x4 pv = ld_stream_u4(w.base + w.c_po + uint64_t(blk) * w.c_pb + (lane & ((1u << w.c_lg) - 1u)) * 16u);
     r.pay = make_uint4(pv.x, pv.y, pv.z, pv.w);
-    r.id = reinterpret_cast<const uint16_t *>(s.base + io)[blk];
-    r.sc = reinterpret_cast<const float *>(s.base + so)[sblk];   // meaningful for integer formats only
+    r.id = reinterpret_cast<const uint16_t *>(w.base + w.c_io)[blk];
+    r.sc = reinterpret_cast<const float *>(w.base + w.c_so)[sblk];   // meaningful for integer formats only
     return r;
 }
 
-// Set up a loader for row tile t and K-blocks [kb0, kb1) of layer w (the
-// range of each format's blocks comes from the kbidx table).
-__device__ __forceinline__ ChunkSrc chunk_src(const LayerDev &w, uint32_t lo_raw[5], uint32_t hi_raw[5]) {
-    ChunkSrc s;
+// A walker over row tile t's blocks in K-blocks [kb0, kb1) of layer w (the
+// range of each format's blocks comes from the kbidx table); not started.
+__device__ __forceinline__ ChunkWalker chunk_src(const LayerDev &w, uint32_t lo_raw[5], uint32_t hi_raw[5]) {
+    ChunkWalker s;
 #pragma unroll
     for (int f = 0; f < 5; ++f) {
         s.hi[f] = min(hi_raw[f], w.counts[f]);
@@ -235,7 +260,7 @@ __device__ __forceinline__ ChunkSrc chunk_src(const LayerDev &w, uint32_t lo_raw
     return s;
 }
 
-__device__ __forceinline__ uint32_t n_chunks(const ChunkSrc &s) {
+__device__ __forceinline__ uint32_t n_chunks(const ChunkWalker &s) {
     return s.nch[0] + s.nch[1] + s.nch[2] + s.nch[3] + s.nch[4];
 }
 

@@ -70,13 +70,16 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(LinArgs a) {
         hi[f] = kbidx[uint64_t(f) * w.nk + col1];
         lo[f] = kbidx[uint64_t(f) * w.nk + col0];
     }
-    const ChunkSrc src = chunk_src(w, lo, hi);
-    const uint32_t C = n_chunks(src);
+    ChunkWalker src = chunk_src(w, lo, hi);
+    walker_start(src, wave, kWaves);
 
     // first batch in flight while x goes into LDS
     Slot sl[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) sl[u] = load_chunk(src, wave + u * kWaves, lane);
+    for (int u = 0; u < kUnroll; ++u) {
+        sl[u] = walker_load(src, lane);
+        walker_advance(src);
+    }
 
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -94,9 +97,12 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(LinArgs a) {
     // the first batch in straight-line code: each chunk waits for its own data
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) consume<M>(sl[u], lane, xs, xstride, P, pstride, kb0, nkb, w.R, w.lgR);
-    for (uint32_t c0 = wave + kWaves * kUnroll; c0 < C; c0 += kWaves * kUnroll) {
+    while (src.f < 5) {   // wave-uniform: chunks left for this wave
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) sl[u] = load_chunk(src, c0 + u * kWaves, lane);
+        for (int u = 0; u < kUnroll; ++u) {
+            sl[u] = walker_load(src, lane);
+            walker_advance(src);
+        }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) consume<M>(sl[u], lane, xs, xstride, P, pstride, kb0, nkb, w.R, w.lgR);
     }

@@ -66,7 +66,7 @@ __device__ __forceinline__ uint32_t wave_groups(uint32_t C, uint32_t wave) {
 
 // Chunk loader state for layer l of this workgroup's tile (from the LDS copy
 // of the tile's block ranges).
-__device__ __forceinline__ ChunkSrc layer_src(const MlpArgs &a, const uint32_t *meta, uint32_t l) {
+__device__ __forceinline__ ChunkWalker layer_src(const MlpArgs &a, const uint32_t *meta, uint32_t l) {
     uint32_t lo[5], hi[5];
 #pragma unroll
     for (int f = 0; f < 5; ++f) {
@@ -229,7 +229,8 @@ __global__ __launch_bounds__(kThreads) void mlp_fused_kernel(MlpArgs a) {
         // slots; slot u is refilled right after it is consumed, with the same
         // slot of the next group (possibly the next layer's).
         uint32_t ll = 0, gl = 0;             // layer and group to load next
-        ChunkSrc src = layer_src(a, meta, 0);
+        ChunkWalker src = layer_src(a, meta, 0);
+        walker_start(src, wave, kLoadWaves);
         uint32_t gcount = wave_groups(n_chunks(src), wave);
         auto advance_loader = [&]() {
             if (++gl == gcount) {
@@ -237,27 +238,33 @@ __global__ __launch_bounds__(kThreads) void mlp_fused_kernel(MlpArgs a) {
                 if (ll + 1 < L) {
                     ++ll;
                     src = layer_src(a, meta, ll);
+                    walker_start(src, wave, kLoadWaves);
                     gcount = wave_groups(n_chunks(src), wave);
                 } else {
                     gcount = ~0u;            // past the last layer: every further slot is empty
                     gl = 1u << 24;
+                    src.f = 5;
+                    walker_cache(src);
                 }
             }
         };
         Slot sl[kSlots];
 #pragma unroll
-        for (int u = 0; u < kSlots; ++u) sl[u] = load_chunk(src, wave + kLoadWaves * (gl * kSlots + u), lane);
+        for (int u = 0; u < kSlots; ++u) {
+            sl[u] = walker_load(src, lane);
+            walker_advance(src);
+        }
         advance_loader();
         for (uint32_t l = 0; l < L; ++l) {
             const LayerDev &w = a.layer[l];
             const uint32_t KB = w.KB, R = w.R, lgR = w.lgR;
             const uint32_t groups = wave_groups(n_chunks(layer_src(a, meta, l)), wave);
             for (uint32_t g = 0; g < groups; ++g) {
-                const uint32_t lbase = wave + kLoadWaves * (gl * kSlots);
 #pragma unroll
                 for (int u = 0; u < kSlots; ++u) {
                     consume<M>(sl[u], lane, xs, a.xcap, P, a.pcap, 0u, KB, R, lgR);
-                    sl[u] = load_chunk(src, lbase + kLoadWaves * u, lane);
+                    sl[u] = walker_load(src, lane);
+                    walker_advance(src);
                 }
                 advance_loader();
             }
