@@ -40,6 +40,7 @@ constexpr uint32_t kSpinLimit = 1u << 21;   // x ~64 clocks per poll: ~50 ms
 constexpr uint32_t kSyncBytes = 256;        // [0] call counter, [2] expired-wait flag
 constexpr uint32_t kLoadWaves = kWaves - 1; // waves streaming weights; the last one stages the input
 constexpr int kSlots = 2;                   // chunks in flight per loading wave
+constexpr uint32_t kLdsBudget = 160 * 1024; // LDS of one compute unit
 
 struct MlpArgs {
     LayerDev layer[kMaxLayers];
@@ -301,6 +302,9 @@ bool fused_fits(uint32_t grid, uint32_t lds) {
     // all workgroups must be resident at once: occupancy x compute units
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return false;
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&mlp_fused_kernel<M>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(kLdsBudget)) != hipSuccess)
+        return false;
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&mlp_fused_kernel<M>),
@@ -346,7 +350,7 @@ ht_status mlp_plan(const ht_packed_weight *const *layers, int32_t L, int64_t M, 
     pl->rmax = rmax;
     pl->grid = tmax;
     pl->lds = 768u + uint32_t(M) * kmax * 4u + uint32_t(M) * rmax * (kbmax + 1u) * 4u;
-    if (pl->lds > 64u * 1024u) fusable = false;
+    if (pl->lds > kLdsBudget) fusable = false;
     pl->fused = fusable && (!probe_device || fused_fits_m(M, pl->grid, pl->lds));
     return HT_OK;
 }

@@ -272,7 +272,8 @@ def mlp4096(orc):
 
 
 @pytest.mark.parametrize("M,path", [(1, B.HT_PATH_AUTO), (1, B.HT_PATH_GEMV), (2, B.HT_PATH_FUSED),
-                                    (4, B.HT_PATH_AUTO), (32, B.HT_PATH_AUTO)])
+                                    (3, B.HT_PATH_FUSED), (4, B.HT_PATH_FUSED), (4, B.HT_PATH_GEMV),
+                                    (32, B.HT_PATH_AUTO)])
 def test_mlp_teacher_forced(orc, mlp4096, M, path):
     Ws, fmts, pws = mlp4096
     x = wl.to_bf16_bits(wl.mlp_activation(M))
@@ -295,7 +296,7 @@ def test_mlp_teacher_forced(orc, mlp4096, M, path):
             check_close(y.cpu().numpy(), np.maximum(z, 0), f"last layer M={M}")
 
 
-@pytest.mark.parametrize("M", [1, 2])
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
 def test_mlp_fused_equals_per_layer(mlp4096, M):
     """The single persistent launch computes exactly what one launch per
     layer computes (same block partials, same fixed-order row sums), and is
@@ -333,14 +334,18 @@ def test_mlp_fused_ragged_layers(orc):
 
 
 def test_mlp_fused_refuses_what_does_not_fit(mlp4096):
-    """M = 4 at width 4096 needs 64 KiB of LDS for x alone: HT_PATH_FUSED
-    reports HT_EINVAL and HT_PATH_AUTO runs one launch per layer."""
+    """The single-launch path takes at most 4 rows of x (16-row tiles x 4 rows
+    fill the 64-entry LDS row buffer): at M = 5 HT_PATH_FUSED reports
+    HT_EINVAL and HT_PATH_AUTO runs one launch per layer."""
     _, _, pws = mlp4096
-    x = bf16_gpu(wl.to_bf16_bits(wl.mlp_activation(4)))
-    ws = api.mlp_workspace(pws, 4, dev())
+    x = bf16_gpu(wl.to_bf16_bits(wl.mlp_activation(5)))
+    ws = api.mlp_workspace(pws, 5, dev())
     with pytest.raises(B.HTError) as e:
         api.mlp(pws, x, ws=ws, path=B.HT_PATH_FUSED)
     assert e.value.code == 1
+    y = api.mlp(pws, x, ws=ws, path=B.HT_PATH_AUTO)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isfinite(y))
 
 
 def test_mlp_end_to_end_info(orc, mlp4096):
