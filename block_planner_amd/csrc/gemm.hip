@@ -37,9 +37,12 @@ struct GemmArgs {
     LayerDev w;
     const uint16_t *x;
     int64_t ldx;
-    float *y;
+    float *y;                 // fp32 output, or
+    uint16_t *ybf;            // bfloat16 output (round to nearest even), or
+    float *partial;           // per-split partial sums [S][M][N] (no activation)
     int64_t ldy;
     uint32_t M;
+    uint32_t KBs;             // K-blocks per split (blockIdx.z)
     int act;
 };
 
@@ -77,6 +80,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
     const uint32_t wm = wave >> 1, wn = wave & 1;          // wave tile: rows [wm*16*MS, +16*MS), cols [wn*32, +32)
     const uint32_t n0 = blockIdx.x * kGemmBN, m0 = blockIdx.y * BM;
     const uint32_t KB = w.KB, R = w.R;
+    const uint32_t kb0 = blockIdx.z * a.KBs, kb1 = min(KB, kb0 + a.KBs);   // this split's K-blocks (non-empty)
 
     // ---- dequantisation role: thread -> (column block gb, quarter part) ----
     const uint32_t gb = tid >> 2, part = tid & 3;
@@ -92,8 +96,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
             v[f] = tile_ok && kb <= KB ? kbidx[uint64_t(f) * w.nk + uint64_t(tile) * KB + kb] : 0u;
     };
     uint32_t ka[5], kn[5];
-    kbidx_at(0, ka);
-    kbidx_at(1, kn);
+    kbidx_at(kb0, ka);
+    kbidx_at(kb0 + 1, kn);
 
     auto load_block = [&](uint32_t kb) -> BlockLoad {
         BlockLoad b;
@@ -252,17 +256,17 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
 
     {   // prologue: step 0 into stage 0
         uint4 xv[kXLoads];
-        const BlockLoad b = load_block(0);
-        load_x(0, xv);
+        const BlockLoad b = load_block(kb0);
+        load_x(kb0, xv);
         store_x(xv, stage[0]);
         store_block(b, stage[0]);
     }
     __syncthreads();
 
     const uint32_t lr = lane & 15, lk = (lane >> 4) * 8;    // MFMA operand row / first k of this lane
-    for (uint32_t kb = 0; kb < KB; ++kb) {
-        GemmStage<MS> &st = stage[kb & 1];
-        const bool more = kb + 1 < KB;
+    for (uint32_t kb = kb0; kb < kb1; ++kb) {
+        GemmStage<MS> &st = stage[(kb - kb0) & 1];
+        const bool more = kb + 1 < kb1;
         uint4 xv[kXLoads];
         BlockLoad b;
         if (more) {   // block loads first: nothing in them waits, so they never wait for x's loads
@@ -308,7 +312,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
                 for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(sc, c[i][e], acc[i][j][e]);
         }
         if (more) {
-            GemmStage<MS> &nx = stage[(kb + 1) & 1];
+            GemmStage<MS> &nx = stage[(kb + 1 - kb0) & 1];
             store_x(xv, nx);
             store_block(b, nx);
         }
@@ -325,9 +329,15 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const uint32_t m = m0 + wm * 16 * MS + 16 * i + 4 * (lane >> 4) + e;
+                if (m >= a.M) continue;
                 float v = acc[i][j][e];
+                if (a.partial) {
+                    a.partial[(uint64_t(blockIdx.z) * a.M + m) * w.N + n] = v;
+                    continue;
+                }
                 if (a.act == HT_ACT_RELU) v = v > 0.0f ? v : 0.0f;   // +0 for zero, negative and NaN
-                if (m < a.M) a.y[int64_t(m) * a.ldy + n] = v;
+                if (a.ybf) a.ybf[int64_t(m) * a.ldy + n] = f32_to_bf16_rne(v);
+                else a.y[int64_t(m) * a.ldy + n] = v;
             }
         }
 }
@@ -345,31 +355,66 @@ void launch_gemm(const GemmArgs &a, hipStream_t s) {
                                   hipFuncAttributeMaxDynamicSharedMemorySize, int(gemm_lds_bytes<MS>()));
         attr = true;
     }
-    const dim3 grid((a.w.N + kGemmBN - 1) / kGemmBN, (a.M + 32 * MS - 1) / (32 * MS));
+    const dim3 grid((a.w.N + kGemmBN - 1) / kGemmBN, (a.M + 32 * MS - 1) / (32 * MS),
+                    (a.w.KB + a.KBs - 1) / a.KBs);
     hipLaunchKernelGGL(gemm_kernel<MS>, grid, dim3(kGemmThreads), gemm_lds_bytes<MS>(), s, a);
 }
 
 }  // namespace
 
-ht_status run_gemm(const ht_packed_weight *w, const uint16_t *x, int64_t M, int64_t ldx, float *y, int64_t ldy,
-                   int act, hipStream_t s) {
+namespace {
+
+constexpr int64_t kGemmChunkRows = 65535 * 32;   // rows per launch (grid y limit at 32-row tiles)
+
+uint32_t gemm_bm(int64_t M) { return M >= 128 ? 128u : M >= 64 ? 64u : 32u; }
+
+// K-splits: enough workgroups for the 256 compute units, at least 4
+// K-blocks per split, every split non-empty.
+uint32_t gemm_splits(const ht_packed_weight *w, int64_t M) {
+    const uint32_t KB = uint32_t(w->K / kBlockK);
+    const uint64_t tiles = uint64_t((w->N + kGemmBN - 1) / kGemmBN) * uint64_t((M + gemm_bm(M) - 1) / gemm_bm(M));
+    if (tiles >= 256 || KB < 8) return 1;
+    uint32_t S = uint32_t((256 + tiles - 1) / tiles);
+    if (S > KB / 4) S = KB / 4;
+    const uint32_t KBs = (KB + S - 1) / S;
+    return (KB + KBs - 1) / KBs;
+}
+
+}  // namespace
+
+size_t gemm_ws(const ht_packed_weight *w, int64_t M) {
+    const int64_t Mt = M < kGemmChunkRows ? M : kGemmChunkRows;
+    const uint32_t S = gemm_splits(w, Mt);
+    return S > 1 ? size_t(S) * size_t(Mt) * size_t(w->N) * sizeof(float) : 0;
+}
+
+ht_status run_gemm(const ht_packed_weight *w, const uint16_t *x, int64_t M, int64_t ldx, float *y, uint16_t *ybf,
+                   int64_t ldy, int act, void *ws, hipStream_t s) {
     GemmArgs a;
     a.w = layer_dev(w);
-    a.x = x;
     a.ldx = ldx;
-    a.y = y;
     a.ldy = ldy;
     a.act = act;
-    // row tiles of at most 65535 x-row tiles per launch (grid y limit)
-    for (int64_t m0 = 0; m0 < M; m0 += 65535 * 32) {
-        const int64_t Mt = M - m0 < 65535 * 32 ? M - m0 : 65535 * 32;
+    for (int64_t m0 = 0; m0 < M; m0 += kGemmChunkRows) {
+        const int64_t Mt = M - m0 < kGemmChunkRows ? M - m0 : kGemmChunkRows;
+        const uint32_t S = gemm_splits(w, Mt);
         a.x = x + m0 * ldx;
-        a.y = y + m0 * ldy;
+        a.y = y ? y + m0 * ldy : nullptr;
+        a.ybf = ybf ? ybf + m0 * ldy : nullptr;
+        a.partial = S > 1 ? static_cast<float *>(ws) : nullptr;
         a.M = uint32_t(Mt);
-        if (Mt >= 128) launch_gemm<4>(a, s);
-        else if (Mt >= 64) launch_gemm<2>(a, s);
-        else launch_gemm<1>(a, s);
+        a.KBs = (a.w.KB + S - 1) / S;
+        switch (gemm_bm(Mt)) {
+        case 128: launch_gemm<4>(a, s); break;
+        case 64: launch_gemm<2>(a, s); break;
+        default: launch_gemm<1>(a, s); break;
+        }
         HT_LAUNCH_CHECK();
+        if (S > 1) {
+            const ht_status st = launch_split_reduce(static_cast<const float *>(ws), S, uint32_t(Mt), a.w.N, a.y,
+                                                     a.ybf, ldy, act, s);
+            if (st != HT_OK) return st;
+        }
     }
     return HT_OK;
 }

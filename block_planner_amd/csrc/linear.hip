@@ -181,6 +181,15 @@ size_t linear_ws(const ht_packed_weight *w, int64_t M) {
     return S > 1 ? size_t(S) * size_t(Mt) * size_t(w->N) * sizeof(float) : 0;
 }
 
+ht_status launch_split_reduce(const float *partial, uint32_t S, uint32_t M, uint32_t N, float *y, uint16_t *ybf,
+                              int64_t ldy, int act, hipStream_t s) {
+    const uint32_t tot = M * N;
+    hipLaunchKernelGGL(split_reduce_kernel, dim3((tot + 255) / 256), dim3(256), 0, s, partial, S, M, N, y, ybf, ldy,
+                       act);
+    HT_LAUNCH_CHECK();
+    return HT_OK;
+}
+
 // One linear over rows [0, M) of x; output either fp32 y or bf16 ybf.
 ht_status run_linear(const ht_packed_weight *w, const uint16_t *x, int64_t M, int64_t ldx, float *y,
                      uint16_t *ybf, int64_t ldy, int act, void *ws, hipStream_t s) {
@@ -215,10 +224,9 @@ ht_status run_linear(const ht_packed_weight *w, const uint16_t *x, int64_t M, in
         }
         HT_LAUNCH_CHECK();
         if (S > 1) {
-            const uint32_t tot = uint32_t(Mt) * a.w.N;
-            hipLaunchKernelGGL(split_reduce_kernel, dim3((tot + 255) / 256), dim3(256), 0, s,
-                               static_cast<const float *>(ws), S, uint32_t(Mt), a.w.N, a.y, a.ybf, ldy, act);
-            HT_LAUNCH_CHECK();
+            const ht_status st = launch_split_reduce(static_cast<const float *>(ws), S, uint32_t(Mt), a.w.N, a.y,
+                                                     a.ybf, ldy, act, s);
+            if (st != HT_OK) return st;
         }
     }
     return HT_OK;
@@ -237,7 +245,7 @@ extern "C" ht_status ht_linear_workspace(const ht_packed_weight *w, int64_t M, i
     if (M <= 0) return HT_ESHAPE;
     if (!path_ok(path)) return HT_EINVAL;
     if (path == HT_PATH_AUTO) path = auto_linear_path(M);
-    *bytes = path == HT_PATH_GEMM ? 0 : linear_ws(w, M);
+    *bytes = path == HT_PATH_GEMM ? gemm_ws(w, M) : linear_ws(w, M);
     return HT_OK;
 }
 
@@ -250,9 +258,10 @@ extern "C" ht_status ht_linear_forward(const ht_packed_weight *w, const uint16_t
     if (M <= 0 || ldx < w->K || ldy < w->N) return HT_ESHAPE;
     if (!al16(x) || !al16(y) || (ldx % 8) || !al16(w->base)) return HT_EALIGN;
     if (path == HT_PATH_AUTO) path = auto_linear_path(M);
-    if (path == HT_PATH_GEMM) return run_gemm(w, x, M, ldx, y, ldy, act, reinterpret_cast<hipStream_t>(stream));
-    const size_t need = linear_ws(w, M);
+    const size_t need = path == HT_PATH_GEMM ? gemm_ws(w, M) : linear_ws(w, M);
     if (need && (!ws || ws_bytes < need)) return HT_ESMALL;
     if (ws && !al16(ws)) return HT_EALIGN;
+    if (path == HT_PATH_GEMM)
+        return run_gemm(w, x, M, ldx, y, nullptr, ldy, act, ws, reinterpret_cast<hipStream_t>(stream));
     return run_linear(w, x, M, ldx, y, nullptr, ldy, act, ws, reinterpret_cast<hipStream_t>(stream));
 }

@@ -18,11 +18,19 @@ size_t linear_ws(const ht_packed_weight *w, int64_t M);
 ht_status run_linear(const ht_packed_weight *w, const uint16_t *x, int64_t M, int64_t ldx, float *y,
                      uint16_t *ybf, int64_t ldy, int act, void *ws, hipStream_t s);
 
-// Enqueue one linear on the MFMA path (fp32 y).  Arguments are assumed checked.
-ht_status run_gemm(const ht_packed_weight *w, const uint16_t *x, int64_t M, int64_t ldx, float *y, int64_t ldy,
-                   int act, hipStream_t s);
+// Workspace bytes of one linear over M rows on the MFMA path (K-split partials).
+size_t gemm_ws(const ht_packed_weight *w, int64_t M);
+
+// Enqueue one linear on the MFMA path: fp32 y or bfloat16 ybf (one of them
+// non-null).  Arguments are assumed checked.
+ht_status run_gemm(const ht_packed_weight *w, const uint16_t *x, int64_t M, int64_t ldx, float *y, uint16_t *ybf,
+                   int64_t ldy, int act, void *ws, hipStream_t s);
+
+// y[m, n] = act(sum over s in order of partial[s][m][n]), fp32 y or bfloat16 ybf.
+ht_status launch_split_reduce(const float *partial, uint32_t S, uint32_t M, uint32_t N, float *y, uint16_t *ybf,
+                              int64_t ldy, int act, hipStream_t s);
 
 // The path HT_PATH_AUTO resolves to for one linear over M rows.
-inline int32_t auto_linear_path(int64_t M) { return M >= 64 ? HT_PATH_GEMM : HT_PATH_GEMV; }
+inline int32_t auto_linear_path(int64_t M) { return M >= 16 ? HT_PATH_GEMM : HT_PATH_GEMV; }
 
 }  // namespace ht

@@ -333,8 +333,9 @@ ht_status mlp_plan(const ht_packed_weight *const *layers, int32_t L, int64_t M, 
         const ht_packed_weight *w = layers[l];
         if (!desc_ok(w)) return HT_EINVAL;
         if (l && w->K != layers[l - 1]->N) return HT_ESHAPE;
-        const size_t p = linear_ws(w, M);
+        const size_t p = linear_ws(w, M), q = gemm_ws(w, M);
         pl->part = p > pl->part ? p : pl->part;
+        pl->part = q > pl->part ? q : pl->part;
         const size_t h = align256(size_t(M) * size_t(w->N) * 2u);
         pl->act = h > pl->act ? h : pl->act;
         if (l + 1 < L) pl->words += align256(size_t(M) * size_t(w->N) * 2u);
@@ -460,19 +461,26 @@ extern "C" ht_status ht_mlp_forward(const ht_packed_weight *const *layers, int32
     const uint16_t *in = x;
     int64_t ld_in = ldx;
     size_t dump_off = 0;
+    // HT_PATH_GEMV: register-path GEMV per layer; HT_PATH_AUTO: the MFMA path
+    // from 16 rows of x on, as for a single linear
+    const bool mfma = path != HT_PATH_GEMV && auto_linear_path(M) == HT_PATH_GEMM;
     for (int32_t l = 0; l < n_layers; ++l) {
         const ht_packed_weight *w = layers[l];
+        float *yo = nullptr;
+        uint16_t *out = nullptr;
+        int64_t ldo = ldy;
         if (l + 1 < n_layers) {
-            uint16_t *out = act_dump ? act_dump + dump_off : ping[l & 1];
+            out = act_dump ? act_dump + dump_off : ping[l & 1];
             dump_off += size_t(M) * size_t(w->N);
-            st = run_linear(w, in, M, ld_in, nullptr, out, w->N, HT_ACT_RELU, part, s);
-            if (st != HT_OK) return st;
-            in = out;
-            ld_in = w->N;
+            ldo = w->N;
         } else {
-            st = run_linear(w, in, M, ld_in, y, nullptr, ldy, HT_ACT_RELU, part, s);
-            if (st != HT_OK) return st;
+            yo = y;
         }
+        st = mfma ? run_gemm(w, in, M, ld_in, yo, out, ldo, HT_ACT_RELU, part, s)
+                  : run_linear(w, in, M, ld_in, yo, out, ldo, HT_ACT_RELU, part, s);
+        if (st != HT_OK) return st;
+        in = out;
+        ld_in = w->N;
     }
     return HT_OK;
 }

@@ -181,9 +181,9 @@ ht_status ht_linear_workspace(const ht_packed_weight *w, int64_t M, int32_t path
  *          codes exactly; FP16 and FP32 entries as a hi + lo pair, exact for
  *          FP16 and to 16 significant bits for FP32) and multiplied with
  *          bf16 MFMA, fp32 accumulation (for prefill, many rows);
- *          HT_PATH_AUTO: GEMM when M >= 64, else GEMV.
- *   ws     workspace of ws_bytes >= ht_linear_workspace(w, M, path) (the
- *          GEMM path needs none). */
+ *          HT_PATH_AUTO: GEMM when M >= 16, else GEMV.
+ *   ws     workspace of ws_bytes >= ht_linear_workspace(w, M, path): K-split
+ *          partial sums, added in split order by a second kernel. */
 ht_status ht_linear_forward(const ht_packed_weight *w, const uint16_t *x, int64_t M,
                             int64_t ldx, float *y, int64_t ldy, int32_t act, int32_t path,
                             void *ws, size_t ws_bytes, ht_stream stream);
@@ -211,10 +211,12 @@ ht_status ht_workspace_init(void *ws, size_t ws_bytes, ht_stream stream);
  *             intermediate h_l (each layer's slab is M * N_l elements, slabs
  *             packed back to back); the layers then read their input from it.
  *   path      HT_PATH_AUTO: one persistent launch for all layers when it fits
- *             (n_layers <= 8, M <= 4, M*K of every layer <= 16384, LDS, and
- *             every workgroup resident at once), else one launch per layer;
- *             HT_PATH_GEMV: one launch per layer; HT_PATH_FUSED: the single
- *             launch or HT_EINVAL if it does not fit.
+ *             (n_layers <= 8, M <= 4, row tile >= 4, x, partial sums and row
+ *             buffer within the 160 KiB LDS of a compute unit, and every
+ *             workgroup resident at once), else one launch per layer, on the
+ *             MFMA path (as HT_PATH_GEMM of ht_linear_forward) from M >= 16;
+ *             HT_PATH_GEMV: one register-path GEMV launch per layer;
+ *             HT_PATH_FUSED: the single launch or HT_EINVAL if it does not fit.
  *   ws        workspace of ws_bytes >= ht_mlp_workspace(...), initialised with
  *             ht_workspace_init before its first use and again whenever it is
  *             used with other layers or another M.  The single launch passes
