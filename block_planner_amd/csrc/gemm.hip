@@ -365,16 +365,18 @@ void launch_gemm(const GemmArgs &a, hipStream_t s) {
 namespace {
 
 constexpr int64_t kGemmChunkRows = 65535 * 32;   // rows per launch (grid y limit at 32-row tiles)
+constexpr uint64_t kSplitTarget = 768;             // workgroups wanted: three per compute unit
 
 uint32_t gemm_bm(int64_t M) { return M >= 128 ? 128u : M >= 64 ? 64u : 32u; }
 
-// K-splits: enough workgroups for the 256 compute units, at least 4
+// K-splits: three workgroups per compute unit (each step of a workgroup
+// waits for its blocks' loads, so more of them in flight hide that), at least 4
 // K-blocks per split, every split non-empty.
 uint32_t gemm_splits(const ht_packed_weight *w, int64_t M) {
     const uint32_t KB = uint32_t(w->K / kBlockK);
     const uint64_t tiles = uint64_t((w->N + kGemmBN - 1) / kGemmBN) * uint64_t((M + gemm_bm(M) - 1) / gemm_bm(M));
-    if (tiles >= 256 || KB < 8) return 1;
-    uint32_t S = uint32_t((256 + tiles - 1) / tiles);
+    if (tiles >= kSplitTarget || KB < 8) return 1;
+    uint32_t S = uint32_t((kSplitTarget + tiles - 1) / tiles);
     if (S > KB / 4) S = KB / 4;
     const uint32_t KBs = (KB + S - 1) / S;
     return (KB + KBs - 1) / KBs;
