@@ -122,10 +122,11 @@ def test_linear_argument_checks():
     need = B.ht_linear_workspace(big, 1)
     assert need > 0                                                            # needs a K-split
     assert f(ctypes.byref(big), x, 1, 64 * 1024, y, 256, 0, 0, None, 0, None) == 4
-    # the MFMA path splits K when it has few output tiles: 256 x 65536 at
-    # M = 1 is 4 tiles -> 64 splits of 16 K-blocks, [64][1][256] fp32 partials
-    assert B.ht_linear_workspace(big, 1, B.HT_PATH_GEMM) == 64 * 1 * 256 * 4
-    assert B.ht_linear_workspace(big, 16, B.HT_PATH_AUTO) == 64 * 16 * 256 * 4   # AUTO: MFMA from 16 rows
+    # the MFMA path splits K when it has few output tiles: [S][M][N] fp32
+    # partials with 2 <= S <= K/64/4 (at least 4 K-blocks per split)
+    for M, path in ((1, B.HT_PATH_GEMM), (16, B.HT_PATH_AUTO)):                 # AUTO: MFMA from 16 rows
+        ws = B.ht_linear_workspace(big, M, path)
+        assert ws % (M * 256 * 4) == 0 and 2 <= ws // (M * 256 * 4) <= 1024 // 4
     wide = _desc(N=16384, K=4096, R=16)
     assert B.ht_linear_workspace(wide, 128, B.HT_PATH_GEMM) == 0                  # 256 tiles: no split
     with pytest.raises(B.HTError):
