@@ -128,7 +128,7 @@ def test_linear_argument_checks():
         ws = B.ht_linear_workspace(big, M, path)
         assert ws % (M * 256 * 4) == 0 and 2 <= ws // (M * 256 * 4) <= 1024 // 4
     wide = _desc(N=16384, K=4096, R=16)
-    assert B.ht_linear_workspace(wide, 128, B.HT_PATH_GEMM) == 0                  # 256 tiles: no split
+    assert B.ht_linear_workspace(wide, 2048, B.HT_PATH_GEMM) == 0                 # 4096 tiles: no split
     with pytest.raises(B.HTError):
         B.ht_linear_workspace(big, 1, B.HT_PATH_FUSED)                        # MLP-only path
     assert f(ctypes.byref(d), x, 1, 256, y, 256, 0, B.HT_PATH_FUSED, None, 0, None) == 1
