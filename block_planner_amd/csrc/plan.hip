@@ -34,24 +34,36 @@ struct PlanArgs {
 
 template <bool EPS16_ZERO>
 __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
+    __shared__ __align__(16) float stage[4][16 * 64];      // per wave: its 16 blocks
     const uint32_t tid = blockIdx.x * 256u + threadIdx.x;
     const uint32_t b = tid >> 2;           // block index n * KB + kb
     const int part = int(threadIdx.x & 3);
     const bool valid = b < a.n_blocks;
+    const uint32_t lane = threadIdx.x & 63u, wv = threadIdx.x >> 6;
 
-    float w[kPerLane];
-    if (valid) {
-        const uint32_t n = fastdiv(b, a.div_kb);
-        const uint32_t kb = b - n * a.KB;
-        const float *src = a.W + int64_t(n) * a.ldw + kb * 64u + part * 16;
+    // The wave's 16 blocks as 4 fully coalesced 1 KiB loads (16-byte piece
+    // p = 64j + lane is piece p % 16 of the wave's block p / 16), through LDS
+    // to the compute layout (lane = 4 * block + part holds pieces 4*lane ..
+    // 4*lane + 3).  Blocks past the end read block 0 and store nothing.
+    {
+        const uint32_t b0 = blockIdx.x * 64u + wv * 16u;
+        f32x4 pc[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const f32x4 v = ld_stream_f4(src + 4 * j);
-            w[4 * j] = v.x; w[4 * j + 1] = v.y; w[4 * j + 2] = v.z; w[4 * j + 3] = v.w;
+            const uint32_t p = 64u * j + lane, bb = b0 + (p >> 4);
+            const uint32_t bc = bb < a.n_blocks ? bb : 0u;
+            const uint32_t n = fastdiv(bc, a.div_kb), kb = bc - n * a.KB;
+            pc[j] = ld_stream_f4(a.W + int64_t(n) * a.ldw + kb * 64u + (p & 15u) * 4u);
         }
-    } else {
 #pragma unroll
-        for (int i = 0; i < kPerLane; ++i) w[i] = 0.0f;
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<f32x4 *>(&stage[wv][(64u * j + lane) * 4u]) = pc[j];
+    }
+    __syncthreads();
+    float w[kPerLane];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(&stage[wv][(4u * lane + k) * 4u]);
+        w[4 * k] = v.x; w[4 * k + 1] = v.y; w[4 * k + 2] = v.z; w[4 * k + 3] = v.w;
     }
 
     // amax and the two scales
@@ -59,18 +71,58 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
     const float s4 = amax / 7.0f;     // correctly rounded fp32 division
     const float s8 = amax / 127.0f;
 
-    // codes, exact residuals d = w - q*s (exactly representable in fp32, so
-    // the fused multiply-add returns it exactly), fp64 tree of d^2
-    float q[kPerLane], d[kPerLane];
+    // codes and exact residuals d = w - q*s (exactly representable in fp32,
+    // so the fused multiply-add returns it exactly)
+    float q[kPerLane], d4[kPerLane], d8[kPerLane];
     lane_codes(w, s4, 7.0f, q);
 #pragma unroll
-    for (int i = 0; i < kPerLane; ++i) d[i] = __builtin_fmaf(-q[i], s4, w[i]);
-    const double err4 = block_tree(tree16_sq(d));
+    for (int i = 0; i < kPerLane; ++i) d4[i] = __builtin_fmaf(-q[i], s4, w[i]);
     lane_codes(w, s8, 127.0f, q);
 #pragma unroll
-    for (int i = 0; i < kPerLane; ++i) d[i] = __builtin_fmaf(-q[i], s8, w[i]);
-    const double err8 = block_tree(tree16_sq(d));
-    const double nrm2 = block_tree(tree16_sq(w));
+    for (int i = 0; i < kPerLane; ++i) d8[i] = __builtin_fmaf(-q[i], s8, w[i]);
+
+    // Screening in fp32: the sums of squares err4, err8, nrm2 to within
+    // 2^-17 relative plus 2^-120 absolute (66 roundings of non-negative
+    // partial sums, underflow included).  A decision that holds for every
+    // value in those intervals equals the decision on the fp64 pairwise
+    // trees; only the other blocks (near-ties, eps = 0, zero blocks,
+    // non-finite or huge entries) compute the fp64 trees, in waves that vote
+    // for them.
+    float e4f = 0.0f, e8f = 0.0f, nf = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) {
+        e4f = __builtin_fmaf(d4[i], d4[i], e4f);
+        e8f = __builtin_fmaf(d8[i], d8[i], e8f);
+        nf = __builtin_fmaf(w[i], w[i], nf);
+    }
+    e4f = e4f + dpp_f32<kDppXor1>(e4f);
+    e8f = e8f + dpp_f32<kDppXor1>(e8f);
+    nf = nf + dpp_f32<kDppXor1>(nf);
+    e4f = e4f + dpp_f32<kDppXor2>(e4f);
+    e8f = e8f + dpp_f32<kDppXor2>(e8f);
+    nf = nf + dpp_f32<kDppXor2>(nf);
+    auto screen = [](double e2, float ef, float nfv) -> int {   // 0 no, 1 yes, 2 undecided
+        if (!(e2 > 0.0)) return 2;
+        const double E = ef, Nn = nfv, rel = 0x1p-17, ab = 0x1p-120;
+        if (E * (1.0 - rel) - ab > e2 * (Nn * (1.0 + rel) + ab)) return 0;
+        if (E * (1.0 + rel) + ab <= e2 * (Nn * (1.0 - rel) - ab)) return 1;
+        return 2;
+    };
+    const bool in_range = nf <= 0x1p126f;   // finite, and no square near overflow
+    const int dec4 = screen(a.e2[0], e4f, nf), dec8 = screen(a.e2[1], e8f, nf);
+    const bool need = !in_range || dec4 == 2 || dec8 == 2;
+    bool ok4 = dec4 == 1, ok8 = dec8 == 1, finite = true;
+    if (__any(need)) {
+        const double err4 = block_tree(tree16_sq(d4));
+        const double err8 = block_tree(tree16_sq(d8));
+        const double nrm2 = block_tree(tree16_sq(w));
+        if (need) {
+            ok4 = err4 <= a.e2[0] * nrm2;
+            ok8 = err8 <= a.e2[1] * nrm2;
+            finite = nrm2 <= DBL_MAX;   // false for Inf and NaN entries
+        }
+    }
+    float (&d)[kPerLane] = d4;   // scratch for the 16-bit tests below
 
     // 16-bit formats
     bool okb, okh;
@@ -99,12 +151,10 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
 #pragma unroll
         for (int i = 0; i < kPerLane; ++i) d[i] = w[i] - round_fp16(w[i]);
         const double errh = block_tree(tree16_sq(d));
+        const double nrm2 = block_tree(tree16_sq(w));
         okb = errb <= a.e2[2] * nrm2;
         okh = errh <= a.e2[3] * nrm2;
     }
-    const bool ok4 = err4 <= a.e2[0] * nrm2;
-    const bool ok8 = err8 <= a.e2[1] * nrm2;
-    const bool finite = nrm2 <= DBL_MAX;   // false for Inf and NaN entries
 
     const int f16a = a.prefer_bf16 ? (okb ? 2 : (okh ? 3 : 4)) : (okh ? 3 : (okb ? 2 : 4));
     int f = ok4 ? 0 : (ok8 ? 1 : f16a);

@@ -43,23 +43,29 @@ __device__ __forceinline__ float block_absmax(const float (&w)[kPerLane]) {
 //
 // Subnormal s: fp32 division (correctly rounded) and the clamp, which then
 // matters (amax = 10 * 2^-149 gives s = 2^-149 and w/s = 10 > 7).
+//
+// The exact path runs only in waves where some lane needs it (a wave vote),
+// so the common case costs one multiply and one rounding per entry.
 __device__ __forceinline__ void lane_codes(const float (&w)[kPerLane], float s, float Qf,
                                            float (&q)[kPerLane]) {
-    if (s >= FLT_MIN && s <= FLT_MAX) {
-        const float rc = __builtin_amdgcn_rcpf(s);
+    const bool normal = s >= FLT_MIN && s <= FLT_MAX;
+    const bool subnormal = s > 0.0f && s < FLT_MIN;
+    const float rc = __builtin_amdgcn_rcpf(s);
+    bool slow = subnormal;
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) {
+        const float t = w[i] * rc;
+        const float r = rintf(t);
+        slow = slow || (normal && fabsf(t - r) > 0.4999f);
+        q[i] = normal ? r : 0.0f;                 // s = 0 or not finite: all codes 0
+    }
+    if (__builtin_expect(__any(slow), 0)) {
 #pragma unroll
         for (int i = 0; i < kPerLane; ++i) {
-            float t = w[i] * rc;
-            float r = rintf(t);
-            if (fabsf(t - r) > 0.4999f) r = fminf(fmaxf(rintf(w[i] / s), -Qf), Qf);
-            q[i] = r;
+            const float t = w[i] * rc;
+            const bool exact = subnormal || (normal && fabsf(t - rintf(t)) > 0.4999f);
+            if (exact) q[i] = fminf(fmaxf(rintf(w[i] / s), -Qf), Qf);
         }
-    } else if (s > 0.0f && s < FLT_MIN) {
-#pragma unroll
-        for (int i = 0; i < kPerLane; ++i) q[i] = fminf(fmaxf(rintf(w[i] / s), -Qf), Qf);
-    } else {
-#pragma unroll
-        for (int i = 0; i < kPerLane; ++i) q[i] = 0.0f;
     }
 }
 

@@ -86,6 +86,22 @@ def test_plan_shapes(orc, shape):
     np.testing.assert_array_equal(gpu_plan(W), orc.plan(W))
 
 
+def test_plan_near_ties(orc):
+    """Thresholds placed at a block's own error ratio and a hair either side
+    (the planner screens decisions in fp32 and computes the fp64 trees only
+    for blocks too close to call): the map equals the oracle's every time."""
+    rng = np.random.default_rng(31)
+    W = (rng.standard_t(4, size=(48, 64 * 8)) * 0.02).astype(np.float32)
+    err2, nrm2 = orc.block_errors(W)
+    for idx in rng.choice(48 * 8, size=12, replace=False):
+        n, kb = divmod(int(idx), 8)
+        for f, key in ((0, "eps_int4"), (1, "eps_int8")):
+            e = float(np.sqrt(err2[n, kb, f] / nrm2[n, kb]))
+            for eps in (e, np.nextafter(e, 0.0), np.nextafter(e, 1.0), e * (1 + 3e-6), e * (1 - 3e-6)):
+                kw = {key: float(eps)}
+                np.testing.assert_array_equal(gpu_plan(W, **kw), orc.plan(W, **kw), err_msg=f"{idx} {kw}")
+
+
 def test_plan_row_stride(orc):
     """ldw > K: the planner reads W[n, :K] of a wider array."""
     Wide = wl.small_weight(seed=3, n=64, k=384)
