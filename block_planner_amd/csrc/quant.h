@@ -34,11 +34,13 @@ __device__ __forceinline__ float block_absmax(const float (&w)[kPerLane]) {
 // Codes of one lane's 16 entries for scale s.
 //
 // Fast path (s a finite normal number): t = w * rcp(s) with the hardware
-// reciprocal (1 ulp).  |t - w/s| <= ~1.5 * 2^-23 * |w/s| <= 2.3e-5 because
-// |w/s| <= 127.0...; and |fl32(w/s) - w/s| <= 2^-18 for |w/s| < 128.  So when
-// t lies more than 1e-4 from a half-integer, fl32(w/s) lies on the same side
-// and rint(t) == rint(fl32(w/s)).  Otherwise the entry takes the exact path:
-// a correctly rounded fp32 division.  No clamp is needed on the fast path:
+// reciprocal (1 ulp).  |t - w/s| <= 1.5 * 2^-23 * |w/s| (+ tiny), with
+// |w/s| < Q + 0.5: at most 2.3e-5 for Q = 127 and 1.4e-6 for Q = 7; and
+// |fl32(w/s) - w/s| <= half an ulp: 2^-18 (3.8e-6) below 128, 2^-21 below 8.
+// So when t lies more than band = 4e-5 (Q = 127) or 3e-6 (Q = 7) from a
+// half-integer, fl32(w/s) lies strictly on the same side and rint(t) ==
+// rint(fl32(w/s)).  Otherwise the entry takes the exact path: a correctly
+// rounded fp32 division.  No clamp is needed on the fast path:
 // s = fl32(amax/Q) >= (amax/Q)(1 - 2^-24) gives |w/s| < Q + 0.5.
 //
 // Subnormal s: fp32 division (correctly rounded) and the clamp, which then
@@ -51,19 +53,20 @@ __device__ __forceinline__ void lane_codes(const float (&w)[kPerLane], float s, 
     const bool normal = s >= FLT_MIN && s <= FLT_MAX;
     const bool subnormal = s > 0.0f && s < FLT_MIN;
     const float rc = __builtin_amdgcn_rcpf(s);
+    const float edge = Qf < 8.0f ? 0.5f - 3e-6f : 0.5f - 4e-5f;   // 0.5 - band
     bool slow = subnormal;
 #pragma unroll
     for (int i = 0; i < kPerLane; ++i) {
         const float t = w[i] * rc;
         const float r = rintf(t);
-        slow = slow || (normal && fabsf(t - r) > 0.4999f);
+        slow = slow || (normal && fabsf(t - r) > edge);
         q[i] = normal ? r : 0.0f;                 // s = 0 or not finite: all codes 0
     }
     if (__builtin_expect(__any(slow), 0)) {
 #pragma unroll
         for (int i = 0; i < kPerLane; ++i) {
             const float t = w[i] * rc;
-            const bool exact = subnormal || (normal && fabsf(t - rintf(t)) > 0.4999f);
+            const bool exact = subnormal || (normal && fabsf(t - rintf(t)) > edge);
             if (exact) q[i] = fminf(fmaxf(rintf(w[i] / s), -Qf), Qf);
         }
     }
