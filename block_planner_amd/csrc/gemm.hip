@@ -4,9 +4,9 @@
 // float block sum_i w_i * x[m, 64kb+i] (HyperTensor 1.0.1 page: "fused
 // mixed-precision operators" run the plan; "Key Features": HyperLinear).
 //
-// A workgroup owns a 32*MS x 64 tile of y and walks K one 64-wide block at a
-// time.  Per step it dequantises the tile's 64 weight blocks (one per output
-// column) into LDS as bfloat16:
+// A workgroup owns a BM x 64 tile of y (BM = 256, 128 or 64 rows of x) and
+// walks K one 64-wide block at a time.  Per step the tile's 64 weight blocks
+// (one per output column) are dequantised into LDS as bfloat16:
 //   INT4 / INT8   the codes themselves (|q| <= 127 is exact in bfloat16);
 //                 the block's scale multiplies the 64-term partial afterwards;
 //   BF16          the values;
@@ -18,9 +18,10 @@
 // groups that hold an FP16 or FP32 block in that step.  Then every output
 // element adds scale[n] * partial[m, n] in fp32, in K order.
 //
-// Pipelining: two LDS stages.  While the MFMAs run on stage kb, the loads of
-// step kb+1 (x tile and packed blocks) are in flight in registers; they are
-// dequantised into the other stage after the MFMAs, then one barrier.
+// Roles and pipeline: four waves run the MFMAs and copy the next step's x
+// tile straight from memory into LDS (global_load_lds); four waves load the
+// packed blocks two steps ahead into registers and dequantise the next
+// step's into the other LDS stage.  One barrier per step.
 #include "gemv_common.h"
 #include "linear_host.h"
 
@@ -28,10 +29,11 @@ namespace ht {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr uint32_t kGemmBN = 64;          // output columns (weight rows) per workgroup
-constexpr uint32_t kGemmThreads = 256;    // 4 waves in a 2 x 2 arrangement
-constexpr uint32_t kLdsRow = 72;          // bfloat16 per LDS row: 64 + 8 of padding
+constexpr uint32_t kGemmBN = 64;          // output columns (weight rows) per workgroup: 4 groups of 16
+constexpr uint32_t kGemmThreads = 512;    // 4 MFMA waves + 4 producer waves
+constexpr uint32_t kLdsRow = 72;          // bfloat16 per weight row in LDS: 64 + 8 of padding
 
 struct GemmArgs {
     LayerDev w;
@@ -42,122 +44,246 @@ struct GemmArgs {
     float *partial;           // per-split partial sums [S][M][N] (no activation)
     int64_t ldy;
     uint32_t M;
-    uint32_t KBs;             // K-blocks per split (blockIdx.z)
+    uint32_t KBs;             // K-blocks per split
+    uint32_t MT, NT;          // row tiles of x, column tiles of the weight
     int act;
 };
 
-// One pipeline stage in LDS.
-template <int MS>
-struct GemmStage {
-    uint16_t xs[32 * MS][kLdsRow];     // x tile, bfloat16
-    uint16_t whi[kGemmBN][kLdsRow];    // weight planes, bfloat16, row = output column
+// The dequantised weight tile of one K-step.
+struct WStage {
+    uint16_t whi[kGemmBN][kLdsRow];    // bfloat16, row = output column
     uint16_t wlo[kGemmBN][kLdsRow];
     float scale[kGemmBN];
     uint32_t need_lo[4];               // per 16-column group
 };
 
-template <int MS>
-constexpr uint32_t gemm_lds_bytes() { return 2u * uint32_t(sizeof(GemmStage<MS>)); }
-
-// The packed block (or its absence) one thread dequantises in a step: block
-// quarter `part` (16 of the 64 entries) of output column n.
+// What one producer thread loads for one K-step: quarter `part` of the packed
+// block of its column (16 of the 64 entries).
 struct BlockLoad {
-    uint4 p[4];        // payload bytes of this quarter (8 / 16 / 32 / 32 / 64 bytes by format)
+    uint4 p[4];        // payload bytes of the quarter (8 / 16 / 32 / 32 / 64 bytes by format)
     float sc;
     uint32_t id2;      // the 4 bytes holding the block id (kb * R + r), as loaded
     uint32_t hi16;     // which half of id2 is the id
     int f;             // format, or 5 for "no block": the column is zero in this step
 };
 
+// Workgroup (mt, nt, split) owns rows [BM*mt, +BM) of x (BM = 64*MS) and
+// weight rows [64*nt, +64), over K-blocks [KBs*split, +KBs).  Consecutive
+// workgroup indices go to different XCDs in turn, so the index is permuted
+// (when the grid is a multiple of 8) such that each XCD gets a contiguous run
+// of tiles, mostly one row tile of x, which its L2 then serves to all of them.
+//
+// Waves 0-3 run the MFMAs (wave c: rows [16*MS*c, +16*MS), all 64 columns)
+// and copy the next step's x tile straight from memory into LDS; waves 4-7
+// load the packed blocks two steps ahead into registers and dequantise the
+// next step's.  Each SIMD holds one wave of each kind, so the matrix cores and
+// the vector ALUs work at the same time.  One workgroup barrier per step.
 template <int MS>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
-    extern __shared__ __align__(16) unsigned char gemm_lds[];
-    GemmStage<MS> *stage = reinterpret_cast<GemmStage<MS> *>(gemm_lds);
-    constexpr uint32_t BM = 32 * MS;
+    constexpr uint32_t BM = 64 * MS;
+    // x tiles: row r at 128 * r bytes, 16-byte slot s holds the row's entries
+    // [8 * (s ^ ((r >> 1) & 7)), +8) (a swizzle that makes the MFMA operand
+    // reads conflict-free); two steps in flight, as separate objects so that
+    // the compiler sees the copy into one does not touch the other
+    __shared__ __align__(16) uint16_t xs0[BM * 64], xs1[BM * 64];
+    __shared__ __align__(16) WStage wt0, wt1;
+
     const LayerDev &w = a.w;
     const uint32_t tid = threadIdx.x, lane = tid & 63;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const uint32_t wm = wave >> 1, wn = wave & 1;          // wave tile: rows [wm*16*MS, +16*MS), cols [wn*32, +32)
-    const uint32_t n0 = blockIdx.x * kGemmBN, m0 = blockIdx.y * BM;
+
+    uint32_t L = blockIdx.x;
+    if ((gridDim.x & 7u) == 0) L = (blockIdx.x & 7u) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    const uint32_t per_split = a.MT * a.NT;
+    const uint32_t zs = L / per_split, rem = L - zs * per_split;
+    const uint32_t mt = rem / a.NT, nt = rem - mt * a.NT;
+    const uint32_t n0 = nt * kGemmBN, m0 = mt * BM;
     const uint32_t KB = w.KB, R = w.R;
-    const uint32_t kb0 = blockIdx.z * a.KBs, kb1 = min(KB, kb0 + a.KBs);   // this split's K-blocks (non-empty)
+    const uint32_t kb0 = zs * a.KBs, kb1 = min(KB, kb0 + a.KBs);   // this split's K-blocks (non-empty)
+    const uint32_t nsteps = kb1 - kb0;
 
-    // ---- dequantisation role: thread -> (column block gb, quarter part) ----
-    const uint32_t gb = tid >> 2, part = tid & 3;
-    const uint32_t tile = n0 / R + gb / R, bi = gb % R;    // tile of the column, block slot within it
-    const bool tile_ok = tile < w.T;
-    const uint32_t *kbidx = reinterpret_cast<const uint32_t *>(w.base + w.off_kbidx);
-    // kbidx[f][tile*KB + kb] for the step about to be loaded (ka) and the one
-    // after it (kn): the index loads run two steps ahead of their use, so a
-    // step's block loads need one memory round trip, not two.
-    auto kbidx_at = [&](uint32_t kb, uint32_t (&v)[5]) {
+    if (wave < 4) {
+        // ================= MFMA waves =================
+        const uint32_t c = wave;
+        // x copy: 8-row group g = 2*MS*c + i of the tile per instruction i;
+        // lane l -> row 8g + l/8, slot l%8
+        const uint32_t xr = lane >> 3, xslot = lane & 7;
+        auto x_copy = [&](uint32_t kb, uint16_t *xs) {
 #pragma unroll
-        for (int f = 0; f < 5; ++f)
-            v[f] = tile_ok && kb <= KB ? kbidx[uint64_t(f) * w.nk + uint64_t(tile) * KB + kb] : 0u;
-    };
-    uint32_t ka[5], kn[5];
-    kbidx_at(kb0, ka);
-    kbidx_at(kb0 + 1, kn);
+            for (uint32_t i = 0; i < 2 * MS; ++i) {
+                const uint32_t g = 2 * MS * c + i, r = 8 * g + xr;
+                const uint32_t seg = xslot ^ ((r >> 1) & 7u);
+                const uint16_t *src = a.x + int64_t(min(m0 + r, a.M - 1u)) * a.ldx + kb * 64u + seg * 8u;
+                __builtin_amdgcn_global_load_lds(src, (lds_void *)(xs + 8 * g * 64), 16, 0, 0);
+            }
+        };
+        const uint32_t lr = lane & 15, lq = lane >> 4;      // MFMA operand row / k-quarter of this lane
+        f32x4 acc[MS][4];
+#pragma unroll
+        for (int i = 0; i < MS; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto load_block = [&](uint32_t kb) -> BlockLoad {
-        BlockLoad b;
-        b.f = 5;
-        b.sc = 1.0f;
+        auto mfma_step = [&](const uint16_t *xs, const WStage &st) {
+            bf16x8 A[MS][2];
+#pragma unroll
+            for (int i = 0; i < MS; ++i) {
+                const uint32_t r = 16 * MS * c + 16 * i + lr;
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    A[i][h] = *reinterpret_cast<const bf16x8 *>(xs + r * 64 + 8 * ((lq + 4 * h) ^ ((r >> 1) & 7u)));
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t c0 = 16 * j;
+                const bf16x8 Bh0 = *reinterpret_cast<const bf16x8 *>(&st.whi[c0 + lr][8 * lq]);
+                const bf16x8 Bh1 = *reinterpret_cast<const bf16x8 *>(&st.whi[c0 + lr][32 + 8 * lq]);
+                const float sc = st.scale[c0 + lr];
+                const bool lo = __builtin_amdgcn_readfirstlane(st.need_lo[j]) != 0u;
+                // independent MFMA chains per 16-row group, straight-line for each case
+                f32x4 cc[MS];
+                if (lo) {
+                    const bf16x8 Bl0 = *reinterpret_cast<const bf16x8 *>(&st.wlo[c0 + lr][8 * lq]);
+                    const bf16x8 Bl1 = *reinterpret_cast<const bf16x8 *>(&st.wlo[c0 + lr][32 + 8 * lq]);
+#pragma unroll
+                    for (int i = 0; i < MS; ++i) {
+                        cc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][0], Bh0, (f32x4{0.f, 0.f, 0.f, 0.f}), 0, 0, 0);
+                        cc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][1], Bh1, cc[i], 0, 0, 0);
+                        cc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][0], Bl0, cc[i], 0, 0, 0);
+                        cc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][1], Bl1, cc[i], 0, 0, 0);
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < MS; ++i) {
+                        cc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][0], Bh0, (f32x4{0.f, 0.f, 0.f, 0.f}), 0, 0, 0);
+                        cc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][1], Bh1, cc[i], 0, 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < MS; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(sc, cc[i][e], acc[i][j][e]);
+            }
+        };
+
+        x_copy(kb0, xs0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copy is in LDS
+        __syncthreads();
+        for (uint32_t t = 0; t < nsteps; t += 2) {
+            if (t + 1 < nsteps) x_copy(kb0 + t + 1, xs1);
+            mfma_step(xs0, wt0);
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            __syncthreads();
+            if (t + 1 < nsteps) {
+                if (t + 2 < nsteps) x_copy(kb0 + t + 2, xs0);
+                mfma_step(xs1, wt1);
+                __builtin_amdgcn_s_waitcnt(0x0F70);
+                __syncthreads();
+            }
+        }
+
+        // ---- output: lane holds column lr, rows 4*(lane/16) + e of each 16x16 tile ----
+#pragma unroll
+        for (int i = 0; i < MS; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t n = n0 + 16 * j + lr;
+                if (n >= w.N) continue;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t m = m0 + 16 * MS * c + 16 * i + 4 * lq + e;
+                    if (m >= a.M) continue;
+                    float v = acc[i][j][e];
+                    if (a.partial) {
+                        a.partial[(uint64_t(zs) * a.M + m) * w.N + n] = v;
+                        continue;
+                    }
+                    if (a.act == HT_ACT_RELU) v = v > 0.0f ? v : 0.0f;   // +0 for zero, negative and NaN
+                    if (a.ybf) a.ybf[int64_t(m) * a.ldy + n] = f32_to_bf16_rne(v);
+                    else a.y[int64_t(m) * a.ldy + n] = v;
+                }
+            }
+        return;
+    }
+
+    // ================= producer waves =================
+    // thread pt -> quarter `part` of column gb
+    const uint32_t pt = tid - 256, pw = wave - 4, part = pt & 3, gb = pt >> 2;
+    const uint8_t *base = w.base;                            // offsets below are 32-bit (buffer < 4 GiB)
+    uint32_t opay[5], oids[5];
+#pragma unroll
+    for (int f = 0; f < 5; ++f) {
+        opay[f] = uint32_t(w.off_pay[f]);
+        oids[f] = uint32_t(w.off_ids[f]);
+    }
+    const uint32_t osc0 = uint32_t(w.off_scale[0]), osc1 = uint32_t(w.off_scale[1]);
+    const uint32_t tile = n0 / R + gb / R, bi = gb % R;     // tile of the column, block slot within it
+    const bool tok = tile < w.T;
+    const uint32_t kbx = uint32_t(w.off_kbidx) + 4u * (tok ? tile * KB : 0u);
+    // kbidx[f][tile*KB + kb]: block index where step kb starts in format f
+    // (loaded by every lane; a column past N reads tile 0 and takes zeros)
+    auto kload = [&](uint32_t kb, uint32_t (&v)[5]) {
+        kb = min(kb, kb1);
+#pragma unroll
+        for (int f = 0; f < 5; ++f) {
+            const uint32_t x = *reinterpret_cast<const uint32_t *>(base + kbx + 4u * (uint32_t(f) * w.nk + kb));
+            v[f] = tok ? x : 0u;
+        }
+    };
+
+    // Loads of one column's block in the step that starts at ka and ends at
+    // kn (a step past the split's end has no blocks): up to four 16-byte loads
+    // at addresses chosen per format; a missing block reads the buffer's first
+    // bytes.  INT4's 8-byte quarter p comes with its neighbour in a 16-byte
+    // load at 16 * (p / 2).
+    auto load_block = [&](const uint32_t (&ka)[5], const uint32_t (&kn)[5]) -> BlockLoad {
+        BlockLoad q;
+        q.f = 5;
         uint32_t cum = 0, blk = 0;
 #pragma unroll
         for (int f = 0; f < 5; ++f) {
-            const uint32_t c = kn[f] - ka[f];
-            if (b.f == 5 && bi < cum + c) {
-                b.f = f;
+            const uint32_t cnt = kn[f] - ka[f];
+            if (q.f == 5 && bi < cum + cnt) {
+                q.f = f;
                 blk = ka[f] + (bi - cum);
             }
-            cum += c;
+            cum += cnt;
         }
-#pragma unroll
-        for (int f = 0; f < 5; ++f) ka[f] = kn[f];
-        kbidx_at(kb + 2, kn);
-        // Branch-free loads (so no load waits for another): four 16-byte loads
-        // at addresses chosen per format, repeating the last one where the
-        // quarter is shorter; a missing block reads the buffer's first bytes.
-        // INT4's 8-byte quarter p comes with its neighbour in a 16-byte load
-        // at 16 * (p / 2); the dequantisation picks its half.
-        const bool has = b.f < 5;
-        const int f = has ? b.f : 0;
-        uint64_t po = 0, io = 0, so = 0;
-        uint32_t qb = 0, nl = 1;
+        const bool has = q.f < 5;
+        const int f = has ? q.f : 0;
+        uint32_t po = 0, io = 0, so = 0, qb = 0, nl = 1;
 #pragma unroll
         for (int g = 0; g < 5; ++g) {
             if (f == g) {
-                po = w.off_pay[g] + uint64_t(blk) * uint32_t(pay_bytes(g));
-                io = w.off_ids[g] + ((2ull * blk) & ~3ull);
-                so = g < 2 ? w.off_scale[g] + 4ull * blk : 0ull;
+                po = opay[g] + blk * uint32_t(pay_bytes(g));
+                io = oids[g] + ((2u * blk) & ~3u);
+                so = g == 0 ? osc0 + 4u * blk : g == 1 ? osc1 + 4u * blk : 0u;
                 qb = g == 0 ? 16u * (part >> 1) : uint32_t(pay_bytes(g) / 4) * part;
                 nl = g < 2 ? 1u : g == 4 ? 4u : 2u;
             }
         }
-        if (!has) po = io = so = 0;
-        const uint8_t *pq = w.base + po + qb;
+        if (!has) po = io = so = qb = 0;
+        // the first 16 bytes always; the rest only for lanes whose quarter is
+        // longer (BF16 / FP16 / FP32), so an integer-only wave skips them
+        q.p[0] = *reinterpret_cast<const uint4 *>(base + (po + qb));
 #pragma unroll
-        for (uint32_t j = 0; j < 4; ++j) {
-            const uint32_t jj = j < nl ? j : nl - 1u;
-            b.p[j] = *reinterpret_cast<const uint4 *>(pq + 16u * jj);
-        }
-        b.id2 = *reinterpret_cast<const uint32_t *>(w.base + io);
-        b.hi16 = blk & 1u;
-        b.sc = *reinterpret_cast<const float *>(w.base + so);   // meaningful for INT4 / INT8 only
-        return b;
+        for (uint32_t j = 1; j < 4; ++j)
+            q.p[j] = j < nl ? *reinterpret_cast<const uint4 *>(base + (po + qb + 16u * j)) : make_uint4(0, 0, 0, 0);
+        q.id2 = *reinterpret_cast<const uint32_t *>(base + io);
+        q.hi16 = blk & 1u;
+        q.sc = *reinterpret_cast<const float *>(base + so);   // meaningful for INT4 / INT8 only
+        return q;
     };
 
-    // Dequantise into stage st: entries [16*part, 16*part + 16) of column gb
-    // (INT4 quarters cover two runs of 8, see the nibble order of the layout).
-    // Entries are produced as packed bfloat16 pairs: integers via an exact
-    // fp32 conversion whose upper half is the bfloat16 (v_perm packs two),
-    // floats as hi = upper half (truncation) and lo = bf16_rne(w - hi)
-    // (v_cvt_pk_bf16_f32).  A non-finite FP16/FP32 entry makes lo NaN, so its
-    // output column is NaN.
-    auto store_block = [&](const BlockLoad &b, GemmStage<MS> &st) {
+    // Dequantise one column's quarter into st: entries [16*part, 16*part + 16)
+    // (INT4 quarters cover two runs of 8, see the nibble order of the layout),
+    // as packed bfloat16 pairs: integers via an exact fp32 conversion whose
+    // upper half is the bfloat16 (v_perm packs two), floats as hi = upper half
+    // (truncation) and lo = bf16_rne(w - hi) (v_cvt_pk_bf16_f32).  A
+    // non-finite FP16/FP32 entry makes lo NaN, so its output column is NaN.
+    auto store_block = [&](const BlockLoad &b, WStage &st) {
         const uint32_t id = b.hi16 ? b.id2 >> 16 : b.id2;
-        const uint32_t col = (gb / R) * R + (b.f < 5 ? (id & (R - 1u)) : bi);   // column within the workgroup's 64
+        const uint32_t col = (gb / R) * R + (b.f < 5 ? (id & (R - 1u)) : bi);   // within the 64
         const bool flt = b.f == 3 || b.f == 4;
         const bool any_lo = __any(flt);                         // this wave's 16 columns need the lo plane
         const uint32_t u[16] = {b.p[0].x, b.p[0].y, b.p[0].z, b.p[0].w, b.p[1].x, b.p[1].y, b.p[1].z, b.p[1].w,
@@ -184,7 +310,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
             k1 = k0 + 16;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const uint32_t wd = (part & 1) ? u[2 + (i >> 1)] : u[i >> 1], sh = 16 * (i & 1);
+                const uint32_t wd = (part & 1) ? ((i >> 1) ? u[3] : u[2]) : ((i >> 1) ? u[1] : u[0]);
+                const uint32_t sh = 16 * (i & 1);
                 hp[i] = pair_hi(float(nib(wd, sh)), float(nib(wd, sh + 8)));
                 hp[4 + i] = pair_hi(float(nib(wd, sh + 4)), float(nib(wd, sh + 12)));
             }
@@ -229,117 +356,40 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
             *reinterpret_cast<uint4 *>(&st.wlo[col][k1]) = make_uint4(lp[4], lp[5], lp[6], lp[7]);
         }
         if (part == 0) st.scale[col] = b.f < 2 ? b.sc : 1.0f;
-        if (lane == 0) st.need_lo[wave] = any_lo ? 1u : 0u;
+        if (lane == 0) st.need_lo[pw] = any_lo ? 1u : 0u;
     };
 
-    // ---- x tile: BM rows x 64 entries, 16 bytes per load ----
-    constexpr uint32_t kXLoads = BM * 8 / kGemmThreads;     // = MS
-    auto load_x = [&](uint32_t kb, uint4 (&xv)[kXLoads]) {
-#pragma unroll
-        for (uint32_t j = 0; j < kXLoads; ++j) {
-            const uint32_t idx = tid + kGemmThreads * j, row = idx >> 3, seg = idx & 7;
-            const uint32_t m = min(m0 + row, a.M - 1u);   // rows past M read row M-1; zeroed when stored
-            xv[j] = *reinterpret_cast<const uint4 *>(a.x + int64_t(m) * a.ldx + kb * 64 + seg * 8);
-        }
-    };
-    auto store_x = [&](const uint4 (&xv)[kXLoads], GemmStage<MS> &st) {
-#pragma unroll
-        for (uint32_t j = 0; j < kXLoads; ++j) {
-            const uint32_t idx = tid + kGemmThreads * j, row = idx >> 3, seg = idx & 7;
-            *reinterpret_cast<uint4 *>(&st.xs[row][seg * 8]) = m0 + row < a.M ? xv[j] : make_uint4(0, 0, 0, 0);
-        }
-    };
-
-    f32x4 acc[MS][2];
-#pragma unroll
-    for (int i = 0; i < MS; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    {   // prologue: step 0 into stage 0
-        uint4 xv[kXLoads];
-        const BlockLoad b = load_block(kb0);
-        load_x(kb0, xv);
-        store_x(xv, stage[0]);
-        store_block(b, stage[0]);
+    // kbidx entries run one step ahead of the block loads, which run two
+    // steps ahead of the dequantisation
+    uint32_t K2[5], K3[5], K4[5];
+    BlockLoad QA, QB;
+    {
+        uint32_t K0[5], K1[5];
+        kload(kb0, K0);
+        kload(kb0 + 1, K1);
+        kload(kb0 + 2, K2);
+        kload(kb0 + 3, K3);
+        QB = load_block(K0, K1);
+        QA = load_block(K1, K2);
+        store_block(QB, wt0);
     }
     __syncthreads();
-
-    const uint32_t lr = lane & 15, lk = (lane >> 4) * 8;    // MFMA operand row / first k of this lane
-    for (uint32_t kb = kb0; kb < kb1; ++kb) {
-        GemmStage<MS> &st = stage[(kb - kb0) & 1];
-        const bool more = kb + 1 < kb1;
-        uint4 xv[kXLoads];
-        BlockLoad b;
-        if (more) {   // block loads first: nothing in them waits, so they never wait for x's loads
-            b = load_block(kb + 1);
-            load_x(kb + 1, xv);
+    // qc: the loads of step t+1; qn receives those of step t+2
+    auto step = [&](uint32_t t, BlockLoad &qc, BlockLoad &qn, WStage &dst) {
+        kload(kb0 + t + 4, K4);
+        qn = load_block(K2, K3);
+#pragma unroll
+        for (int f = 0; f < 5; ++f) {
+            K2[f] = K3[f];
+            K3[f] = K4[f];
         }
-        // MFMAs on this stage
-        bf16x8 A[MS][2];
-#pragma unroll
-        for (int i = 0; i < MS; ++i)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                A[i][h] = *reinterpret_cast<const bf16x8 *>(&st.xs[wm * 16 * MS + 16 * i + lr][32 * h + lk]);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const uint32_t c0 = wn * 32 + 16 * j;
-            const bf16x8 Bh0 = *reinterpret_cast<const bf16x8 *>(&st.whi[c0 + lr][lk]);
-            const bf16x8 Bh1 = *reinterpret_cast<const bf16x8 *>(&st.whi[c0 + lr][32 + lk]);
-            const float sc = st.scale[c0 + lr];
-            const bool lo = __builtin_amdgcn_readfirstlane(st.need_lo[c0 >> 4]) != 0u;
-            // independent MFMA chains per 16-row group, straight-line for each case
-            f32x4 c[MS];
-            if (lo) {
-                const bf16x8 Bl0 = *reinterpret_cast<const bf16x8 *>(&st.wlo[c0 + lr][lk]);
-                const bf16x8 Bl1 = *reinterpret_cast<const bf16x8 *>(&st.wlo[c0 + lr][32 + lk]);
-#pragma unroll
-                for (int i = 0; i < MS; ++i) {
-                    c[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][0], Bh0, (f32x4{0.f, 0.f, 0.f, 0.f}), 0, 0, 0);
-                    c[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][1], Bh1, c[i], 0, 0, 0);
-                    c[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][0], Bl0, c[i], 0, 0, 0);
-                    c[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][1], Bl1, c[i], 0, 0, 0);
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < MS; ++i) {
-                    c[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][0], Bh0, (f32x4{0.f, 0.f, 0.f, 0.f}), 0, 0, 0);
-                    c[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][1], Bh1, c[i], 0, 0, 0);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < MS; ++i)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(sc, c[i][e], acc[i][j][e]);
-        }
-        if (more) {
-            GemmStage<MS> &nx = stage[(kb + 1 - kb0) & 1];
-            store_x(xv, nx);
-            store_block(b, nx);
-        }
+        if (t + 1 < nsteps) store_block(qc, dst);
         __syncthreads();
+    };
+    for (uint32_t t = 0; t < nsteps; t += 2) {
+        step(t, QA, QB, wt1);
+        if (t + 1 < nsteps) step(t + 1, QB, QA, wt0);
     }
-
-    // ---- output: lane holds column lr, rows 4*(lane/16) + e of each 16x16 tile ----
-#pragma unroll
-    for (int i = 0; i < MS; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const uint32_t n = n0 + wn * 32 + 16 * j + lr;
-            if (n >= w.N) continue;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t m = m0 + wm * 16 * MS + 16 * i + 4 * (lane >> 4) + e;
-                if (m >= a.M) continue;
-                float v = acc[i][j][e];
-                if (a.partial) {
-                    a.partial[(uint64_t(blockIdx.z) * a.M + m) * w.N + n] = v;
-                    continue;
-                }
-                if (a.act == HT_ACT_RELU) v = v > 0.0f ? v : 0.0f;   // +0 for zero, negative and NaN
-                if (a.ybf) a.ybf[int64_t(m) * a.ldy + n] = f32_to_bf16_rne(v);
-                else a.y[int64_t(m) * a.ldy + n] = v;
-            }
-        }
 }
 
 // ---------------------------------------------------------------------------
@@ -348,36 +398,28 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
 namespace {
 
 template <int MS>
-void launch_gemm(const GemmArgs &a, hipStream_t s) {
-    static bool attr = false;   // dynamic LDS above 64 KiB must be allowed once per kernel
-    if (!attr) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_kernel<MS>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(gemm_lds_bytes<MS>()));
-        attr = true;
-    }
-    const dim3 grid((a.w.N + kGemmBN - 1) / kGemmBN, (a.M + 32 * MS - 1) / (32 * MS),
-                    (a.w.KB + a.KBs - 1) / a.KBs);
-    hipLaunchKernelGGL(gemm_kernel<MS>, grid, dim3(kGemmThreads), gemm_lds_bytes<MS>(), s, a);
+void launch_gemm(const GemmArgs &a, uint32_t S, hipStream_t s) {
+    const uint32_t grid = a.MT * a.NT * S;
+    hipLaunchKernelGGL(gemm_kernel<MS>, dim3(grid), dim3(kGemmThreads), 0, s, a);
 }
 
 }  // namespace
 
 namespace {
 
-constexpr int64_t kGemmChunkRows = 65535 * 32;   // rows per launch (grid y limit at 32-row tiles)
-constexpr uint64_t kSplitTarget = 768;             // workgroups wanted: three per compute unit
+constexpr int64_t kGemmChunkRows = int64_t(1) << 20;   // rows per launch
+constexpr uint64_t kSplitTarget = 256;                   // workgroups wanted: one per compute unit
 
-uint32_t gemm_bm(int64_t M) { return M >= 128 ? 128u : M >= 64 ? 64u : 32u; }
+uint32_t gemm_bm(int64_t M) { return M >= 256 ? 256u : M >= 128 ? 128u : 64u; }
 
-// K-splits: three workgroups per compute unit (each step of a workgroup
-// waits for its blocks' loads, so more of them in flight hide that), at least 4
-// K-blocks per split, every split non-empty.
+// K-splits when there are fewer tiles than compute units: at least 8 K-blocks
+// per split, every split non-empty.
 uint32_t gemm_splits(const ht_packed_weight *w, int64_t M) {
     const uint32_t KB = uint32_t(w->K / kBlockK);
     const uint64_t tiles = uint64_t((w->N + kGemmBN - 1) / kGemmBN) * uint64_t((M + gemm_bm(M) - 1) / gemm_bm(M));
-    if (tiles >= kSplitTarget || KB < 8) return 1;
+    if (tiles * 4 >= kSplitTarget * 3 || KB < 16) return 1;
     uint32_t S = uint32_t((kSplitTarget + tiles - 1) / tiles);
-    if (S > KB / 4) S = KB / 4;
+    if (S > KB / 8) S = KB / 8;
     const uint32_t KBs = (KB + S - 1) / S;
     return (KB + KBs - 1) / KBs;
 }
@@ -400,16 +442,19 @@ ht_status run_gemm(const ht_packed_weight *w, const uint16_t *x, int64_t M, int6
     for (int64_t m0 = 0; m0 < M; m0 += kGemmChunkRows) {
         const int64_t Mt = M - m0 < kGemmChunkRows ? M - m0 : kGemmChunkRows;
         const uint32_t S = gemm_splits(w, Mt);
+        const uint32_t BM = gemm_bm(Mt);
         a.x = x + m0 * ldx;
         a.y = y ? y + m0 * ldy : nullptr;
         a.ybf = ybf ? ybf + m0 * ldy : nullptr;
         a.partial = S > 1 ? static_cast<float *>(ws) : nullptr;
         a.M = uint32_t(Mt);
         a.KBs = (a.w.KB + S - 1) / S;
-        switch (gemm_bm(Mt)) {
-        case 128: launch_gemm<4>(a, s); break;
-        case 64: launch_gemm<2>(a, s); break;
-        default: launch_gemm<1>(a, s); break;
+        a.MT = uint32_t((Mt + BM - 1) / BM);
+        a.NT = uint32_t((a.w.N + kGemmBN - 1) / kGemmBN);
+        switch (BM) {
+        case 256: launch_gemm<4>(a, S, s); break;
+        case 128: launch_gemm<2>(a, S, s); break;
+        default: launch_gemm<1>(a, S, s); break;
         }
         HT_LAUNCH_CHECK();
         if (S > 1) {

@@ -172,6 +172,7 @@ bool desc_ok(const ht_packed_weight *w) {
     const int64_t R = w->row_tile;
     if (!(R == 1 || R == 2 || R == 4 || R == 8 || R == 16)) return false;
     if (w->n_tiles != (w->N + R - 1) / R) return false;
+    if (w->bytes > 0xFFFFFFFFull) return false;   // addressed with 32-bit offsets
     return true;
 }
 

@@ -236,6 +236,7 @@ ht_status layout_of(int64_t N, int64_t K, int64_t R, const int64_t c[5], Layout 
         o += align256(uint64_t(pay_bytes(f)) * uint64_t(c[f]));
     }
     L->total = o;
+    if (o > 0xFFFFFFFFull) return HT_ESHAPE;   // the kernels address the buffer with 32-bit offsets
     return HT_OK;
 }
 

@@ -142,7 +142,9 @@ ht_status ht_plan_counts(const uint8_t *fmt_map, int64_t N, int64_t K,
                          int64_t *counts5, ht_stream stream);
 
 /* ht_pack_bytes -- size of the packed buffer (host only, no GPU work).
- *   row_tile in {1, 2, 4, 8, 16}; counts5 (host) from ht_plan_counts. */
+ *   row_tile in {1, 2, 4, 8, 16}; counts5 (host) from ht_plan_counts.
+ *   HT_ESHAPE when the buffer would exceed 4 GiB - 1 (the kernels address
+ *   it with 32-bit offsets): split such a weight along N. */
 ht_status ht_pack_bytes(int64_t N, int64_t K, int64_t row_tile,
                         const int64_t counts5[5], size_t *bytes);
 

@@ -52,6 +52,7 @@ def test_pack_bytes_matches_layout(orc):
     ((256, 256, 16, [-1, 1025, 0, 0, 0]), 1),
     ((0, 256, 16, [0, 0, 0, 0, 0]), 2),
     ((16, 64 * 5000, 16, [0, 80000, 0, 0, 0]), 2), # K/64 * R > 65536 (16-bit block ids)
+    ((32768, 32768, 16, [0, 0, 0, 0, 32768 * 512]), 2),  # 4 GiB of FP32 blocks: past 32-bit offsets
 ])
 def test_pack_bytes_rejects(args, code):
     with pytest.raises(B.HTError) as e:
