@@ -29,7 +29,6 @@ namespace ht {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr uint32_t kGemmBN = 64;          // output columns (weight rows) per workgroup: 4 groups of 16
 constexpr uint32_t kGemmThreads = 512;    // 4 MFMA waves + 4 producer waves
@@ -83,9 +82,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
     constexpr uint32_t BM = 64 * MS;
     // x tiles: row r at 128 * r bytes, 16-byte slot s holds the row's entries
     // [8 * (s ^ ((r >> 1) & 7)), +8) (a swizzle that makes the MFMA operand
-    // reads conflict-free); two steps in flight, as separate objects so that
-    // the compiler sees the copy into one does not touch the other
-    __shared__ __align__(16) uint16_t xs0[BM * 64], xs1[BM * 64];
+    // reads conflict-free); three steps in flight, as separate objects so
+    // that the compiler sees the copies into one do not touch the others
+    __shared__ __align__(16) uint16_t xs0[BM * 64], xs1[BM * 64], xs2[BM * 64];
     __shared__ __align__(16) WStage wt0, wt1;
 
     const LayerDev &w = a.w;
@@ -108,13 +107,22 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
         // x copy: 8-row group g = 2*MS*c + i of the tile per instruction i;
         // lane l -> row 8g + l/8, slot l%8
         const uint32_t xr = lane >> 3, xslot = lane & 7;
+        // Issued as inline assembly (M0 = LDS destination of the wave's 1 KiB),
+        // so the compiler does not add waits for these copies before unrelated
+        // LDS reads; this wave issues no other vector-memory loads, and waits
+        // for its copies explicitly (vmcnt(0)) before the barrier that
+        // publishes them.
         auto x_copy = [&](uint32_t kb, uint16_t *xs) {
 #pragma unroll
             for (uint32_t i = 0; i < 2 * MS; ++i) {
                 const uint32_t g = 2 * MS * c + i, r = 8 * g + xr;
                 const uint32_t seg = xslot ^ ((r >> 1) & 7u);
                 const uint16_t *src = a.x + int64_t(min(m0 + r, a.M - 1u)) * a.ldx + kb * 64u + seg * 8u;
-                __builtin_amdgcn_global_load_lds(src, (lds_void *)(xs + 8 * g * 64), 16, 0, 0);
+                const uint32_t dst = uint32_t(uintptr_t((__attribute__((address_space(3))) uint16_t *)(xs + 8 * g * 64)));
+                asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                             :
+                             : "v"(src), "s"(dst)
+                             : "memory", "m0");
             }
         };
         const uint32_t lr = lane & 15, lq = lane >> 4;      // MFMA operand row / k-quarter of this lane
@@ -124,8 +132,15 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+        // One K-step on LDS stages xs / st.  Hi planes: a fresh 64-term partial
+        // per 16x16 tile, added to acc times the column's scale (all operands
+        // read first, so the MFMAs and the scaling run as one straight-line
+        // sequence).  Lo planes (only in 16-column groups with an FP16 / FP32
+        // block; zero in integer columns, and float blocks have scale 1) go
+        // into acc directly through the MFMA accumulator.
         auto mfma_step = [&](const uint16_t *xs, const WStage &st) {
-            bf16x8 A[MS][2];
+            bf16x8 A[MS][2], Bh[4][2];
+            float sc[4];
 #pragma unroll
             for (int i = 0; i < MS; ++i) {
                 const uint32_t r = 16 * MS * c + 16 * i + lr;
@@ -135,51 +150,59 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const uint32_t c0 = 16 * j;
-                const bf16x8 Bh0 = *reinterpret_cast<const bf16x8 *>(&st.whi[c0 + lr][8 * lq]);
-                const bf16x8 Bh1 = *reinterpret_cast<const bf16x8 *>(&st.whi[c0 + lr][32 + 8 * lq]);
-                const float sc = st.scale[c0 + lr];
-                const bool lo = __builtin_amdgcn_readfirstlane(st.need_lo[j]) != 0u;
-                // independent MFMA chains per 16-row group, straight-line for each case
-                f32x4 cc[MS];
-                if (lo) {
-                    const bf16x8 Bl0 = *reinterpret_cast<const bf16x8 *>(&st.wlo[c0 + lr][8 * lq]);
-                    const bf16x8 Bl1 = *reinterpret_cast<const bf16x8 *>(&st.wlo[c0 + lr][32 + 8 * lq]);
+                Bh[j][0] = *reinterpret_cast<const bf16x8 *>(&st.whi[16 * j + lr][8 * lq]);
+                Bh[j][1] = *reinterpret_cast<const bf16x8 *>(&st.whi[16 * j + lr][32 + 8 * lq]);
+                sc[j] = st.scale[16 * j + lr];
+            }
+            const uint4 nlo = *reinterpret_cast<const uint4 *>(st.need_lo);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int i = 0; i < MS; ++i) {
+                    f32x4 cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][0], Bh[j][0], (f32x4{0.f, 0.f, 0.f, 0.f}), 0, 0, 0);
+                    cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][1], Bh[j][1], cc, 0, 0, 0);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(sc[j], cc[e], acc[i][j][e]);
+                }
+            const uint32_t lo[4] = {nlo.x, nlo.y, nlo.z, nlo.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (__builtin_amdgcn_readfirstlane(lo[j]) != 0u) {
+                    const bf16x8 Bl0 = *reinterpret_cast<const bf16x8 *>(&st.wlo[16 * j + lr][8 * lq]);
+                    const bf16x8 Bl1 = *reinterpret_cast<const bf16x8 *>(&st.wlo[16 * j + lr][32 + 8 * lq]);
 #pragma unroll
                     for (int i = 0; i < MS; ++i) {
-                        cc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][0], Bh0, (f32x4{0.f, 0.f, 0.f, 0.f}), 0, 0, 0);
-                        cc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][1], Bh1, cc[i], 0, 0, 0);
-                        cc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][0], Bl0, cc[i], 0, 0, 0);
-                        cc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][1], Bl1, cc[i], 0, 0, 0);
-                    }
-                } else {
-#pragma unroll
-                    for (int i = 0; i < MS; ++i) {
-                        cc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][0], Bh0, (f32x4{0.f, 0.f, 0.f, 0.f}), 0, 0, 0);
-                        cc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][1], Bh1, cc[i], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][0], Bl0, acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][1], Bl1, acc[i][j], 0, 0, 0);
                     }
                 }
-#pragma unroll
-                for (int i = 0; i < MS; ++i)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(sc, cc[i][e], acc[i][j][e]);
             }
         };
 
+        // Workgroup barrier that leaves this wave's outstanding x copies in
+        // flight (the copy of a step is waited for, vmcnt(0), at the end of
+        // the step before the one that reads it).
+        auto cbar = [&]() {
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+            __builtin_amdgcn_s_barrier();
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        };
+        // x: three LDS stages; the copy for step t+2 is issued at the end of step t
         x_copy(kb0, xs0);
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copy is in LDS
-        __syncthreads();
-        for (uint32_t t = 0; t < nsteps; t += 2) {
-            if (t + 1 < nsteps) x_copy(kb0 + t + 1, xs1);
-            mfma_step(xs0, wt0);
-            __builtin_amdgcn_s_waitcnt(0x0F70);
-            __syncthreads();
-            if (t + 1 < nsteps) {
-                if (t + 2 < nsteps) x_copy(kb0 + t + 2, xs0);
-                mfma_step(xs1, wt1);
-                __builtin_amdgcn_s_waitcnt(0x0F70);
-                __syncthreads();
-            }
+        if (nsteps > 1) x_copy(kb0 + 1, xs1);
+        cbar();
+        auto cstep = [&](uint32_t t, const uint16_t *xc, uint16_t *xn2) {
+            mfma_step(xc, (t & 1) ? wt1 : wt0);
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the copy for step t+1 is in LDS
+            if (t + 2 < nsteps) x_copy(kb0 + t + 2, xn2);
+            cbar();
+        };
+        for (uint32_t t = 0; t < nsteps; t += 3) {
+            cstep(t, xs0, xs2);
+            if (t + 1 < nsteps) cstep(t + 1, xs1, xs0);
+            if (t + 2 < nsteps) cstep(t + 2, xs2, xs1);
         }
 
         // ---- output: lane holds column lr, rows 4*(lane/16) + e of each 16x16 tile ----
