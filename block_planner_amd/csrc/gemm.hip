@@ -141,24 +141,29 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
         auto mfma_step = [&](const uint16_t *xs, const WStage &st) {
             bf16x8 A[MS][2], Bh[4][2];
             float sc[4];
-#pragma unroll
-            for (int i = 0; i < MS; ++i) {
+            // read order = first use: row tile 0, all column groups, then the
+            // other row tiles (LDS reads complete in order, so the first MFMAs
+            // wait for four reads, not all of them)
+            auto readA = [&](int i) {
                 const uint32_t r = 16 * MS * c + 16 * i + lr;
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
                     A[i][h] = *reinterpret_cast<const bf16x8 *>(xs + r * 64 + 8 * ((lq + 4 * h) ^ ((r >> 1) & 7u)));
-            }
+            };
+            readA(0);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 Bh[j][0] = *reinterpret_cast<const bf16x8 *>(&st.whi[16 * j + lr][8 * lq]);
                 Bh[j][1] = *reinterpret_cast<const bf16x8 *>(&st.whi[16 * j + lr][32 + 8 * lq]);
                 sc[j] = st.scale[16 * j + lr];
             }
+#pragma unroll
+            for (int i = 1; i < MS; ++i) readA(i);
             const uint4 nlo = *reinterpret_cast<const uint4 *>(st.need_lo);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int i = 0; i < MS; ++i)
 #pragma unroll
-                for (int i = 0; i < MS; ++i) {
+                for (int j = 0; j < 4; ++j) {
                     f32x4 cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][0], Bh[j][0], (f32x4{0.f, 0.f, 0.f, 0.f}), 0, 0, 0);
                     cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][1], Bh[j][1], cc, 0, 0, 0);
 #pragma unroll
