@@ -436,17 +436,19 @@ void launch_gemm(const GemmArgs &a, uint32_t S, hipStream_t s) {
 namespace {
 
 constexpr int64_t kGemmChunkRows = int64_t(1) << 20;   // rows per launch
-constexpr uint64_t kSplitTarget = 256;                   // workgroups wanted: one per compute unit
+constexpr uint64_t kSplitTarget = 256;                   // compute units
 
 uint32_t gemm_bm(int64_t M) { return M >= 256 ? 256u : M >= 128 ? 128u : 64u; }
 
-// K-splits when there are fewer tiles than compute units: at least 8 K-blocks
-// per split, every split non-empty.
+// K-splits when there are fewer tiles than workgroup slots (one per compute
+// unit, two for 64-row tiles, whose LDS and registers allow two): at least 8
+// K-blocks per split, every split non-empty.
 uint32_t gemm_splits(const ht_packed_weight *w, int64_t M) {
     const uint32_t KB = uint32_t(w->K / kBlockK);
     const uint64_t tiles = uint64_t((w->N + kGemmBN - 1) / kGemmBN) * uint64_t((M + gemm_bm(M) - 1) / gemm_bm(M));
-    if (tiles * 4 >= kSplitTarget * 3 || KB < 16) return 1;
-    uint32_t S = uint32_t((kSplitTarget + tiles - 1) / tiles);
+    const uint64_t target = gemm_bm(M) == 64 ? 2 * kSplitTarget : kSplitTarget;   // two 64-row workgroups fit a CU
+    if (tiles * 4 >= target * 3 || KB < 16) return 1;
+    uint32_t S = uint32_t((target + tiles - 1) / tiles);
     if (S > KB / 8) S = KB / 8;
     const uint32_t KBs = (KB + S - 1) / S;
     return (KB + KBs - 1) / KBs;
