@@ -3,17 +3,16 @@
 // buffers"; "Key Features": inference-only mode, which drops the fp32 master
 // weights -- after packing, the buffers are all the linear needs).
 //
-// Three kernels on the caller's stream:
-//   1. column counts: per (row tile t, K-block kb) and format, the number of
-//      rows of the tile holding that format -> kbidx[f][t*KB + kb];
-//   2. exclusive scan of each format's counts in (t, kb) order (one
-//      workgroup per format), total at kbidx[f][T*KB];
-//   3. scatter: one quad of lanes per block, in (t, kb, r) order; a block's
+// Two kernels on the caller's stream:
+//   1. index: one workgroup per format counts, per (row tile t, K-block kb),
+//      the rows of the tile holding that format and writes the exclusive
+//      scan of these counts in (t, kb) order -> kbidx[f][t*KB + kb], total at
+//      kbidx[f][T*KB]; workgroup 0 also zeroes the alignment padding between
+//      regions so that every byte of the buffer is defined;
+//   2. scatter: one quad of lanes per block, in (t, kb, r) order; a block's
 //      position is kbidx[f][t*KB+kb] plus its rank among the column's rows of
 //      the same format (wave ballot).  Codes and scales are recomputed from W
 //      with the planner's exact arithmetic.  Stores are 16 bytes per lane.
-// A fourth tiny kernel zeroes the alignment padding between regions so that
-// every byte of the buffer is defined.
 #include "quant.h"
 
 namespace ht {
@@ -29,76 +28,164 @@ struct PackArgs {
     uint32_t counts[5];
 };
 
-__global__ __launch_bounds__(256) void pack_count_kernel(PackArgs a) {
-    const uint32_t c = blockIdx.x * 256u + threadIdx.x;   // column t*KB + kb
-    if (c >= a.T * a.KB) return;
-    const uint32_t t = fastdiv(c, a.div_kb);
-    const uint32_t kb = c - t * a.KB;
-    uint32_t cnt[5] = {0, 0, 0, 0, 0};
-    for (uint32_t r = 0; r < a.R; ++r) {
-        const uint32_t n = t * a.R + r;
-        if (n >= a.N) break;
-        const uint32_t f = a.fmt[uint64_t(n) * a.KB + kb];
-#pragma unroll
-        for (int g = 0; g < 5; ++g) cnt[g] += (f == uint32_t(g)) ? 1u : 0u;
-    }
-    uint32_t *kbidx = reinterpret_cast<uint32_t *>(a.buf + a.off_kbidx);
-#pragma unroll
-    for (int g = 0; g < 5; ++g) kbidx[uint64_t(g) * a.nk + c] = cnt[g];
+struct PadArgs {
+    uint64_t start[13];
+    uint32_t len[13];
+    int n;
+};
+
+// 0x01 in each byte of v that equals byte b (b replicated in bb = b * 0x01010101)
+__device__ __forceinline__ uint32_t eq_bytes(uint32_t v, uint32_t bb) {
+    const uint32_t x = v ^ bb;
+    return (~(((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x | 0x7F7F7F7Fu)) >> 7;
 }
 
-// In-place exclusive scan of kbidx[f][0 .. L) (L = T*KB), total into [L].
-// 1024 threads, 4 entries per thread per pass, a running carry across passes.
-__global__ __launch_bounds__(1024) void pack_scan_kernel(PackArgs a) {
+// Workgroup f: kbidx[f][c] = number of format-f blocks in columns before c
+// (column c = t*KB + kb, counted over the tile's rows), in chunks of 16384
+// columns, 16 consecutive columns per thread.  `rows16`: KB % 16 == 0 and the
+// map is 16-byte aligned, so a thread's 16 columns are one 16-byte piece of
+// each of the tile's rows of the map.
+__global__ __launch_bounds__(1024) void pack_index_kernel(PackArgs a, PadArgs pad, int rows16) {
     __shared__ uint32_t wsum[16];
-    __shared__ uint32_t carry_s;
+    __shared__ __align__(16) uint8_t cbytes[1024 * 16];
+    __shared__ __align__(16) uint32_t outv[1024 * 16];   // the chunk's results, stored coalesced
     const uint32_t f = blockIdx.x;
     uint32_t *v = reinterpret_cast<uint32_t *>(a.buf + a.off_kbidx) + uint64_t(f) * a.nk;
     const uint32_t L = a.T * a.KB;
     const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (threadIdx.x == 0) carry_s = 0;
-    __syncthreads();
-    for (uint32_t base = 0; base < L; base += 4096) {
-        const uint32_t i0 = base + threadIdx.x * 4;
-        uint32_t e[4];
+    const uint32_t fb = f * 0x01010101u;
+    uint32_t carry = 0;
+    for (uint32_t base = 0; base < L; base += 16384u) {
+        const uint32_t c0 = base + threadIdx.x * 16u;
+        // all 16 row loads are issued before any is used (rows past the tile
+        // or past N read a valid row and are masked), so a chunk costs one
+        // memory round trip, not one per row
+        uint32_t cnt[16];
+        if (rows16) {
+            uint32_t acc[4] = {0u, 0u, 0u, 0u};
+            const uint32_t cc = c0 < L ? c0 : 0u;
+            const uint32_t t = fastdiv(cc, a.div_kb), kb0 = cc - t * a.KB;
+            uint4 row[16];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) e[j] = (i0 + j < L) ? v[i0 + j] : 0u;
-        const uint32_t local = e[0] + e[1] + e[2] + e[3];
-        // inclusive scan of `local` across the wave
-        uint32_t inc = local;
+            for (uint32_t r = 0; r < 16; ++r) {
+                const uint32_t n = min(t * a.R + min(r, a.R - 1u), a.N - 1u);
+                row[r] = *reinterpret_cast<const uint4 *>(a.fmt + uint64_t(n) * a.KB + kb0);
+            }
+#pragma unroll
+            for (uint32_t r = 0; r < 16; ++r) {
+                if (c0 < L && r < a.R && t * a.R + r < a.N) {
+                    acc[0] += eq_bytes(row[r].x, fb);
+                    acc[1] += eq_bytes(row[r].y, fb);
+                    acc[2] += eq_bytes(row[r].z, fb);
+                    acc[3] += eq_bytes(row[r].w, fb);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 16; ++j) cnt[j] = (acc[j >> 2] >> (8 * (j & 3))) & 0xFFu;   // <= 16 per byte
+        } else {
+            // byte-wise: one column at a time (its 16 row loads in flight),
+            // counts kept as bytes in LDS
+#pragma unroll 1
+            for (uint32_t j = 0; j < 16; ++j) {
+                const uint32_t c = min(c0 + j, L - 1u);
+                const uint32_t t = fastdiv(c, a.div_kb), kb = c - t * a.KB;
+                uint32_t b[16];
+#pragma unroll
+                for (uint32_t r = 0; r < 16; ++r)
+                    b[r] = a.fmt[uint64_t(min(t * a.R + min(r, a.R - 1u), a.N - 1u)) * a.KB + kb];
+                uint32_t k = 0;
+#pragma unroll
+                for (uint32_t r = 0; r < 16; ++r)
+                    k += (c0 + j < L && r < a.R && t * a.R + r < a.N && b[r] == f) ? 1u : 0u;
+                cbytes[threadIdx.x * 16u + j] = uint8_t(k);
+            }
+            const uint4 cb = *reinterpret_cast<const uint4 *>(&cbytes[threadIdx.x * 16u]);   // own bytes only
+            const uint32_t cw[4] = {cb.x, cb.y, cb.z, cb.w};
+#pragma unroll
+            for (int j = 0; j < 16; ++j) cnt[j] = (cw[j >> 2] >> (8 * (j & 3))) & 0xFFu;
+        }
+        uint32_t tot = 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const uint32_t e = cnt[j];
+            cnt[j] = tot;   // exclusive within the thread
+            tot += e;
+        }
+        uint32_t inc = tot;   // inclusive scan across the wave
+#pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
-            uint32_t o = __shfl_up(inc, off);
+            const uint32_t o = __shfl_up(inc, off);
             if (lane >= uint32_t(off)) inc += o;
         }
         if (lane == 63) wsum[wave] = inc;
         __syncthreads();
-        uint32_t wprefix = 0;
-        for (uint32_t k = 0; k < wave; ++k) wprefix += wsum[k];
-        const uint32_t carry = carry_s;
-        uint32_t run = carry + wprefix + inc - local;
+        uint32_t wprefix = 0, all = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (i0 + j < L) v[i0 + j] = run;
-            run += e[j];
+        for (uint32_t k = 0; k < 16; ++k) {
+            const uint32_t ws = wsum[k];
+            wprefix += k < wave ? ws : 0u;
+            all += ws;
         }
+        const uint32_t run = carry + wprefix + inc - tot;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<uint4 *>(&outv[threadIdx.x * 16u + 4 * j]) =
+                make_uint4(run + cnt[4 * j], run + cnt[4 * j + 1], run + cnt[4 * j + 2], run + cnt[4 * j + 3]);
         __syncthreads();
-        if (threadIdx.x == 1023) carry_s = run;
-        __syncthreads();
+#pragma unroll
+        for (uint32_t k = 0; k < 16; ++k) {
+            const uint32_t i = threadIdx.x + 1024u * k;
+            if (base + i < L) v[base + i] = outv[i];
+        }
+        carry += all;
+        __syncthreads();   // wsum and outv are rewritten by the next chunk
     }
-    if (threadIdx.x == 0) v[L] = carry_s;
+    if (threadIdx.x == 0) v[L] = carry;
+    if (f == 0) {
+        for (int k = 0; k < pad.n; ++k)
+            for (uint32_t i = threadIdx.x; i < pad.len[k]; i += 1024u) a.buf[pad.start[k] + i] = 0;
+    }
 }
 
 __global__ __launch_bounds__(256) void pack_scatter_kernel(PackArgs a) {
+    __shared__ __align__(16) float stage[4][16 * 64];      // per wave: its 16 blocks
     const uint32_t tid = blockIdx.x * 256u + threadIdx.x;
     const uint32_t g = tid >> 2;                 // slot in (t, kb, r) order
     const int part = int(threadIdx.x & 3);
-    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const uint32_t col = g >> a.lgR;             // t*KB + kb
     const uint32_t r = g & (a.R - 1u);
     const uint32_t t = fastdiv(col, a.div_kb);
     const uint32_t kb = col - t * a.KB;
     const uint32_t n = t * a.R + r;
     const bool valid = col < a.T * a.KB && n < a.N;
+
+    // The wave's 16 blocks (each 256 contiguous bytes of W) as 4 loads of four
+    // whole blocks each (16-byte piece p = 64j + lane is piece p % 16 of the
+    // wave's block p / 16), through LDS to the compute layout (lane = 4 * block
+    // + part holds pieces 4*lane .. 4*lane + 3).  Missing blocks read W's
+    // first block and store nothing.
+    {
+        const uint32_t g0 = (blockIdx.x * 256u + wv * 64u) >> 2;
+        f32x4 pc[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t p = 64u * j + lane, gg = g0 + (p >> 4);
+            const uint32_t cc = gg >> a.lgR, rr = gg & (a.R - 1u);
+            const uint32_t tt = fastdiv(cc, a.div_kb), kk = cc - tt * a.KB, nn = tt * a.R + rr;
+            const bool ok = cc < a.T * a.KB && nn < a.N;
+            pc[j] = ld_stream_f4(a.W + (ok ? int64_t(nn) * a.ldw + kk * 64u : 0) + (p & 15u) * 4u);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<f32x4 *>(&stage[wv][(64u * j + lane) * 4u]) = pc[j];
+    }
+    __syncthreads();
+    float w[kPerLane];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(&stage[wv][(4u * lane + k) * 4u]);
+        w[4 * k] = v.x; w[4 * k + 1] = v.y; w[4 * k + 2] = v.z; w[4 * k + 3] = v.w;
+    }
     const uint32_t f = valid ? uint32_t(a.fmt[uint64_t(n) * a.KB + kb]) : 255u;
 
     // rank among the column's earlier rows with the same format
@@ -118,13 +205,6 @@ __global__ __launch_bounds__(256) void pack_scatter_kernel(PackArgs a) {
     const uint32_t pos = kbidx[uint64_t(f) * a.nk + col] + rank;
     if (pos >= a.counts[f]) return;                      // inconsistent counts: write nothing
 
-    float w[kPerLane];
-    const float *src = a.W + int64_t(n) * a.ldw + kb * 64u + part * 16;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const f32x4 v = ld_stream_f4(src + 4 * j);
-        w[4 * j] = v.x; w[4 * j + 1] = v.y; w[4 * j + 2] = v.z; w[4 * j + 3] = v.w;
-    }
     if (part == 0) {
         uint16_t id = uint16_t(kb * a.R + r);
         *reinterpret_cast<uint16_t *>(a.buf + a.off_ids[f] + 2ull * pos) = id;
@@ -188,17 +268,6 @@ __global__ __launch_bounds__(256) void pack_scatter_kernel(PackArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) dst[j] = make_float4(w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]);
     }
-}
-
-struct PadArgs {
-    uint8_t *buf;
-    uint64_t start[13];
-    uint32_t len[13];
-};
-
-__global__ __launch_bounds__(256) void pack_pad_kernel(PadArgs p) {
-    const int k = blockIdx.x;
-    for (uint32_t i = threadIdx.x; i < p.len[k]; i += 256) p.buf[p.start[k] + i] = 0;
 }
 
 }  // namespace ht
@@ -285,18 +354,11 @@ extern "C" ht_status ht_pack(const float *W, int64_t N, int64_t K, int64_t ldw, 
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const uint32_t cols = uint32_t(T * KB);
-    hipLaunchKernelGGL(pack_count_kernel, dim3((cols + 255) / 256), dim3(256), 0, s, a);
-    HT_LAUNCH_CHECK();
-    hipLaunchKernelGGL(pack_scan_kernel, dim3(5), dim3(1024), 0, s, a);
-    HT_LAUNCH_CHECK();
     const uint64_t slots = uint64_t(cols) * uint64_t(R);
     const uint64_t grid = (slots * 4 + 255) / 256;
     if (grid > 0xFFFFFFFFull || slots * 4 > 0xFFFFFFFFull) return HT_ESHAPE;
-    hipLaunchKernelGGL(pack_scatter_kernel, dim3(uint32_t(grid)), dim3(256), 0, s, a);
-    HT_LAUNCH_CHECK();
 
     PadArgs p;
-    p.buf = a.buf;
     const uint64_t starts[12] = {L.kbidx, L.ids[0], L.ids[1], L.ids[2], L.ids[3], L.ids[4],
                                  L.scale[0], L.scale[1], L.pay[0], L.pay[1], L.pay[2], L.pay[3]};
     // region k ends where region k+1 starts; the last (FP32 payload) ends at total
@@ -308,17 +370,18 @@ extern "C" ht_status ht_pack(const float *W, int64_t N, int64_t K, int64_t ldw, 
         p.len[k] = uint32_t(nexts[i] - p.start[k]);
         if (p.len[k]) ++k;
     }
-    // FP32 payload tail
-    uint64_t used_last = uint64_t(pay_bytes(4)) * uint64_t(counts5[4]);
+    const uint64_t used_last = uint64_t(pay_bytes(4)) * uint64_t(counts5[4]);   // FP32 payload tail
     if (L.total - (L.pay[4] + used_last)) {
         p.start[k] = L.pay[4] + used_last;
         p.len[k] = uint32_t(L.total - p.start[k]);
         ++k;
     }
-    if (k) {
-        hipLaunchKernelGGL(pack_pad_kernel, dim3(k), dim3(256), 0, s, p);
-        HT_LAUNCH_CHECK();
-    }
+    p.n = k;
+    const int rows16 = (KB % 16 == 0) && (reinterpret_cast<uintptr_t>(fmt_map) % 16 == 0);
+    hipLaunchKernelGGL(pack_index_kernel, dim3(5), dim3(1024), 0, s, a, p, rows16);
+    HT_LAUNCH_CHECK();
+    hipLaunchKernelGGL(pack_scatter_kernel, dim3(uint32_t(grid)), dim3(256), 0, s, a);
+    HT_LAUNCH_CHECK();
 
     desc->N = N;
     desc->K = K;

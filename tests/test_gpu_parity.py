@@ -179,6 +179,25 @@ def test_pack_edge_blocks_16bit(orc, force):
     np.testing.assert_array_equal(got, orc.pack(W, fmt, 8))
 
 
+@pytest.mark.parametrize("N,KB,R,offset", [
+    (1030, 272, 16, 0),   # 65 x 272 columns: two chunks of the index scan, 16-byte map rows, ragged tile
+    (1030, 277, 4, 0),    # KB not a multiple of 16: the byte-wise count, five chunks
+    (1030, 272, 16, 1),   # map at an address that is not 16-byte aligned: the byte-wise count
+])
+def test_pack_index_chunks(orc, N, KB, R, offset):
+    """The per-format counts and their scan over more than one chunk of
+    columns, on both counting paths; random formats so every format occurs."""
+    rng = np.random.default_rng(N + KB + R + offset)
+    W = (rng.normal(size=(N, 64 * KB)) * 0.05).astype(np.float32)
+    fmt = rng.integers(0, 5, size=(N, KB)).astype(np.uint8)
+    raw = torch.zeros(N * KB + 64, dtype=torch.uint8, device=dev())
+    fmt_d = raw[offset:offset + N * KB].view(N, KB)
+    fmt_d.copy_(gpu(fmt))
+    pw = api.pack(gpu(W), fmt_d, row_tile=R)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(pw.buf.cpu().numpy(), orc.pack(W, fmt, R))
+
+
 def test_pack_mlp_layer(orc):
     W = wl.mlp_weight(2, dim=4096)[:512]
     fmt = orc.plan(W)
