@@ -54,20 +54,26 @@ __device__ __forceinline__ void lane_codes(const float (&w)[kPerLane], float s, 
     const bool subnormal = s > 0.0f && s < FLT_MIN;
     const float rc = __builtin_amdgcn_rcpf(s);
     const float edge = Qf < 8.0f ? 0.5f - 3e-6f : 0.5f - 4e-5f;   // 0.5 - band
-    bool slow = subnormal;
+    // fast path: the largest distance to the rounded value decides, per
+    // lane, whether any entry lies within the band (maxNum ignores NaN
+    // entries, whose codes do not matter: such a block is never stored as an
+    // integer format)
+    float dev = 0.0f;
 #pragma unroll
     for (int i = 0; i < kPerLane; ++i) {
         const float t = w[i] * rc;
         const float r = rintf(t);
-        slow = slow || (normal && fabsf(t - r) > edge);
-        q[i] = normal ? r : 0.0f;                 // s = 0 or not finite: all codes 0
+        dev = fmaxf(dev, fabsf(t - r));
+        q[i] = r;
     }
-    if (__builtin_expect(__any(slow), 0)) {
+    const bool rare = !normal || subnormal || dev > edge;
+    if (__builtin_expect(__any(rare), 0)) {
 #pragma unroll
         for (int i = 0; i < kPerLane; ++i) {
             const float t = w[i] * rc;
             const bool exact = subnormal || (normal && fabsf(t - rintf(t)) > edge);
             if (exact) q[i] = fminf(fmaxf(rintf(w[i] / s), -Qf), Qf);
+            if (!normal && !subnormal) q[i] = 0.0f;   // s = 0 or not finite: all codes 0
         }
     }
 }
