@@ -163,7 +163,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
     if (valid && part == 0) a.fmt[b] = uint8_t(f);
 }
 
-// Per-format block counts of a format map: one 64-bit atomic per wave and
+// Per-format block counts of a format map: one 64-bit atomic per workgroup and
 // format (integer addition, so the result does not depend on the order).
 __global__ __launch_bounds__(256) void zero_counts_kernel(int64_t *counts) {
     if (threadIdx.x < 5) counts[threadIdx.x] = 0;
@@ -192,12 +192,19 @@ __global__ __launch_bounds__(256) void count_kernel(const uint8_t *fmt, uint64_t
             }
         }
     }
+    // wave sums, then one atomic per workgroup and format (the five counters
+    // share a cache line, so fewer atomics means less serialisation)
+    __shared__ uint32_t part[4][5];
 #pragma unroll
     for (int g = 0; g < 5; ++g) {
         uint32_t v = c[g];
         for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-        if ((threadIdx.x & 63) == 0 && v) atomicAdd(reinterpret_cast<unsigned long long *>(counts + g),
-                                                    (unsigned long long)v);
+        if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6][g] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < 5) {
+        const uint32_t v = part[0][threadIdx.x] + part[1][threadIdx.x] + part[2][threadIdx.x] + part[3][threadIdx.x];
+        if (v) atomicAdd(reinterpret_cast<unsigned long long *>(counts + threadIdx.x), (unsigned long long)v);
     }
 }
 
