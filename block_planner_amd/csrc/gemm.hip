@@ -13,14 +13,16 @@
 //   FP16 / FP32   two planes, hi = w with the low 16 bits cleared and
 //                 lo = bf16(w - hi) (exact for FP16; 16 significant bits for
 //                 FP32), scale 1; a non-finite entry gives a NaN column.
-// The partial of each step comes from bf16 MFMAs (v_mfma_f32_16x16x32_bf16)
-// with a fresh accumulator; the lo plane is multiplied only for 16-column
-// groups that hold an FP16 or FP32 block in that step.  Then every output
-// element adds scale[n] * partial[m, n] in fp32, in K order.
+// The hi plane's partial of each step comes from bf16 MFMAs
+// (v_mfma_f32_16x16x32_bf16) with a fresh accumulator, and every output
+// element adds scale[n] * partial[m, n] in fp32, in K order.  The lo plane
+// is multiplied only for 16-column groups that hold an FP16 or FP32 block in
+// that step, straight into the accumulators (float blocks have scale 1, and
+// integer columns hold zeros in the lo plane).
 //
-// Roles and pipeline: four waves run the MFMAs and copy the next step's x
-// tile straight from memory into LDS (global_load_lds); four waves load the
-// packed blocks two steps ahead into registers and dequantise the next
+// Roles and pipeline: four waves run the MFMAs and copy x tiles straight
+// from memory into LDS (global_load_lds) two steps ahead; four waves load
+// the packed blocks two steps ahead into registers and dequantise the next
 // step's into the other LDS stage.  One barrier per step.
 #include "gemv_common.h"
 #include "linear_host.h"
@@ -75,8 +77,9 @@ struct BlockLoad {
 // Waves 0-3 run the MFMAs (wave c: rows [16*MS*c, +16*MS), all 64 columns)
 // and copy the next step's x tile straight from memory into LDS; waves 4-7
 // load the packed blocks two steps ahead into registers and dequantise the
-// next step's.  Each SIMD holds one wave of each kind, so the matrix cores and
-// the vector ALUs work at the same time.  One workgroup barrier per step.
+// next step's.  A workgroup's waves are spread over the four SIMDs in turn,
+// so each SIMD normally runs one wave of each kind and its matrix core and
+// vector ALU can work at the same time.  One workgroup barrier per step.
 template <int MS>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
     constexpr uint32_t BM = 64 * MS;
