@@ -426,3 +426,29 @@ def test_full_size_layers_sampled(orc, cfg, name):
     # scale: the largest sampled oracle value (a lower bound of max|y|, so
     # the bound is at least as strict as the full-output one)
     assert np.max(np.abs(y.cpu().numpy()[mi, ni] - ys)) <= TOL * np.max(np.abs(ys)), (cfg, name, M)
+
+
+def test_decode_batch4_full_layer(orc):
+    """Llama-8B-shaped q projection (4096 x 4096) at batch 4 on the decode
+    path, every output against the oracle."""
+    shp = [s for s in wl.llama8b_shapes() if s.name == "q"][0]
+    W = wl.llama8b_weight(0, shp)
+    fmt = orc.plan(W)
+    pw = api.pack(gpu(W), gpu(fmt))
+    x = wl.to_bf16_bits(wl.activation("llama8b", 4, shp.k, seed=3))
+    y = api.linear(pw, bf16_gpu(x))
+    torch.cuda.synchronize()
+    check_close(y.cpu().numpy(), orc.linear(W, fmt, x), "llama8b.q M=4")
+
+
+@pytest.mark.parametrize("force", [INT4, INT8])
+def test_plan_pack_forced_full_layer(orc, force):
+    """The planner/packer sweep's reference points at full layer size: every
+    block forced to INT4 or INT8 on the 14336 x 4096 gate weight; the map and
+    the whole packed buffer byte for byte."""
+    shp = [s for s in wl.llama8b_shapes() if s.name == "gate"][0]
+    W = wl.llama8b_weight(0, shp)
+    fmt = gpu_plan(W, force_format=force)
+    np.testing.assert_array_equal(fmt, orc.plan(W, force=force))
+    got, _ = gpu_pack_bytes(W, fmt, 16)
+    np.testing.assert_array_equal(got, orc.pack(W, fmt, 16))
