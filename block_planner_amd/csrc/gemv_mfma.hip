@@ -1,0 +1,386 @@
+// gemv_mfma.hip -- the mixed-format linear for a few rows of x (decode at
+// batch 1 to 32 per launch) with the dot products on the matrix cores (HyperTensor 1.0.1
+// page: "fused mixed-precision operators" run the plan; "Key Features":
+// HyperLinear).  Same sums as the MFMA prefill path:
+//   y[m, n] = sum over K-blocks kb of  blk(m, n, kb),
+//   INT4 / INT8   blk = s * (sum_i q_i * x[m, 64kb+i]),
+//   BF16          blk = sum_i w_i * x[m, 64kb+i],
+//   FP16 / FP32   the same with w = hi + lo, two bfloat16 planes
+//                 (hi = w with the low 16 bits cleared, lo = bf16(w - hi)),
+// with bf16 MFMA products and fp32 accumulation.
+//
+// No LDS staging of weights: a wavefront takes one 16-row tile (row tile 16)
+// and a run of K-blocks; for each K-block ("column") lane (j, q) = (lane % 16,
+// lane / 16) dequantises entries [16q, 16q + 16) of the column's j-th block in
+// the packed order (format by format, rows ascending) straight into the B
+// operand of v_mfma_f32_16x16x32_bf16, and loads the matching 32 bytes of x
+// rows 16g + j as the A operand.  The K index inside an MFMA is a permutation
+// of the block's entries, the same for A and B, so the products are the
+// block's dot products.  The MFMA result's column j then belongs to the row
+// named by that block's id; a forward lane permute moves it (and the block's
+// scale) to the lane that owns the row before acc += scale * partial.
+//
+// A workgroup (16 wavefronts) owns one row tile and one K range: wavefront w
+// takes K-blocks [w*CW, w*CW + CW) of it, the workgroup adds the 16 partial
+// sums in wavefront order through LDS, and writes y (or, with several K
+// ranges, the split's partial sums, which a second kernel adds in split
+// order).  Each wavefront keeps the next column's loads in flight while it
+// multiplies the current one.
+#include "gemv_common.h"
+#include "linear_host.h"
+
+namespace ht {
+
+typedef __bf16 dbf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 dbf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr uint32_t kDecWaves = 16;
+constexpr uint32_t kDecThreads = 64 * kDecWaves;
+constexpr uint32_t kDecMaxCW = 15;   // K-blocks per wavefront (one 16-entry kbidx window)
+
+struct DecArgs {
+    LayerDev w;
+    const uint16_t *x;
+    int64_t ldx;
+    float *y;                 // fp32 output, or
+    uint16_t *ybf;            // bfloat16 output, or
+    float *partial;           // per-split partial sums [S][M][N] (no activation)
+    int64_t ldy;
+    uint32_t M;
+    uint32_t KBs;             // K-blocks per split
+    uint32_t CW;              // K-blocks per wavefront (<= kDecMaxCW)
+    int act;
+};
+
+// What one lane loads for one column: its quarter of the block in slot j.
+template <int MG>
+struct DecLoad {
+    uint4 p[4];               // payload: 16 (INT4, INT8), 32 (BF16, FP16) or 64 (FP32) bytes
+    uint4 xa[MG][2];          // x rows 16g + j, entries [16q, 16q + 16) of the K-block
+    uint32_t id2;             // the 4 bytes holding the block id
+    float sc;
+    uint32_t hi16;
+    int f;                    // format, or 5: no block in this slot
+};
+
+template <int MG>
+__global__ __launch_bounds__(kDecThreads) void gemv_mfma_kernel(DecArgs a) {
+    __shared__ float red[kDecWaves][MG * 4][64];
+    const LayerDev &w = a.w;
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t j = lane & 15, q = lane >> 4;
+    const uint32_t t = blockIdx.x;                         // row tile (16 rows)
+    const uint32_t kbs0 = blockIdx.y * a.KBs;
+    const uint32_t kbs1 = min(w.KB, kbs0 + a.KBs);
+    const uint32_t kb0 = min(kbs1, kbs0 + wave * a.CW);
+    const uint32_t nc = min(kbs1, kb0 + a.CW) - kb0;       // this wavefront's columns (may be 0)
+    const uint8_t *base = w.base;                          // offsets below are 32-bit (buffer < 4 GiB)
+
+    // kbidx[f][t*KB + kb0 + c] for c = 0..15: lane i holds format i / 16
+    // (formats 0-3) and, in kv4, format 4, at column i % 16
+    const uint32_t *kbt = reinterpret_cast<const uint32_t *>(base + w.off_kbidx) + t * w.KB;
+    const uint32_t ci = min(kb0 + j, w.KB);
+    const uint32_t kv = kbt[q * w.nk + ci];
+    const uint32_t kv4 = kbt[4u * w.nk + ci];
+
+    uint32_t opay[5], oids[5];
+#pragma unroll
+    for (int f = 0; f < 5; ++f) {
+        opay[f] = uint32_t(w.off_pay[f]);
+        oids[f] = uint32_t(w.off_ids[f]);
+    }
+    const uint32_t osc0 = uint32_t(w.off_scale[0]), osc1 = uint32_t(w.off_scale[1]);
+
+    // rows of x this lane feeds to the A operand (rows past M repeat row M-1;
+    // their outputs are never stored)
+    const uint16_t *xrow[MG];
+#pragma unroll
+    for (int g = 0; g < MG; ++g) xrow[g] = a.x + int64_t(min(16u * g + j, a.M - 1u)) * a.ldx + 16u * q;
+
+    auto kbidx_at = [&](uint32_t c, uint32_t (&v)[5]) {   // wave-uniform (c < 16)
+#pragma unroll
+        for (int f = 0; f < 4; ++f) v[f] = __builtin_amdgcn_readlane(kv, 16 * f + c);
+        v[4] = __builtin_amdgcn_readlane(kv4, c);
+    };
+
+    // Loads of column c: the lane's block is slot j of the column in the
+    // packed order; a missing block (slot past the tile's rows) reads the
+    // buffer's first bytes.
+    auto load_col = [&](uint32_t c) -> DecLoad<MG> {
+        DecLoad<MG> d;
+        uint32_t ka[5], kn[5];
+        kbidx_at(c, ka);
+        kbidx_at(c + 1, kn);
+        uint32_t cum = 0, blk = 0;
+        int f = 5;
+        uint32_t nlw = 1;                                  // 16-byte pieces some lane needs (uniform)
+#pragma unroll
+        for (int g = 0; g < 5; ++g) {
+            const uint32_t cnt = kn[g] - ka[g];
+            if (f == 5 && j - cum < cnt) {
+                f = g;
+                blk = ka[g] + (j - cum);
+            }
+            cum += cnt;
+            if (cnt) nlw = g == 4 ? 4u : (g >= 2 && nlw < 2u) ? 2u : nlw;
+        }
+        uint32_t po = 0, io = 0, so = 0, nl = 1;
+#pragma unroll
+        for (int g = 0; g < 5; ++g) {
+            if (f == g) {
+                po = opay[g] + blk * uint32_t(pay_bytes(g)) +
+                     (g == 0 ? 16u * (q >> 1) : g == 1 ? 16u * q : g == 4 ? 64u * q : 32u * q);
+                io = oids[g] + ((2u * blk) & ~3u);
+                so = g == 0 ? osc0 + 4u * blk : g == 1 ? osc1 + 4u * blk : 0u;
+                nl = g < 2 ? 1u : g == 4 ? 4u : 2u;
+            }
+        }
+        d.f = f;
+        d.hi16 = blk & 1u;
+        const u32x4 p0 = ld_stream_u4(base + po);
+        d.p[0] = make_uint4(p0.x, p0.y, p0.z, p0.w);
+        // further pieces only when some lane of the column needs them; a lane
+        // that needs fewer re-reads its first piece (same cache line)
+#pragma unroll
+        for (uint32_t i = 1; i < 4; ++i) {
+            d.p[i] = make_uint4(0u, 0u, 0u, 0u);
+            if (i < nlw) {
+                const u32x4 pi = ld_stream_u4(base + po + (i < nl ? 16u * i : 0u));
+                d.p[i] = make_uint4(pi.x, pi.y, pi.z, pi.w);
+            }
+        }
+        d.id2 = *reinterpret_cast<const uint32_t *>(base + io);
+        d.sc = *reinterpret_cast<const float *>(base + so);
+        const uint32_t koff = (kb0 + c) * 64u;
+#pragma unroll
+        for (int g = 0; g < MG; ++g) {
+            const uint4 *xp = reinterpret_cast<const uint4 *>(xrow[g] + koff);
+            d.xa[g][0] = xp[0];
+            d.xa[g][1] = xp[1];
+        }
+        return d;
+    };
+
+    f32x4 acc[MG];
+#pragma unroll
+    for (int g = 0; g < MG; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto pair_hi = [](float f0, float f1) {   // upper halves of two fp32 -> one word
+        return __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+    };
+    auto pair_lo = [](float f0, float f1) {   // bf16_rne(f - trunc(f)) of two fp32
+        const float r0 = f0 - __uint_as_float(__float_as_uint(f0) & 0xffff0000u);
+        const float r1 = f1 - __uint_as_float(__float_as_uint(f1) & 0xffff0000u);
+        const dbf16x2 v = {(__bf16)r0, (__bf16)r1};
+        return __builtin_bit_cast(uint32_t, v);
+    };
+
+    // Multiply one loaded column into acc.
+    auto compute = [&](const DecLoad<MG> &d) {
+        const uint32_t u[16] = {d.p[0].x, d.p[0].y, d.p[0].z, d.p[0].w, d.p[1].x, d.p[1].y, d.p[1].z, d.p[1].w,
+                                d.p[2].x, d.p[2].y, d.p[2].z, d.p[2].w, d.p[3].x, d.p[3].y, d.p[3].z, d.p[3].w};
+        uint32_t hp[8], lp[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) lp[i] = 0u;
+        switch (d.f) {
+        case 0: {
+            // entry i of the quarter = nibble (q & 1) of byte i of the 16 bytes
+            const uint32_t sh = 4u * (q & 1u);
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                const uint32_t wd = u[p >> 1] >> sh;
+                const uint32_t b = 16u * (p & 1);
+                hp[p] = pair_hi(float(int32_t(wd << (28u - b)) >> 28), float(int32_t(wd << (20u - b)) >> 28));
+            }
+            break;
+        }
+        case 1:
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                const uint32_t wd = u[p >> 1], b = 16u * (p & 1);
+                hp[p] = pair_hi(float(int8_t(wd >> b)), float(int8_t(wd >> (b + 8))));
+            }
+            break;
+        case 2:
+#pragma unroll
+            for (int p = 0; p < 8; ++p) hp[p] = u[p];
+            break;
+        case 3:
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                const float f0 = float(__builtin_bit_cast(_Float16, uint16_t(u[p])));
+                const float f1 = float(__builtin_bit_cast(_Float16, uint16_t(u[p] >> 16)));
+                hp[p] = pair_hi(f0, f1);
+                lp[p] = pair_lo(f0, f1);
+            }
+            break;
+        case 4:
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                const float f0 = __uint_as_float(u[2 * p]), f1 = __uint_as_float(u[2 * p + 1]);
+                hp[p] = pair_hi(f0, f1);
+                lp[p] = pair_lo(f0, f1);
+            }
+            break;
+        default:
+#pragma unroll
+            for (int p = 0; p < 8; ++p) hp[p] = 0u;
+            break;
+        }
+        const dbf16x8 bh0 = __builtin_bit_cast(dbf16x8, make_uint4(hp[0], hp[1], hp[2], hp[3]));
+        const dbf16x8 bh1 = __builtin_bit_cast(dbf16x8, make_uint4(hp[4], hp[5], hp[6], hp[7]));
+        const bool any_lo = __any(d.f == 3 || d.f == 4);
+        f32x4 cc[MG];
+#pragma unroll
+        for (int g = 0; g < MG; ++g) {
+            const dbf16x8 a0 = __builtin_bit_cast(dbf16x8, d.xa[g][0]);
+            const dbf16x8 a1 = __builtin_bit_cast(dbf16x8, d.xa[g][1]);
+            cc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bh0, (f32x4{0.f, 0.f, 0.f, 0.f}), 0, 0, 0);
+            cc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bh1, cc[g], 0, 0, 0);
+        }
+        if (any_lo) {
+            const dbf16x8 bl0 = __builtin_bit_cast(dbf16x8, make_uint4(lp[0], lp[1], lp[2], lp[3]));
+            const dbf16x8 bl1 = __builtin_bit_cast(dbf16x8, make_uint4(lp[4], lp[5], lp[6], lp[7]));
+#pragma unroll
+            for (int g = 0; g < MG; ++g) {
+                const dbf16x8 a0 = __builtin_bit_cast(dbf16x8, d.xa[g][0]);
+                const dbf16x8 a1 = __builtin_bit_cast(dbf16x8, d.xa[g][1]);
+                cc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bl0, cc[g], 0, 0, 0);
+                cc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bl1, cc[g], 0, 0, 0);
+            }
+        }
+        // column j of cc is the block of row (id & 15) (a missing block: row
+        // j, which then has no block either, so the map is a permutation of
+        // the 16 rows); move it and the scale to the lane of that row
+        const uint32_t id = d.hi16 ? d.id2 >> 16 : d.id2 & 0xFFFFu;
+        const uint32_t r = d.f < 5 ? (id & 15u) : j;
+        const float sc = d.f < 2 ? d.sc : d.f < 5 ? 1.0f : 0.0f;
+        const int dst = int(4u * (r + 16u * q));
+        const float scr = __int_as_float(__builtin_amdgcn_ds_permute(dst, __float_as_int(sc)));
+#pragma unroll
+        for (int g = 0; g < MG; ++g)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float v = __int_as_float(__builtin_amdgcn_ds_permute(dst, __float_as_int(cc[g][e])));
+                acc[g][e] = __builtin_fmaf(scr, v, acc[g][e]);
+            }
+    };
+
+    if (nc) {
+        DecLoad<MG> cur = load_col(0);
+        for (uint32_t c = 0; c < nc; ++c) {
+            // unconditional (the last column re-loads itself), so every path
+            // through the loop issues the same loads and each wait covers
+            // only the current column's
+            DecLoad<MG> nxt = load_col(c + 1 < nc ? c + 1 : c);
+            compute(cur);
+            cur = nxt;
+        }
+    }
+
+    // lane (r, q) holds rows m = 16g + 4q + e of output row t*16 + r
+#pragma unroll
+    for (int g = 0; g < MG; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[wave][g * 4 + e][lane] = acc[g][e];
+    __syncthreads();
+    const uint32_t o = threadIdx.x;
+    if (o < 256u * MG) {
+        const uint32_t m = o >> 4, r = o & 15u;
+        const uint32_t g = m >> 4, qq = (m >> 2) & 3u, e = m & 3u;
+        float v = 0.0f;
+#pragma unroll
+        for (uint32_t k = 0; k < kDecWaves; ++k) v += red[k][g * 4 + e][r + 16u * qq];
+        const uint32_t n = t * 16u + r;
+        if (m < a.M && n < w.N) {
+            if (a.partial) {
+                a.partial[(uint64_t(blockIdx.y) * a.M + m) * w.N + n] = v;
+            } else {
+                if (a.act == HT_ACT_RELU) v = v > 0.0f ? v : 0.0f;
+                if (a.ybf) a.ybf[int64_t(m) * a.ldy + n] = f32_to_bf16_rne(v);
+                else a.y[int64_t(m) * a.ldy + n] = v;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr uint32_t kDecMinGrid = 192;   // workgroups before K is split further
+constexpr int64_t kDecMaxM = 32;        // rows of x per launch (two MFMA row groups)
+
+struct DecShape {
+    uint32_t S, KBs, CW;
+};
+
+// K-splits: enough workgroups to cover the chip while every wavefront keeps
+// at least one K-block, and at most 15 K-blocks per wavefront.
+DecShape dec_shape(const ht_packed_weight *w) {
+    const uint32_t KB = uint32_t(w->K / kBlockK), T = uint32_t(w->n_tiles);
+    uint32_t S = (KB + kDecWaves * kDecMaxCW - 1) / (kDecWaves * kDecMaxCW);
+    while (uint64_t(T) * S < kDecMinGrid && KB / (S + 1) >= kDecWaves) ++S;
+    DecShape d;
+    d.KBs = (KB + S - 1) / S;
+    d.S = (KB + d.KBs - 1) / d.KBs;
+    d.CW = (d.KBs + kDecWaves - 1) / kDecWaves;
+    return d;
+}
+
+template <int MG>
+void launch_dec(const DecArgs &a, uint32_t T, uint32_t S, hipStream_t s) {
+    hipLaunchKernelGGL(gemv_mfma_kernel<MG>, dim3(T, S), dim3(kDecThreads), 0, s, a);
+}
+
+}  // namespace
+
+bool dec_ok(const ht_packed_weight *w) { return w->row_tile == 16; }
+
+size_t dec_ws(const ht_packed_weight *w, int64_t M) {
+    const int64_t Mt = M < kDecMaxM ? M : kDecMaxM;
+    const DecShape d = dec_shape(w);
+    return d.S > 1 ? size_t(d.S) * size_t(Mt) * size_t(w->N) * sizeof(float) : 0;
+}
+
+ht_status run_dec(const ht_packed_weight *w, const uint16_t *x, int64_t M, int64_t ldx, float *y, uint16_t *ybf,
+                  int64_t ldy, int act, void *ws, hipStream_t s) {
+    const DecShape d = dec_shape(w);
+    DecArgs a;
+    a.w = layer_dev(w);
+    a.ldx = ldx;
+    a.ldy = ldy;
+    a.act = act;
+    a.KBs = d.KBs;
+    a.CW = d.CW;
+    for (int64_t m0 = 0; m0 < M; m0 += kDecMaxM) {
+        const int64_t Mt = M - m0 < kDecMaxM ? M - m0 : kDecMaxM;
+        a.x = x + m0 * ldx;
+        a.M = uint32_t(Mt);
+        a.y = nullptr;
+        a.ybf = nullptr;
+        a.partial = nullptr;
+        float *yo = y ? y + m0 * ldy : nullptr;
+        uint16_t *yb = ybf ? ybf + m0 * ldy : nullptr;
+        if (d.S > 1) {
+            a.partial = static_cast<float *>(ws);
+        } else {
+            a.y = yo;
+            a.ybf = yb;
+        }
+        const uint32_t T = uint32_t(w->n_tiles);
+        if (Mt <= 16) launch_dec<1>(a, T, d.S, s);
+        else launch_dec<2>(a, T, d.S, s);
+        HT_LAUNCH_CHECK();
+        if (d.S > 1) {
+            const ht_status st = launch_split_reduce(static_cast<const float *>(ws), d.S, uint32_t(Mt), a.w.N, yo,
+                                                     yb, ldy, act, s);
+            if (st != HT_OK) return st;
+        }
+    }
+    return HT_OK;
+}
+
+}  // namespace ht

@@ -30,6 +30,14 @@ ht_status run_gemm(const ht_packed_weight *w, const uint16_t *x, int64_t M, int6
 ht_status launch_split_reduce(const float *partial, uint32_t S, uint32_t M, uint32_t N, float *y, uint16_t *ybf,
                               int64_t ldy, int act, hipStream_t s);
 
+// The register-dequantising MFMA path (row tile 16 only): whether it takes
+// this weight, its workspace bytes for M rows (K-split partials), and one
+// linear on it (fp32 y or bfloat16 ybf; arguments assumed checked).
+bool dec_ok(const ht_packed_weight *w);
+size_t dec_ws(const ht_packed_weight *w, int64_t M);
+ht_status run_dec(const ht_packed_weight *w, const uint16_t *x, int64_t M, int64_t ldx, float *y, uint16_t *ybf,
+                  int64_t ldy, int act, void *ws, hipStream_t s);
+
 // The path HT_PATH_AUTO resolves to for one linear over M rows.
 inline int32_t auto_linear_path(int64_t M) { return M >= 16 ? HT_PATH_GEMM : HT_PATH_GEMV; }
 

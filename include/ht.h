@@ -113,7 +113,8 @@ enum {
     HT_PATH_AUTO = 0,   /* let the library choose                                  */
     HT_PATH_GEMV = 1,   /* one fused GEMV launch per layer                          */
     HT_PATH_FUSED = 2,  /* ht_mlp_forward only: all layers in one persistent launch */
-    HT_PATH_GEMM = 3    /* ht_linear_forward only: LDS dequantisation + bf16 MFMA   */
+    HT_PATH_GEMM = 3,   /* ht_linear_forward only: LDS dequantisation + bf16 MFMA   */
+    HT_PATH_GEMV_MFMA = 4 /* ht_linear_forward only: register dequantisation + bf16 MFMA (row tile 16) */
 };
 
 /* Human-readable name of a status code (static storage; never NULL). */
@@ -164,7 +165,8 @@ ht_status ht_pack(const float *W, int64_t N, int64_t K, int64_t ldw,
                   void *buf, size_t buf_bytes, ht_packed_weight *desc, ht_stream stream);
 
 /* ht_linear_workspace -- workspace bytes ht_linear_forward needs for M rows
- * on `path` (HT_PATH_AUTO, HT_PATH_GEMV or HT_PATH_GEMM). */
+ * on `path` (HT_PATH_AUTO, HT_PATH_GEMV, HT_PATH_GEMM or HT_PATH_GEMV_MFMA;
+ * HT_EINVAL for HT_PATH_GEMV_MFMA with a row tile other than 16). */
 ht_status ht_linear_workspace(const ht_packed_weight *w, int64_t M, int32_t path,
                               size_t *bytes);
 
@@ -183,6 +185,10 @@ ht_status ht_linear_workspace(const ht_packed_weight *w, int64_t M, int32_t path
  *          codes exactly; FP16 and FP32 entries as a hi + lo pair, exact for
  *          FP16 and to 16 significant bits for FP32) and multiplied with
  *          bf16 MFMA, fp32 accumulation (for prefill, many rows);
+ *          HT_PATH_GEMV_MFMA: for decode at a few to a few tens of rows
+ *          (row tile 16 only, else HT_EINVAL): each block is dequantised
+ *          in registers straight into the operands of bf16 MFMAs (the same
+ *          bfloat16 planes as HT_PATH_GEMM), 32 rows of x per launch;
  *          HT_PATH_AUTO: GEMM when M >= 16, else GEMV.
  *   ws     workspace of ws_bytes >= ht_linear_workspace(w, M, path): K-split
  *          partial sums, added in split order by a second kernel. */
