@@ -10,22 +10,23 @@
 // with bf16 MFMA products and fp32 accumulation.
 //
 // No LDS staging of weights: a wavefront takes one 16-row tile (row tile 16)
-// and a run of K-blocks; for each K-block ("column") lane (j, q) = (lane % 16,
-// lane / 16) dequantises entries [16q, 16q + 16) of the column's j-th block in
-// the packed order (format by format, rows ascending) straight into the B
-// operand of v_mfma_f32_16x16x32_bf16, and loads the matching 32 bytes of x
-// rows 16g + j as the A operand.  The K index inside an MFMA is a permutation
-// of the block's entries, the same for A and B, so the products are the
-// block's dot products.  The MFMA result's column j then belongs to the row
-// named by that block's id; a forward lane permute moves it (and the block's
-// scale) to the lane that owns the row before acc += scale * partial.
+// and a few K-blocks at a time; for each K-block ("column") lane (j, q) =
+// (lane % 16, lane / 16) dequantises entries [16q, 16q + 16) of the column's
+// j-th block in the packed order (format by format, rows ascending) straight
+// into the B operand of v_mfma_f32_16x16x32_bf16; the A operand is x rows
+// 16g + j at the same entries, from LDS.  The K index inside an MFMA is a
+// permutation of the block's entries, the same for A and B, so the products
+// are the block's dot products.  The MFMA result's column j then belongs to
+// the row named by that block's id; a forward lane permute moves it (and the
+// block's scale) to the lane that owns the row before acc += scale * partial.
 //
-// A workgroup (16 wavefronts) owns one row tile and one K range: wavefront w
-// takes K-blocks [w*CW, w*CW + CW) of it, the workgroup adds the 16 partial
-// sums in wavefront order through LDS, and writes y (or, with several K
-// ranges, the split's partial sums, which a second kernel adds in split
-// order).  Each wavefront keeps the next column's loads in flight while it
-// multiplies the current one.
+// A workgroup (16 wavefronts) owns one row tile and one K range, walked in
+// rounds of 64 / MG K-blocks: the round's x rows are staged in LDS while
+// every wavefront has the loads of all of its columns of the round (four, or
+// two at MG = 2) in flight, so a round costs about one memory round trip.
+// The workgroup then adds the 16 wavefronts' sums in wavefront order through
+// LDS and writes y (or, with several K ranges, the range's partial sums,
+// which a second kernel adds in range order).
 #include "gemv_common.h"
 #include "linear_host.h"
 
@@ -36,7 +37,6 @@ typedef __bf16 dbf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr uint32_t kDecWaves = 16;
 constexpr uint32_t kDecThreads = 64 * kDecWaves;
-constexpr uint32_t kDecMaxCW = 15;   // K-blocks per wavefront (one 16-entry kbidx window)
 
 struct DecArgs {
     LayerDev w;
@@ -48,24 +48,31 @@ struct DecArgs {
     int64_t ldy;
     uint32_t M;
     uint32_t KBs;             // K-blocks per split
-    uint32_t CW;              // K-blocks per wavefront (<= kDecMaxCW)
     int act;
 };
 
 // What one lane loads for one column: its quarter of the block in slot j.
-template <int MG>
 struct DecLoad {
     uint4 p[4];               // payload: 16 (INT4, INT8), 32 (BF16, FP16) or 64 (FP32) bytes
-    uint4 xa[MG][2];          // x rows 16g + j, entries [16q, 16q + 16) of the K-block
     uint32_t id2;             // the 4 bytes holding the block id
     float sc;
     uint32_t hi16;
     int f;                    // format, or 5: no block in this slot
 };
 
+// x staging: a chunk of kDecChunk / MG K-blocks of x rows [0, 16 MG) per
+// round, row stride padded by 16 bytes so that the 16 rows an MFMA operand
+// read touches fall in distinct banks.
+constexpr uint32_t kDecChunk = 64;                    // K-blocks per round at MG = 1
+template <int MG> constexpr uint32_t dec_row() { return (kDecChunk / MG) * 64u + 8u; }   // bfloat16 entries
+
 template <int MG>
 __global__ __launch_bounds__(kDecThreads) void gemv_mfma_kernel(DecArgs a) {
-    __shared__ float red[kDecWaves][MG * 4][64];
+    constexpr uint32_t CK = kDecChunk / MG;           // K-blocks per round
+    constexpr uint32_t CW = CK / kDecWaves;           // K-blocks per wavefront per round (4 or 2)
+    constexpr uint32_t XR = dec_row<MG>();
+    __shared__ __align__(16) uint16_t xs[16 * MG * XR];
+    float *red = reinterpret_cast<float *>(xs);       // [wave][MG * 4][64] after the last round
     const LayerDev &w = a.w;
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -73,16 +80,8 @@ __global__ __launch_bounds__(kDecThreads) void gemv_mfma_kernel(DecArgs a) {
     const uint32_t t = blockIdx.x;                         // row tile (16 rows)
     const uint32_t kbs0 = blockIdx.y * a.KBs;
     const uint32_t kbs1 = min(w.KB, kbs0 + a.KBs);
-    const uint32_t kb0 = min(kbs1, kbs0 + wave * a.CW);
-    const uint32_t nc = min(kbs1, kb0 + a.CW) - kb0;       // this wavefront's columns (may be 0)
     const uint8_t *base = w.base;                          // offsets below are 32-bit (buffer < 4 GiB)
-
-    // kbidx[f][t*KB + kb0 + c] for c = 0..15: lane i holds format i / 16
-    // (formats 0-3) and, in kv4, format 4, at column i % 16
     const uint32_t *kbt = reinterpret_cast<const uint32_t *>(base + w.off_kbidx) + t * w.KB;
-    const uint32_t ci = min(kb0 + j, w.KB);
-    const uint32_t kv = kbt[q * w.nk + ci];
-    const uint32_t kv4 = kbt[4u * w.nk + ci];
 
     uint32_t opay[5], oids[5];
 #pragma unroll
@@ -92,26 +91,28 @@ __global__ __launch_bounds__(kDecThreads) void gemv_mfma_kernel(DecArgs a) {
     }
     const uint32_t osc0 = uint32_t(w.off_scale[0]), osc1 = uint32_t(w.off_scale[1]);
 
-    // rows of x this lane feeds to the A operand (rows past M repeat row M-1;
-    // their outputs are never stored)
-    const uint16_t *xrow[MG];
-#pragma unroll
-    for (int g = 0; g < MG; ++g) xrow[g] = a.x + int64_t(min(16u * g + j, a.M - 1u)) * a.ldx + 16u * q;
-
-    auto kbidx_at = [&](uint32_t c, uint32_t (&v)[5]) {   // wave-uniform (c < 16)
+    // kbidx[f][t*KB + kb0 + c] for c = 0..15 of the wavefront's columns in a
+    // round starting at kc: lane i holds format i / 16 (formats 0-3) and, in
+    // kv4, format 4, at column i % 16
+    auto kbidx_window = [&](uint32_t kc, uint32_t &v, uint32_t &v4) {
+        const uint32_t ci = min(kc + wave * CW + j, w.KB);
+        v = kbt[q * w.nk + ci];
+        v4 = kbt[4u * w.nk + ci];
+    };
+    auto kbidx_at = [&](uint32_t kv, uint32_t kv4, uint32_t c, uint32_t (&v)[5]) {   // wave-uniform
 #pragma unroll
         for (int f = 0; f < 4; ++f) v[f] = __builtin_amdgcn_readlane(kv, 16 * f + c);
         v[4] = __builtin_amdgcn_readlane(kv4, c);
     };
 
-    // Loads of column c: the lane's block is slot j of the column in the
-    // packed order; a missing block (slot past the tile's rows) reads the
-    // buffer's first bytes.
-    auto load_col = [&](uint32_t c) -> DecLoad<MG> {
-        DecLoad<MG> d;
+    // Loads of column c of the window: the lane's block is slot j of the
+    // column in the packed order; a missing block (slot past the tile's rows,
+    // or a column past the range) reads the buffer's first bytes.
+    auto load_col = [&](uint32_t kv, uint32_t kv4, uint32_t c) -> DecLoad {
+        DecLoad d;
         uint32_t ka[5], kn[5];
-        kbidx_at(c, ka);
-        kbidx_at(c + 1, kn);
+        kbidx_at(kv, kv4, c, ka);
+        kbidx_at(kv, kv4, c + 1, kn);
         uint32_t cum = 0, blk = 0;
         int f = 5;
         uint32_t nlw = 1;                                  // 16-byte pieces some lane needs (uniform)
@@ -152,13 +153,6 @@ __global__ __launch_bounds__(kDecThreads) void gemv_mfma_kernel(DecArgs a) {
         }
         d.id2 = *reinterpret_cast<const uint32_t *>(base + io);
         d.sc = *reinterpret_cast<const float *>(base + so);
-        const uint32_t koff = (kb0 + c) * 64u;
-#pragma unroll
-        for (int g = 0; g < MG; ++g) {
-            const uint4 *xp = reinterpret_cast<const uint4 *>(xrow[g] + koff);
-            d.xa[g][0] = xp[0];
-            d.xa[g][1] = xp[1];
-        }
         return d;
     };
 
@@ -176,8 +170,8 @@ __global__ __launch_bounds__(kDecThreads) void gemv_mfma_kernel(DecArgs a) {
         return __builtin_bit_cast(uint32_t, v);
     };
 
-    // Multiply one loaded column into acc.
-    auto compute = [&](const DecLoad<MG> &d) {
+    // Multiply one loaded column (K-block kl of the round) into acc.
+    auto compute = [&](const DecLoad &d, uint32_t kl) {
         const uint32_t u[16] = {d.p[0].x, d.p[0].y, d.p[0].z, d.p[0].w, d.p[1].x, d.p[1].y, d.p[1].z, d.p[1].w,
                                 d.p[2].x, d.p[2].y, d.p[2].z, d.p[2].w, d.p[3].x, d.p[3].y, d.p[3].z, d.p[3].w};
         uint32_t hp[8], lp[8];
@@ -230,60 +224,89 @@ __global__ __launch_bounds__(kDecThreads) void gemv_mfma_kernel(DecArgs a) {
         }
         const dbf16x8 bh0 = __builtin_bit_cast(dbf16x8, make_uint4(hp[0], hp[1], hp[2], hp[3]));
         const dbf16x8 bh1 = __builtin_bit_cast(dbf16x8, make_uint4(hp[4], hp[5], hp[6], hp[7]));
+        const dbf16x8 bl0 = __builtin_bit_cast(dbf16x8, make_uint4(lp[0], lp[1], lp[2], lp[3]));
+        const dbf16x8 bl1 = __builtin_bit_cast(dbf16x8, make_uint4(lp[4], lp[5], lp[6], lp[7]));
         const bool any_lo = __any(d.f == 3 || d.f == 4);
-        f32x4 cc[MG];
-#pragma unroll
-        for (int g = 0; g < MG; ++g) {
-            const dbf16x8 a0 = __builtin_bit_cast(dbf16x8, d.xa[g][0]);
-            const dbf16x8 a1 = __builtin_bit_cast(dbf16x8, d.xa[g][1]);
-            cc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bh0, (f32x4{0.f, 0.f, 0.f, 0.f}), 0, 0, 0);
-            cc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bh1, cc[g], 0, 0, 0);
-        }
-        if (any_lo) {
-            const dbf16x8 bl0 = __builtin_bit_cast(dbf16x8, make_uint4(lp[0], lp[1], lp[2], lp[3]));
-            const dbf16x8 bl1 = __builtin_bit_cast(dbf16x8, make_uint4(lp[4], lp[5], lp[6], lp[7]));
-#pragma unroll
-            for (int g = 0; g < MG; ++g) {
-                const dbf16x8 a0 = __builtin_bit_cast(dbf16x8, d.xa[g][0]);
-                const dbf16x8 a1 = __builtin_bit_cast(dbf16x8, d.xa[g][1]);
-                cc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bl0, cc[g], 0, 0, 0);
-                cc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bl1, cc[g], 0, 0, 0);
-            }
-        }
-        // column j of cc is the block of row (id & 15) (a missing block: row
-        // j, which then has no block either, so the map is a permutation of
-        // the 16 rows); move it and the scale to the lane of that row
+        // column j of the product is the block of row (id & 15) (a missing
+        // block: row j, which then has no block either, so the map is a
+        // permutation of the 16 rows); it moves, with the scale, to the lane
+        // of that row
         const uint32_t id = d.hi16 ? d.id2 >> 16 : d.id2 & 0xFFFFu;
         const uint32_t r = d.f < 5 ? (id & 15u) : j;
         const float sc = d.f < 2 ? d.sc : d.f < 5 ? 1.0f : 0.0f;
         const int dst = int(4u * (r + 16u * q));
         const float scr = __int_as_float(__builtin_amdgcn_ds_permute(dst, __float_as_int(sc)));
 #pragma unroll
-        for (int g = 0; g < MG; ++g)
+        for (int g = 0; g < MG; ++g) {
+            // A operand: x row 16g + j, entries [16q, 16q + 16) of the K-block
+            const uint16_t *xp = xs + (16u * g + j) * XR + kl * 64u + 16u * q;
+            const dbf16x8 a0 = *reinterpret_cast<const dbf16x8 *>(xp);
+            const dbf16x8 a1 = *reinterpret_cast<const dbf16x8 *>(xp + 8);
+            f32x4 cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bh0, (f32x4{0.f, 0.f, 0.f, 0.f}), 0, 0, 0);
+            cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bh1, cc, 0, 0, 0);
+            if (any_lo) {
+                cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bl0, cc, 0, 0, 0);
+                cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bl1, cc, 0, 0, 0);
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float v = __int_as_float(__builtin_amdgcn_ds_permute(dst, __float_as_int(cc[g][e])));
+                const float v = __int_as_float(__builtin_amdgcn_ds_permute(dst, __float_as_int(cc[e])));
                 acc[g][e] = __builtin_fmaf(scr, v, acc[g][e]);
             }
+        }
     };
 
-    if (nc) {
-        DecLoad<MG> cur = load_col(0);
-        for (uint32_t c = 0; c < nc; ++c) {
-            // unconditional (the last column re-loads itself), so every path
-            // through the loop issues the same loads and each wait covers
-            // only the current column's
-            DecLoad<MG> nxt = load_col(c + 1 < nc ? c + 1 : c);
-            compute(cur);
-            cur = nxt;
+    // Rounds of CK K-blocks.  The round's x rows [0, 16 MG) are copied
+    // straight from memory into LDS (global_load_lds, issued as inline
+    // assembly with M0 = the LDS destination of a wavefront's 1 KiB piece;
+    // rows past M repeat row M - 1 and entries past the range repeat its last
+    // piece, so no copy is masked): the first round's before the first
+    // K-block index window is loaded, so the two trips overlap, each later
+    // round's right after the previous round's MFMAs.  In a round each
+    // wavefront issues the loads of all CW of its columns, then one wait for
+    // everything, one barrier, the MFMAs, and a barrier before the next
+    // round's copies overwrite x.
+    constexpr uint32_t PPR = CK / 8;                      // 1 KiB pieces per x row
+    auto stage_x = [&](uint32_t kc) {                     // 16 MG * PPR = 128 pieces, 8 per wavefront
+        const uint32_t nkc = min(CK, kbs1 - kc);
+#pragma unroll
+        for (uint32_t i = 0; i < 8; ++i) {
+            const uint32_t P = wave + kDecWaves * i;
+            const uint32_t row = P / PPR, pc = P % PPR;
+            const uint32_t cu = min(pc * 64u + lane, 8u * nkc - 1u);
+            const uint16_t *src = a.x + int64_t(min(row, a.M - 1u)) * a.ldx + kc * 64u + 8u * cu;
+            const uint32_t dst =
+                uint32_t(uintptr_t((__attribute__((address_space(3))) uint16_t *)(xs + row * XR + pc * 512u)));
+            asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                         :
+                         : "v"(src), "s"(dst)
+                         : "memory", "m0");
         }
+    };
+    uint32_t kv, kv4;
+    stage_x(kbs0);                                        // in flight together with the first window
+    kbidx_window(kbs0, kv, kv4);
+    for (uint32_t kc = kbs0; kc < kbs1; kc += CK) {
+        const uint32_t nkc = min(CK, kbs1 - kc);
+        DecLoad d[CW];
+#pragma unroll
+        for (uint32_t c = 0; c < CW; ++c) d[c] = load_col(kv, kv4, c);
+        const uint32_t nc = min(nkc, wave * CW + CW) - min(nkc, wave * CW);   // columns of this wavefront
+        kbidx_window(kc + CK, kv, kv4);                   // next round's window (clamped past the end)
+        __builtin_amdgcn_s_waitcnt(0x0F70);               // vmcnt(0): this wavefront's x pieces are in LDS
+        __syncthreads();
+#pragma unroll
+        for (uint32_t c = 0; c < CW; ++c)
+            if (c < nc) compute(d[c], wave * CW + c);
+        __syncthreads();
+        if (kc + CK < kbs1) stage_x(kc + CK);
     }
 
     // lane (r, q) holds rows m = 16g + 4q + e of output row t*16 + r
 #pragma unroll
     for (int g = 0; g < MG; ++g)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) red[wave][g * 4 + e][lane] = acc[g][e];
+        for (int e = 0; e < 4; ++e) red[(wave * (MG * 4) + g * 4 + e) * 64 + lane] = acc[g][e];
     __syncthreads();
     const uint32_t o = threadIdx.x;
     if (o < 256u * MG) {
@@ -291,7 +314,7 @@ __global__ __launch_bounds__(kDecThreads) void gemv_mfma_kernel(DecArgs a) {
         const uint32_t g = m >> 4, qq = (m >> 2) & 3u, e = m & 3u;
         float v = 0.0f;
 #pragma unroll
-        for (uint32_t k = 0; k < kDecWaves; ++k) v += red[k][g * 4 + e][r + 16u * qq];
+        for (uint32_t k = 0; k < kDecWaves; ++k) v += red[(k * (MG * 4) + g * 4 + e) * 64 + r + 16u * qq];
         const uint32_t n = t * 16u + r;
         if (m < a.M && n < w.N) {
             if (a.partial) {
@@ -314,19 +337,18 @@ constexpr uint32_t kDecMinGrid = 192;   // workgroups before K is split further
 constexpr int64_t kDecMaxM = 32;        // rows of x per launch (two MFMA row groups)
 
 struct DecShape {
-    uint32_t S, KBs, CW;
+    uint32_t S, KBs;
 };
 
-// K-splits: enough workgroups to cover the chip while every wavefront keeps
-// at least one K-block, and at most 15 K-blocks per wavefront.
+// K-splits only to cover the chip when there are few row tiles (at least 16
+// K-blocks per split, every split non-empty).
 DecShape dec_shape(const ht_packed_weight *w) {
     const uint32_t KB = uint32_t(w->K / kBlockK), T = uint32_t(w->n_tiles);
-    uint32_t S = (KB + kDecWaves * kDecMaxCW - 1) / (kDecWaves * kDecMaxCW);
+    uint32_t S = 1;
     while (uint64_t(T) * S < kDecMinGrid && KB / (S + 1) >= kDecWaves) ++S;
     DecShape d;
     d.KBs = (KB + S - 1) / S;
     d.S = (KB + d.KBs - 1) / d.KBs;
-    d.CW = (d.KBs + kDecWaves - 1) / kDecWaves;
     return d;
 }
 
@@ -354,7 +376,6 @@ ht_status run_dec(const ht_packed_weight *w, const uint16_t *x, int64_t M, int64
     a.ldy = ldy;
     a.act = act;
     a.KBs = d.KBs;
-    a.CW = d.CW;
     for (int64_t m0 = 0; m0 < M; m0 += kDecMaxM) {
         const int64_t Mt = M - m0 < kDecMaxM ? M - m0 : kDecMaxM;
         a.x = x + m0 * ldx;

@@ -251,7 +251,7 @@ extern "C" ht_status ht_linear_workspace(const ht_packed_weight *w, int64_t M, i
     if (!bytes || !desc_ok(w)) return HT_EINVAL;
     if (M <= 0) return HT_ESHAPE;
     if (!path_ok(path)) return HT_EINVAL;
-    if (path == HT_PATH_AUTO) path = auto_linear_path(M);
+    if (path == HT_PATH_AUTO) path = auto_linear_path(w, M);
     if (path == HT_PATH_GEMV_MFMA && !dec_ok(w)) return HT_EINVAL;
     *bytes = path_ws(w, M, path);
     return HT_OK;
@@ -265,7 +265,7 @@ extern "C" ht_status ht_linear_forward(const ht_packed_weight *w, const uint16_t
     if (!path_ok(path)) return HT_EINVAL;
     if (M <= 0 || ldx < w->K || ldy < w->N) return HT_ESHAPE;
     if (!al16(x) || !al16(y) || (ldx % 8) || !al16(w->base)) return HT_EALIGN;
-    if (path == HT_PATH_AUTO) path = auto_linear_path(M);
+    if (path == HT_PATH_AUTO) path = auto_linear_path(w, M);
     if (path == HT_PATH_GEMV_MFMA && !dec_ok(w)) return HT_EINVAL;
     const size_t need = path_ws(w, M, path);
     if (need && (!ws || ws_bytes < need)) return HT_ESMALL;

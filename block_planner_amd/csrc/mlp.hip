@@ -333,9 +333,10 @@ ht_status mlp_plan(const ht_packed_weight *const *layers, int32_t L, int64_t M, 
         const ht_packed_weight *w = layers[l];
         if (!desc_ok(w)) return HT_EINVAL;
         if (l && w->K != layers[l - 1]->N) return HT_ESHAPE;
-        const size_t p = linear_ws(w, M), q = gemm_ws(w, M);
+        const size_t p = linear_ws(w, M), q = gemm_ws(w, M), r = dec_ok(w) ? dec_ws(w, M) : 0;
         pl->part = p > pl->part ? p : pl->part;
         pl->part = q > pl->part ? q : pl->part;
+        pl->part = r > pl->part ? r : pl->part;
         const size_t h = align256(size_t(M) * size_t(w->N) * 2u);
         pl->act = h > pl->act ? h : pl->act;
         if (l + 1 < L) pl->words += align256(size_t(M) * size_t(w->N) * 2u);
@@ -461,9 +462,8 @@ extern "C" ht_status ht_mlp_forward(const ht_packed_weight *const *layers, int32
     const uint16_t *in = x;
     int64_t ld_in = ldx;
     size_t dump_off = 0;
-    // HT_PATH_GEMV: register-path GEMV per layer; HT_PATH_AUTO: the MFMA path
-    // from 16 rows of x on, as for a single linear
-    const bool mfma = path != HT_PATH_GEMV && auto_linear_path(M) == HT_PATH_GEMM;
+    // HT_PATH_GEMV: register-path GEMV per layer; HT_PATH_AUTO: each layer on
+    // the path a single linear of M rows takes
     for (int32_t l = 0; l < n_layers; ++l) {
         const ht_packed_weight *w = layers[l];
         float *yo = nullptr;
@@ -476,8 +476,10 @@ extern "C" ht_status ht_mlp_forward(const ht_packed_weight *const *layers, int32
         } else {
             yo = y;
         }
-        st = mfma ? run_gemm(w, in, M, ld_in, yo, out, ldo, HT_ACT_RELU, part, s)
-                  : run_linear(w, in, M, ld_in, yo, out, ldo, HT_ACT_RELU, part, s);
+        const int32_t lp = path == HT_PATH_GEMV ? HT_PATH_GEMV : auto_linear_path(w, M);
+        st = lp == HT_PATH_GEMM        ? run_gemm(w, in, M, ld_in, yo, out, ldo, HT_ACT_RELU, part, s)
+             : lp == HT_PATH_GEMV_MFMA ? run_dec(w, in, M, ld_in, yo, out, ldo, HT_ACT_RELU, part, s)
+                                       : run_linear(w, in, M, ld_in, yo, out, ldo, HT_ACT_RELU, part, s);
         if (st != HT_OK) return st;
         in = out;
         ld_in = w->N;

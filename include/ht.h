@@ -189,7 +189,8 @@ ht_status ht_linear_workspace(const ht_packed_weight *w, int64_t M, int32_t path
  *          (row tile 16 only, else HT_EINVAL): each block is dequantised
  *          in registers straight into the operands of bf16 MFMAs (the same
  *          bfloat16 planes as HT_PATH_GEMM), 32 rows of x per launch;
- *          HT_PATH_AUTO: GEMM when M >= 16, else GEMV.
+ *          HT_PATH_AUTO: GEMV_MFMA for 5 <= M <= 32 with row tile 16;
+ *          otherwise GEMM when M >= 16, else GEMV.
  *   ws     workspace of ws_bytes >= ht_linear_workspace(w, M, path): K-split
  *          partial sums, added in split order by a second kernel. */
 ht_status ht_linear_forward(const ht_packed_weight *w, const uint16_t *x, int64_t M,
@@ -221,8 +222,8 @@ ht_status ht_workspace_init(void *ws, size_t ws_bytes, ht_stream stream);
  *   path      HT_PATH_AUTO: one persistent launch for all layers when it fits
  *             (n_layers <= 8, M <= 4, row tile >= 4, x, partial sums and row
  *             buffer within the 160 KiB LDS of a compute unit, and every
- *             workgroup resident at once), else one launch per layer, on the
- *             MFMA path (as HT_PATH_GEMM of ht_linear_forward) from M >= 16;
+ *             workgroup resident at once), else one launch per layer, each
+ *             on the path HT_PATH_AUTO of ht_linear_forward takes for it;
  *             HT_PATH_GEMV: one register-path GEMV launch per layer;
  *             HT_PATH_FUSED: the single launch or HT_EINVAL if it does not fit.
  *   ws        workspace of ws_bytes >= ht_mlp_workspace(...), initialised with

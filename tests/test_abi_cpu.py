@@ -125,9 +125,20 @@ def test_linear_argument_checks():
     assert f(ctypes.byref(big), x, 1, 64 * 1024, y, 256, 0, 0, None, 0, None) == 4
     # the MFMA path splits K when it has few output tiles: [S][M][N] fp32
     # partials with 2 <= S <= K/64/4 (at least 4 K-blocks per split)
-    for M, path in ((1, B.HT_PATH_GEMM), (16, B.HT_PATH_AUTO)):                 # AUTO: MFMA from 16 rows
+    for M, path in ((1, B.HT_PATH_GEMM), (16, B.HT_PATH_AUTO), (20, B.HT_PATH_GEMV_MFMA)):
         ws = B.ht_linear_workspace(big, M, path)
         assert ws % (M * 256 * 4) == 0 and 2 <= ws // (M * 256 * 4) <= 1024 // 4
+    # the MFMA decode path: 32 rows per launch (partials sized for 32 at
+    # most), no split with enough row tiles, row tile 16 only
+    assert B.ht_linear_workspace(big, 64, B.HT_PATH_GEMV_MFMA) == B.ht_linear_workspace(big, 32, B.HT_PATH_GEMV_MFMA)
+    assert B.ht_linear_workspace(_desc(N=4096, K=4096, R=16), 32, B.HT_PATH_GEMV_MFMA) == 0
+    for R in (1, 2, 4, 8):
+        with pytest.raises(B.HTError):
+            B.ht_linear_workspace(_desc(N=256, K=4096, R=R), 8, B.HT_PATH_GEMV_MFMA)
+        assert f(ctypes.byref(_desc(R=R)), x, 8, 256, y, 256, 0, B.HT_PATH_GEMV_MFMA, None, 0, None) == 1
+    # AUTO on a row tile other than 16 keeps to the other two paths
+    assert B.ht_linear_workspace(_desc(N=256, K=64 * 1024, R=8), 8, B.HT_PATH_AUTO) == \
+        B.ht_linear_workspace(_desc(N=256, K=64 * 1024, R=8), 8, B.HT_PATH_GEMV)
     wide = _desc(N=16384, K=4096, R=16)
     assert B.ht_linear_workspace(wide, 2048, B.HT_PATH_GEMM) == 0                 # 4096 tiles: no split
     with pytest.raises(B.HTError):

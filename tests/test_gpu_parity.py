@@ -308,7 +308,8 @@ def mlp4096(orc):
 
 @pytest.mark.parametrize("M,path", [(1, B.HT_PATH_AUTO), (1, B.HT_PATH_GEMV), (2, B.HT_PATH_FUSED),
                                     (3, B.HT_PATH_FUSED), (4, B.HT_PATH_FUSED), (4, B.HT_PATH_GEMV),
-                                    (32, B.HT_PATH_AUTO)])
+                                    (8, B.HT_PATH_AUTO), (16, B.HT_PATH_AUTO), (32, B.HT_PATH_AUTO),
+                                    (48, B.HT_PATH_AUTO)])
 def test_mlp_teacher_forced(orc, mlp4096, M, path):
     Ws, fmts, pws = mlp4096
     x = wl.to_bf16_bits(wl.mlp_activation(M))
