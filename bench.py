@@ -81,8 +81,8 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=6)
     ap.add_argument("--cpu-steps", type=int, default=20, help="oracle MLP forwards timed for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "gemv", "mlp", "gemm"], default="all",
-                    help="'gemv' / 'mlp' / 'gemm': only that timing leg (for counter runs)")
+    ap.add_argument("--only", choices=["all", "gemv", "mlp", "gemm", "decode"], default="all",
+                    help="'gemv' / 'mlp' / 'gemm' / 'decode': only that timing leg (for profiler runs)")
     ap.add_argument("--no-gemm", action="store_true", help="skip the prefill GEMM leg")
     args = ap.parse_args()
 
@@ -222,6 +222,21 @@ def main() -> int:
     mlp_fn(x1, y1)(0)
     torch.cuda.synchronize()
     y_eager = y1.clone()
+
+    if args.only == "decode":
+        # Decode at batch 16 and 32: one launch per layer on the MFMA decode
+        # path (gemv_mfma_kernel<1> / <2>; HT_PATH_AUTO takes it for 5..32
+        # rows), graphs of C forwards over the rotating copies, replayed.
+        out = {}
+        for M in (16, 32):
+            xm, ym = xbf(M), torch.empty((M, D), dtype=torch.float32, device=dev)
+            gm = graph_of(mlp_fn(xm, ym), C)
+            tm = replay_timed(gm, max(2, reps // 4), 1) / C
+            bm = sum(layer_bytes(counts[l], M, D, D, 2 if l + 1 < L else 4) for l in range(L))
+            out[f"mlp_batch{M}"] = {"us_per_forward": round(tm * 1e6, 2), "GBps": round(bm / tm / 1e9, 1)}
+            del gm
+        print(json.dumps({"kernel": "gemv_mfma_kernel<1> (batch 16) / <2> (batch 32)", "legs": out}))
+        return 0
 
     # ---- single-layer GEMV leg ---------------------------------------------
     # G back-to-back single-layer launches per graph, replayed; events on the
