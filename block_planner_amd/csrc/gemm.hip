@@ -1,8 +1,8 @@
 // gemm.hip -- the mixed-format linear for many rows of x (prefill):
 // y[m, n] = sum over K-blocks kb of  blk(m, n, kb)  with fp32 accumulation,
 // where an integer block contributes s * (sum_i q_i * x[m, 64kb+i]) and a
-// float block sum_i w_i * x[m, 64kb+i] (HyperTensor 1.0.1 page: "fused
-// mixed-precision operators" run the plan; "Key Features": HyperLinear).
+// float block sum_i w_i * x[m, 64kb+i] (HyperTensor 1.0.1 page, intro: fused
+// kernels execute the mixed-precision plan; "Key Features": HyperLinear).
 //
 // A workgroup owns a BM x 64 tile of y (BM = 256, 128 or 64 rows of x) and
 // walks K one 64-wide block at a time.  Per step the tile's 64 weight blocks

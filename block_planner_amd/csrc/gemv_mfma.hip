@@ -1,7 +1,7 @@
 // gemv_mfma.hip -- the mixed-format linear for a few rows of x (decode at
-// batch 1 to 32 per launch) with the dot products on the matrix cores (HyperTensor 1.0.1
-// page: "fused mixed-precision operators" run the plan; "Key Features":
-// HyperLinear).  Same sums as the MFMA prefill path:
+// batch 1 to 32 per launch) with the dot products on the matrix cores
+// (HyperTensor 1.0.1 page, intro: fused kernels execute the mixed-precision
+// plan; "Key Features": HyperLinear).  Same sums as the MFMA prefill path:
 //   y[m, n] = sum over K-blocks kb of  blk(m, n, kb),
 //   INT4 / INT8   blk = s * (sum_i q_i * x[m, 64kb+i]),
 //   BF16          blk = sum_i w_i * x[m, 64kb+i],

@@ -1,6 +1,6 @@
 // linear.hip -- one fused mixed-format linear over the packed execution
-// buffers (HyperTensor 1.0.1 page: "fused mixed-precision operators" run the
-// plan; "Key Features": HyperLinear, a drop-in nn.Linear).
+// buffers (HyperTensor 1.0.1 page, intro: fused kernels execute the
+// mixed-precision plan; "Key Features": HyperLinear, a drop-in nn.Linear).
 //
 // y[m, n] = sum over n's K-blocks kb of  blk(m, n, kb), where
 //   INT4 / INT8:  blk = s * (sum_i q_i * x[m, 64kb+i])   (scale after the partial)

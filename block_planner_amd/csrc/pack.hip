@@ -1,18 +1,22 @@
 // pack.hip -- compile a format map into execution buffers (HyperTensor 1.0.1
-// page, intro: the planner's format map "is compiled into optimized execution
-// buffers"; "Key Features": inference-only mode, which drops the fp32 master
-// weights -- after packing, the buffers are all the linear needs).
+// page, intro: the planner's per-block map is turned into buffers that the
+// fused kernels run from; "Key Features": inference-only mode, which drops
+// the fp32 master weights -- after packing, the buffers are all the linear
+// needs).
 //
-// Two kernels on the caller's stream:
-//   1. index: one workgroup per format counts, per (row tile t, K-block kb),
-//      the rows of the tile holding that format and writes the exclusive
-//      scan of these counts in (t, kb) order -> kbidx[f][t*KB + kb], total at
-//      kbidx[f][T*KB]; workgroup 0 also zeroes the alignment padding between
-//      regions so that every byte of the buffer is defined;
-//   2. scatter: one quad of lanes per block, in (t, kb, r) order; a block's
+// Three kernels on the caller's stream:
+//   1. count: a workgroup per 256 (row tile t, K-block kb) columns counts,
+//      per format, the tile's rows holding that format, scans the counts
+//      within its columns into kbidx[f][t*KB + kb], and leaves the
+//      segment's totals in the (not yet written) ids area;
+//   2. offset: each segment adds the totals of the segments before it (the
+//      last also writes each format's total at kbidx[f][T*KB]);
+//   3. scatter: one quad of lanes per block, in (t, kb, r) order; a block's
 //      position is kbidx[f][t*KB+kb] plus its rank among the column's rows of
 //      the same format (wave ballot).  Codes and scales are recomputed from W
 //      with the planner's exact arithmetic.  Stores are 16 bytes per lane.
+//      Its last workgroup zeroes the alignment padding between regions, so
+//      every byte of the buffer is defined.
 #include "quant.h"
 
 namespace ht {
@@ -34,121 +38,122 @@ struct PadArgs {
     int n;
 };
 
-// 0x01 in each byte of v that equals byte b (b replicated in bb = b * 0x01010101)
-__device__ __forceinline__ uint32_t eq_bytes(uint32_t v, uint32_t bb) {
-    const uint32_t x = v ^ bb;
-    return (~(((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x | 0x7F7F7F7Fu)) >> 7;
-}
+constexpr uint32_t kSeg = 256;   // columns per workgroup of the two index passes
 
-// Workgroup f: kbidx[f][c] = number of format-f blocks in columns before c
-// (column c = t*KB + kb, counted over the tile's rows), in chunks of 16384
-// columns, 16 consecutive columns per thread.  `rows16`: KB % 16 == 0 and the
-// map is 16-byte aligned, so a thread's 16 columns are one 16-byte piece of
-// each of the tile's rows of the map.
-__global__ __launch_bounds__(1024) void pack_index_kernel(PackArgs a, PadArgs pad, int rows16) {
-    __shared__ uint32_t wsum[16];
-    __shared__ __align__(16) uint8_t cbytes[1024 * 16];
-    __shared__ __align__(16) uint32_t outv[1024 * 16];   // the chunk's results, stored coalesced
-    const uint32_t f = blockIdx.x;
-    uint32_t *v = reinterpret_cast<uint32_t *>(a.buf + a.off_kbidx) + uint64_t(f) * a.nk;
+// Index pass 1.  Workgroup s owns columns [256 s, 256 s + 256) (column c =
+// t*KB + kb, one per thread): it counts, per format, the rows of tile t
+// holding that format in K-block kb, writes the exclusive scan of the counts
+// within the segment to kbidx[f][c], and the segment's totals to
+// tot[f * S + s].  Counts travel as 16-bit fields, two formats per word (a
+// segment holds at most 256 * 16 = 4096 blocks).  Codes above 4 are not
+// counted.
+__global__ __launch_bounds__(256) void pack_count_kernel(PackArgs a, uint32_t *tot, uint32_t S) {
+    __shared__ uint32_t wsum[4][3];
     const uint32_t L = a.T * a.KB;
+    const uint32_t c = blockIdx.x * kSeg + threadIdx.x;
     const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint32_t fb = f * 0x01010101u;
-    uint32_t carry = 0;
-    for (uint32_t base = 0; base < L; base += 16384u) {
-        const uint32_t c0 = base + threadIdx.x * 16u;
-        // all 16 row loads are issued before any is used (rows past the tile
-        // or past N read a valid row and are masked), so a chunk costs one
-        // memory round trip, not one per row
-        uint32_t cnt[16];
-        if (rows16) {
-            uint32_t acc[4] = {0u, 0u, 0u, 0u};
-            const uint32_t cc = c0 < L ? c0 : 0u;
-            const uint32_t t = fastdiv(cc, a.div_kb), kb0 = cc - t * a.KB;
-            uint4 row[16];
+    const uint32_t cc = min(c, L - 1u);
+    const uint32_t t = fastdiv(cc, a.div_kb), kb = cc - t * a.KB;
+    // all 16 row loads in flight at once (rows past the tile or past N read
+    // a valid row and are not counted)
+    uint32_t b[16];
 #pragma unroll
-            for (uint32_t r = 0; r < 16; ++r) {
-                const uint32_t n = min(t * a.R + min(r, a.R - 1u), a.N - 1u);
-                row[r] = *reinterpret_cast<const uint4 *>(a.fmt + uint64_t(n) * a.KB + kb0);
-            }
+    for (uint32_t r = 0; r < 16; ++r) b[r] = a.fmt[uint64_t(min(t * a.R + min(r, a.R - 1u), a.N - 1u)) * a.KB + kb];
+    uint32_t w[3] = {0u, 0u, 0u};   // formats 0 | 1 << 16, 2 | 3 << 16, 4
 #pragma unroll
-            for (uint32_t r = 0; r < 16; ++r) {
-                if (c0 < L && r < a.R && t * a.R + r < a.N) {
-                    acc[0] += eq_bytes(row[r].x, fb);
-                    acc[1] += eq_bytes(row[r].y, fb);
-                    acc[2] += eq_bytes(row[r].z, fb);
-                    acc[3] += eq_bytes(row[r].w, fb);
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < 16; ++j) cnt[j] = (acc[j >> 2] >> (8 * (j & 3))) & 0xFFu;   // <= 16 per byte
-        } else {
-            // byte-wise: one column at a time (its 16 row loads in flight),
-            // counts kept as bytes in LDS
-#pragma unroll 1
-            for (uint32_t j = 0; j < 16; ++j) {
-                const uint32_t c = min(c0 + j, L - 1u);
-                const uint32_t t = fastdiv(c, a.div_kb), kb = c - t * a.KB;
-                uint32_t b[16];
-#pragma unroll
-                for (uint32_t r = 0; r < 16; ++r)
-                    b[r] = a.fmt[uint64_t(min(t * a.R + min(r, a.R - 1u), a.N - 1u)) * a.KB + kb];
-                uint32_t k = 0;
-#pragma unroll
-                for (uint32_t r = 0; r < 16; ++r)
-                    k += (c0 + j < L && r < a.R && t * a.R + r < a.N && b[r] == f) ? 1u : 0u;
-                cbytes[threadIdx.x * 16u + j] = uint8_t(k);
-            }
-            const uint4 cb = *reinterpret_cast<const uint4 *>(&cbytes[threadIdx.x * 16u]);   // own bytes only
-            const uint32_t cw[4] = {cb.x, cb.y, cb.z, cb.w};
-#pragma unroll
-            for (int j = 0; j < 16; ++j) cnt[j] = (cw[j >> 2] >> (8 * (j & 3))) & 0xFFu;
+    for (uint32_t r = 0; r < 16; ++r) {
+        const uint32_t f = b[r];
+        if (c < L && r < a.R && t * a.R + r < a.N) {
+            w[0] += (f == 0u ? 1u : 0u) + (f == 1u ? 0x10000u : 0u);
+            w[1] += (f == 2u ? 1u : 0u) + (f == 3u ? 0x10000u : 0u);
+            w[2] += f == 4u ? 1u : 0u;
         }
-        uint32_t tot = 0;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const uint32_t e = cnt[j];
-            cnt[j] = tot;   // exclusive within the thread
-            tot += e;
-        }
-        uint32_t inc = tot;   // inclusive scan across the wave
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t o = __shfl_up(inc, off);
-            if (lane >= uint32_t(off)) inc += o;
-        }
-        if (lane == 63) wsum[wave] = inc;
-        __syncthreads();
-        uint32_t wprefix = 0, all = 0;
-#pragma unroll
-        for (uint32_t k = 0; k < 16; ++k) {
-            const uint32_t ws = wsum[k];
-            wprefix += k < wave ? ws : 0u;
-            all += ws;
-        }
-        const uint32_t run = carry + wprefix + inc - tot;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            *reinterpret_cast<uint4 *>(&outv[threadIdx.x * 16u + 4 * j]) =
-                make_uint4(run + cnt[4 * j], run + cnt[4 * j + 1], run + cnt[4 * j + 2], run + cnt[4 * j + 3]);
-        __syncthreads();
-#pragma unroll
-        for (uint32_t k = 0; k < 16; ++k) {
-            const uint32_t i = threadIdx.x + 1024u * k;
-            if (base + i < L) v[base + i] = outv[i];
-        }
-        carry += all;
-        __syncthreads();   // wsum and outv are rewritten by the next chunk
     }
-    if (threadIdx.x == 0) v[L] = carry;
-    if (f == 0) {
-        for (int k = 0; k < pad.n; ++k)
-            for (uint32_t i = threadIdx.x; i < pad.len[k]; i += 1024u) a.buf[pad.start[k] + i] = 0;
+    uint32_t inc[3] = {w[0], w[1], w[2]};   // inclusive scan across the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            const uint32_t o = __shfl_up(inc[k], off);
+            if (lane >= uint32_t(off)) inc[k] += o;
+        }
+    }
+    if (lane == 63) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k) wsum[wave][k] = inc[k];
+    }
+    __syncthreads();
+    uint32_t ex[3], all[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        uint32_t pre = 0, sum = 0;
+#pragma unroll
+        for (uint32_t v = 0; v < 4; ++v) {
+            pre += v < wave ? wsum[v][k] : 0u;
+            sum += wsum[v][k];
+        }
+        ex[k] = pre + inc[k] - w[k];
+        all[k] = sum;
+    }
+    uint32_t *kbidx = reinterpret_cast<uint32_t *>(a.buf + a.off_kbidx);
+    if (c < L) {
+#pragma unroll
+        for (int f = 0; f < 5; ++f) kbidx[uint64_t(f) * a.nk + c] = (ex[f >> 1] >> (16 * (f & 1))) & 0xFFFFu;
+    }
+    if (threadIdx.x < 5) {
+        const uint32_t f = threadIdx.x;
+        const uint32_t v = f == 0 ? all[0] : f == 1 ? all[0] >> 16 : f == 2 ? all[1] : f == 3 ? all[1] >> 16 : all[2];
+        tot[f * S + blockIdx.x] = v & 0xFFFFu;
     }
 }
 
-__global__ __launch_bounds__(256) void pack_scatter_kernel(PackArgs a) {
+// Index pass 2.  Workgroup s adds to its columns' kbidx entries the number of
+// format-f blocks in the segments before it (a sum of integers: any order
+// gives the same value); the last workgroup also writes each format's total
+// at kbidx[f][T*KB].
+__global__ __launch_bounds__(256) void pack_offset_kernel(PackArgs a, const uint32_t *tot, uint32_t S) {
+    __shared__ uint32_t red[4][5];
+    const uint32_t s = blockIdx.x, L = a.T * a.KB;
+    const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t v[5] = {0u, 0u, 0u, 0u, 0u};
+    for (uint32_t i = threadIdx.x; i < s; i += kSeg) {
+#pragma unroll
+        for (int f = 0; f < 5; ++f) v[f] += tot[f * S + i];
+    }
+#pragma unroll
+    for (int f = 0; f < 5; ++f) {
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) v[f] += __shfl_xor(v[f], off);
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int f = 0; f < 5; ++f) red[wave][f] = v[f];
+    }
+    __syncthreads();
+    uint32_t off[5];
+#pragma unroll
+    for (int f = 0; f < 5; ++f) off[f] = red[0][f] + red[1][f] + red[2][f] + red[3][f];
+    uint32_t *kbidx = reinterpret_cast<uint32_t *>(a.buf + a.off_kbidx);
+    const uint32_t c = s * kSeg + threadIdx.x;
+    if (c < L) {
+#pragma unroll
+        for (int f = 0; f < 5; ++f) kbidx[uint64_t(f) * a.nk + c] += off[f];
+    }
+    if (s == S - 1u && threadIdx.x < 5) {
+        const uint32_t f = threadIdx.x;
+        kbidx[uint64_t(f) * a.nk + L] = (f == 0 ? off[0] : f == 1 ? off[1] : f == 2 ? off[2] : f == 3 ? off[3] : off[4]) +
+                                        tot[f * S + s];
+    }
+}
+
+__global__ __launch_bounds__(256) void pack_scatter_kernel(PackArgs a, PadArgs pad) {
     __shared__ __align__(16) float stage[4][16 * 64];      // per wave: its 16 blocks
+    // the last workgroup zeroes the alignment padding between regions (the
+    // index passes kept scratch totals in the ids area, so not before now)
+    if (blockIdx.x == gridDim.x - 1u) {
+        for (int k = 0; k < pad.n; ++k)
+            for (uint32_t i = threadIdx.x; i < pad.len[k]; i += 256u) a.buf[pad.start[k] + i] = 0;
+    }
     const uint32_t tid = blockIdx.x * 256u + threadIdx.x;
     const uint32_t g = tid >> 2;                 // slot in (t, kb, r) order
     const int part = int(threadIdx.x & 3);
@@ -377,10 +382,16 @@ extern "C" ht_status ht_pack(const float *W, int64_t N, int64_t K, int64_t ldw, 
         ++k;
     }
     p.n = k;
-    const int rows16 = (KB % 16 == 0) && (reinterpret_cast<uintptr_t>(fmt_map) % 16 == 0);
-    hipLaunchKernelGGL(pack_index_kernel, dim3(5), dim3(1024), 0, s, a, p, rows16);
+    // the index passes keep 5 * S segment totals in the ids area (at least
+    // 2 bytes per column; the scatter rewrites it and zeroes the padding)
+    const uint32_t S = uint32_t((uint64_t(cols) + kSeg - 1) / kSeg);
+    if (uint64_t(S) * 20u > L.scale[0] - L.ids[0]) return HT_ESHAPE;   // cannot happen (see above)
+    uint32_t *tot = reinterpret_cast<uint32_t *>(a.buf + L.ids[0]);
+    hipLaunchKernelGGL(pack_count_kernel, dim3(S), dim3(kSeg), 0, s, a, tot, S);
     HT_LAUNCH_CHECK();
-    hipLaunchKernelGGL(pack_scatter_kernel, dim3(uint32_t(grid)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(pack_offset_kernel, dim3(S), dim3(kSeg), 0, s, a, static_cast<const uint32_t *>(tot), S);
+    HT_LAUNCH_CHECK();
+    hipLaunchKernelGGL(pack_scatter_kernel, dim3(uint32_t(grid)), dim3(256), 0, s, a, p);
     HT_LAUNCH_CHECK();
 
     desc->N = N;

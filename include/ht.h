@@ -4,9 +4,8 @@
  * The method (HyperTensor 1.0.1 project page): a precision planner measures
  * the reconstruction error of each weight block and keeps the lowest format
  * that stays safe ("What it does", "Key Features": per-block selection among
- * INT4 / INT8 / FP16 / BF16 / FP32); the resulting format map is compiled
- * into execution buffers and run by fused mixed-precision operators (intro
- * paragraph).  The page's user calls map onto this ABI as follows:
+ * INT4 / INT8 / FP16 / BF16 / FP32); the map it produces becomes packed
+ * buffers that fused kernels multiply from (intro paragraph).  The page's user calls map onto this ABI as follows:
  *   scan_model(...)                    ("Convert model")  -> ht_plan
  *   wrap_model_with_hypertensor(...)   ("Convert model")  -> ht_pack
  *   HyperLinear(...).forward           ("Usage Example")  -> ht_linear_forward
@@ -150,7 +149,7 @@ ht_status ht_pack_bytes(int64_t N, int64_t K, int64_t row_tile,
                         const int64_t counts5[5], size_t *bytes);
 
 /* ht_pack -- compile a plan into execution buffers (intro paragraph: the
- * format map "is compiled into optimized execution buffers").
+ * per-block format map is turned into buffers the fused kernels run from).
  *   W, N, K, ldw  as for ht_plan (W is only read; the caller may free it
  *                 afterwards: the buffers hold everything the linear needs,
  *                 the page's inference-only mode).

@@ -11,8 +11,8 @@
  *   - "Key Features": per-block precision selection (PER_BLOCK).
  *   - "Convert model": eps_fp16 = eps_bf16 = 0 and prefer_bf16 = True are the
  *     defaults of the scan.
- *   - Intro paragraph: the planner's format map is compiled into execution
- *     buffers that the fused mixed-precision operators consume.
+ *   - Intro paragraph: the planner's map becomes packed buffers that fused
+ *     kernels multiply from.
  * The numeric rule used for every block (the pages leave it open and it is
  * fixed by the method's specification):
  *   block      = 64 consecutive entries of one row of W[N, K] (a K-block);
