@@ -180,13 +180,15 @@ def test_pack_edge_blocks_16bit(orc, force):
 
 
 @pytest.mark.parametrize("N,KB,R,offset", [
-    (1030, 272, 16, 0),   # 65 x 272 columns: two chunks of the index scan, 16-byte map rows, ragged tile
-    (1030, 277, 4, 0),    # KB not a multiple of 16: the byte-wise count, five chunks
-    (1030, 272, 16, 1),   # map at an address that is not 16-byte aligned: the byte-wise count
+    (1030, 272, 16, 0),   # 65 x 272 columns: 70 segments of the index passes, ragged last tile and segment
+    (1030, 277, 4, 0),    # 258 x 277 columns: 280 segments, segment edges inside tiles
+    (1030, 272, 16, 1),   # map at an address that is not 16-byte aligned
 ])
 def test_pack_index_chunks(orc, N, KB, R, offset):
-    """The per-format counts and their scan over more than one chunk of
-    columns, on both counting paths; random formats so every format occurs."""
+    """The per-format counts, their scan within 256-column segments and the
+    segment offsets over many segments; random formats so every format
+    occurs.  (A segment holding 4096 blocks of one format, the largest its
+    16-bit fields carry, is in the forced full-layer packs below.)"""
     rng = np.random.default_rng(N + KB + R + offset)
     W = (rng.normal(size=(N, 64 * KB)) * 0.05).astype(np.float32)
     fmt = rng.integers(0, 5, size=(N, KB)).astype(np.uint8)
