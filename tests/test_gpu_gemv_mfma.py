@@ -159,3 +159,21 @@ def test_dec_needs_row_tile_16():
         B.ht_linear_workspace(pw.desc, 4, DEC)
     with pytest.raises(B.HTError):
         B.ht_linear_forward(pw.desc, x, y, path=DEC)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_dec_random_shapes(orc, seed):
+    """Seeded random shapes: rows from 1 to 600 (ragged last tile), 1 to 300
+    K-blocks (a partial last round of 64 or 32 K-blocks, K-splits when there
+    are few row tiles), 1 to 40 rows of x, random formats, ReLU half the
+    time."""
+    rng = np.random.default_rng(1000 + seed)
+    N = int(rng.integers(1, 601))
+    KB = int(rng.integers(1, 301))
+    M = int(rng.integers(1, 41))
+    act = int(rng.integers(0, 2))
+    W = (rng.standard_t(4, size=(N, 64 * KB)) * 0.03).astype(np.float32)
+    fmt = rng.integers(0, 5, size=(N, KB)).astype(np.uint8)
+    x = wl.to_bf16_bits(rng.normal(size=(M, 64 * KB)).astype(np.float32))
+    y_or = orc.linear(W, fmt, x)
+    check_close(run_dec(W, fmt, x, act=act), relu(y_or) if act else y_or, f"N={N} KB={KB} M={M} act={act}")
