@@ -210,26 +210,29 @@ def test_pack_mlp_layer(orc):
 # ---------------------------------------------------------------------------
 # Linear
 # ---------------------------------------------------------------------------
-def run_linear(W, fmt, xbits, R=16, act=0, ldx_pad=0, ldy_pad=0):
+def run_linear(W, fmt, xbits, R=16, act=0, ldx_pad=0, ldy_pad=0, path=B.HT_PATH_AUTO):
     pw = api.pack(gpu(W), gpu(fmt), row_tile=R)
     M, K = xbits.shape
     xs = torch.zeros((M, K + ldx_pad), dtype=torch.bfloat16, device=dev())
     xs[:, :K] = bf16_gpu(xbits)
     ys = torch.full((M, W.shape[0] + ldy_pad), 7.0, dtype=torch.float32, device=dev())
     x_v, y_v = xs[:, :K], ys[:, :W.shape[0]]
-    api.linear(pw, x_v, act=act, out=y_v)
+    api.linear(pw, x_v, act=act, out=y_v, path=path)
     torch.cuda.synchronize()
     if ldy_pad:
         assert torch.all(ys[:, W.shape[0]:] == 7.0)   # padding untouched
     return y_v.cpu().numpy()
 
 
+@pytest.mark.parametrize("path", [B.HT_PATH_GEMV, B.HT_PATH_AUTO])
 @pytest.mark.parametrize("M", [1, 2, 5, 8, 13])
-def test_linear_small_weight(orc, M):
+def test_linear_small_weight(orc, M, path):
+    """The register path at 1 to 13 rows (up to 8 rows per launch, so 13 is
+    two launches), and what AUTO picks (the MFMA decode path from 5 rows)."""
     W = wl.small_weight()
     fmt = orc.plan(W)
     x = wl.to_bf16_bits(wl.small_activation(m=M))
-    check_close(run_linear(W, fmt, x), orc.linear(W, fmt, x), f"M={M}")
+    check_close(run_linear(W, fmt, x, path=path), orc.linear(W, fmt, x), f"M={M} path={path}")
 
 
 @pytest.mark.parametrize("R", [1, 4, 16])
