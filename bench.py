@@ -326,7 +326,8 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp32-accumulate over int4/int8/bf16/fp16/fp32 weights, bf16 activations",
+        "dtype": "fp32",
+        "operands": "int4/int8/bf16/fp16/fp32 weight blocks, bf16 activations, fp32 products and sums",
         "data": "synthetic (seeded Student-t weights, N(0,1) activations)",
         "config": {"workload": "4-layer MLP, Linear(4096,4096)+ReLU x4, no bias, batch 1, bf16 activations, "
                                "default eps (0.08/0.01/0/0), 64-wide K-blocks, row tile 16",
