@@ -20,13 +20,15 @@
 // the row named by that block's id; a forward lane permute moves it (and the
 // block's scale) to the lane that owns the row before acc += scale * partial.
 //
-// A workgroup (16 wavefronts) owns one row tile and one K range, walked in
-// rounds of 64 / MG K-blocks: the round's x rows are staged in LDS while
-// every wavefront has the loads of all of its columns of the round (four, or
-// two at MG = 2) in flight, so a round costs about one memory round trip.
-// The workgroup then adds the 16 wavefronts' sums in wavefront order through
-// LDS and writes y (or, with several K ranges, the range's partial sums,
-// which a second kernel adds in range order).
+// A workgroup (16 wavefronts) owns one K range and one to four row tiles
+// (tiles blockIdx.x + i * gridDim.x; several only when there are more tiles
+// than compute units), walked in rounds of 64 / MG K-blocks: the round's x
+// rows are staged in LDS once for all of its tiles, and for each tile every
+// wavefront has the loads of all of its columns of the round (four, or two
+// at MG = 2) in flight, so a tile costs about one memory round trip per
+// round.  The workgroup then adds each tile's 16 wavefront sums in wavefront
+// order through LDS and writes y (or, with several K ranges, the range's
+// partial sums, which a second kernel adds in range order).
 #include "gemv_common.h"
 #include "linear_host.h"
 
@@ -48,6 +50,7 @@ struct DecArgs {
     int64_t ldy;
     uint32_t M;
     uint32_t KBs;             // K-blocks per split
+    uint32_t TPW;             // row tiles per workgroup (tiles blockIdx.x + i * gridDim.x, i < TPW)
     int act;
 };
 
@@ -64,6 +67,7 @@ struct DecLoad {
 // round, row stride padded by 16 bytes so that the 16 rows an MFMA operand
 // read touches fall in distinct banks.
 constexpr uint32_t kDecChunk = 64;                    // K-blocks per round at MG = 1
+constexpr uint32_t kDecMaxTPW = 4;                    // row tiles per workgroup at most
 template <int MG> constexpr uint32_t dec_row() { return (kDecChunk / MG) * 64u + 8u; }   // bfloat16 entries
 
 template <int MG>
@@ -77,11 +81,10 @@ __global__ __launch_bounds__(kDecThreads) void gemv_mfma_kernel(DecArgs a) {
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t j = lane & 15, q = lane >> 4;
-    const uint32_t t = blockIdx.x;                         // row tile (16 rows)
     const uint32_t kbs0 = blockIdx.y * a.KBs;
     const uint32_t kbs1 = min(w.KB, kbs0 + a.KBs);
     const uint8_t *base = w.base;                          // offsets below are 32-bit (buffer < 4 GiB)
-    const uint32_t *kbt = reinterpret_cast<const uint32_t *>(base + w.off_kbidx) + t * w.KB;
+    const uint32_t *kbx = reinterpret_cast<const uint32_t *>(base + w.off_kbidx);
 
     uint32_t opay[5], oids[5];
 #pragma unroll
@@ -91,13 +94,13 @@ __global__ __launch_bounds__(kDecThreads) void gemv_mfma_kernel(DecArgs a) {
     }
     const uint32_t osc0 = uint32_t(w.off_scale[0]), osc1 = uint32_t(w.off_scale[1]);
 
-    // kbidx[f][t*KB + kb0 + c] for c = 0..15 of the wavefront's columns in a
-    // round starting at kc: lane i holds format i / 16 (formats 0-3) and, in
-    // kv4, format 4, at column i % 16
-    auto kbidx_window = [&](uint32_t kc, uint32_t &v, uint32_t &v4) {
-        const uint32_t ci = min(kc + wave * CW + j, w.KB);
-        v = kbt[q * w.nk + ci];
-        v4 = kbt[4u * w.nk + ci];
+    // kbidx[f][t*KB + kb0 + c] for c = 0..15 of the wavefront's columns of
+    // row tile t in a round starting at kc: lane i holds format i / 16
+    // (formats 0-3) and, in kv4, format 4, at column i % 16
+    auto kbidx_window = [&](uint32_t t, uint32_t kc, uint32_t &v, uint32_t &v4) {
+        const uint32_t ci = t * w.KB + min(kc + wave * CW + j, w.KB);
+        v = kbx[q * w.nk + ci];
+        v4 = kbx[4u * w.nk + ci];
     };
     auto kbidx_at = [&](uint32_t kv, uint32_t kv4, uint32_t c, uint32_t (&v)[5]) {   // wave-uniform
 #pragma unroll
@@ -156,9 +159,11 @@ __global__ __launch_bounds__(kDecThreads) void gemv_mfma_kernel(DecArgs a) {
         return d;
     };
 
-    f32x4 acc[MG];
+    f32x4 acc[kDecMaxTPW][MG];
 #pragma unroll
-    for (int g = 0; g < MG; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < int(kDecMaxTPW); ++i)
+#pragma unroll
+        for (int g = 0; g < MG; ++g) acc[i][g] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     auto pair_hi = [](float f0, float f1) {   // upper halves of two fp32 -> one word
         return __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
@@ -170,8 +175,8 @@ __global__ __launch_bounds__(kDecThreads) void gemv_mfma_kernel(DecArgs a) {
         return __builtin_bit_cast(uint32_t, v);
     };
 
-    // Multiply one loaded column (K-block kl of the round) into acc.
-    auto compute = [&](const DecLoad &d, uint32_t kl) {
+    // Multiply one loaded column (K-block kl of the round) into acc[i].
+    auto compute = [&](const DecLoad &d, uint32_t kl, f32x4 (&acc)[MG]) {
         const uint32_t u[16] = {d.p[0].x, d.p[0].y, d.p[0].z, d.p[0].w, d.p[1].x, d.p[1].y, d.p[1].z, d.p[1].w,
                                 d.p[2].x, d.p[2].y, d.p[2].z, d.p[2].w, d.p[3].x, d.p[3].y, d.p[3].z, d.p[3].w};
         uint32_t hp[8], lp[8];
@@ -283,46 +288,90 @@ __global__ __launch_bounds__(kDecThreads) void gemv_mfma_kernel(DecArgs a) {
                          : "memory", "m0");
         }
     };
+    // Rounds over K outside, the workgroup's row tiles inside: the round's x
+    // is copied once for all of them.  The column registers roll: as soon as
+    // column c of the current (round, tile) has been multiplied, they are
+    // reloaded with column c of the next (round, tile), whose kbidx window is
+    // already in registers (the window after that is then requested), so the
+    // next tile's loads overlap this tile's arithmetic.  Windows past the end
+    // of K are clamped to it: their loads find no block.
+    const uint32_t tpw = a.TPW;
+    auto tile_ok = [&](uint32_t i) { return i < tpw && blockIdx.x + i * gridDim.x < w.T; };
+    uint32_t pk = kbs0, pi = 0;                           // (round, tile) whose window is in kv
+    auto advance = [&]() {                                // to the next (round, tile)
+        if (tile_ok(pi + 1)) {
+            ++pi;
+        } else {
+            pi = 0;
+            pk += CK;
+        }
+    };
+    auto window = [&](uint32_t &kv, uint32_t &kv4) {
+        kbidx_window(blockIdx.x + pi * gridDim.x, pk < kbs1 ? pk : w.KB, kv, kv4);
+    };
     uint32_t kv, kv4;
     stage_x(kbs0);                                        // in flight together with the first window
-    kbidx_window(kbs0, kv, kv4);
+    window(kv, kv4);
+    DecLoad d[CW];
+#pragma unroll
+    for (uint32_t c = 0; c < CW; ++c) d[c] = load_col(kv, kv4, c);
+    advance();
+    if (MG == 1 || pk < kbs1) window(kv, kv4);
     for (uint32_t kc = kbs0; kc < kbs1; kc += CK) {
         const uint32_t nkc = min(CK, kbs1 - kc);
-        DecLoad d[CW];
-#pragma unroll
-        for (uint32_t c = 0; c < CW; ++c) d[c] = load_col(kv, kv4, c);
         const uint32_t nc = min(nkc, wave * CW + CW) - min(nkc, wave * CW);   // columns of this wavefront
-        kbidx_window(kc + CK, kv, kv4);                   // next round's window (clamped past the end)
-        __builtin_amdgcn_s_waitcnt(0x0F70);               // vmcnt(0): this wavefront's x pieces are in LDS
-        __syncthreads();
 #pragma unroll
-        for (uint32_t c = 0; c < CW; ++c)
-            if (c < nc) compute(d[c], wave * CW + c);
+        for (uint32_t i = 0; i < kDecMaxTPW; ++i) {
+            if (!tile_ok(i)) continue;                    // workgroup-uniform
+            if (i == 0) {
+                __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): this wavefront's x pieces are in LDS
+                __syncthreads();
+            }
+            // after the workgroup's last tile of its last round there is
+            // nothing to refill; at MG = 2 the loads are skipped then, at
+            // MG = 1 they stay unconditional (clamped windows, no block
+            // found), which keeps the register allocation free of spills
+            const bool more = MG == 1 || pk < kbs1;       // workgroup-uniform
+#pragma unroll
+            for (uint32_t c = 0; c < CW; ++c) {
+                if (c < nc) compute(d[c], wave * CW + c, acc[i]);
+                if (more) d[c] = load_col(kv, kv4, c);
+            }
+            advance();
+            if (MG == 1 || pk < kbs1) window(kv, kv4);
+        }
         __syncthreads();
         if (kc + CK < kbs1) stage_x(kc + CK);
     }
 
-    // lane (r, q) holds rows m = 16g + 4q + e of output row t*16 + r
+    // Per tile: lane (r, q) holds rows m = 16g + 4q + e of output row
+    // t*16 + r; the 16 wavefronts' sums are added in wavefront order.
 #pragma unroll
-    for (int g = 0; g < MG; ++g)
+    for (uint32_t i = 0; i < kDecMaxTPW; ++i) {
+        if (!tile_ok(i)) continue;                        // workgroup-uniform
+        const uint32_t t = blockIdx.x + i * gridDim.x;
+        if (i) __syncthreads();                           // the previous tile's sums are read
 #pragma unroll
-        for (int e = 0; e < 4; ++e) red[(wave * (MG * 4) + g * 4 + e) * 64 + lane] = acc[g][e];
-    __syncthreads();
-    const uint32_t o = threadIdx.x;
-    if (o < 256u * MG) {
-        const uint32_t m = o >> 4, r = o & 15u;
-        const uint32_t g = m >> 4, qq = (m >> 2) & 3u, e = m & 3u;
-        float v = 0.0f;
+        for (int g = 0; g < MG; ++g)
 #pragma unroll
-        for (uint32_t k = 0; k < kDecWaves; ++k) v += red[(k * (MG * 4) + g * 4 + e) * 64 + r + 16u * qq];
-        const uint32_t n = t * 16u + r;
-        if (m < a.M && n < w.N) {
-            if (a.partial) {
-                a.partial[(uint64_t(blockIdx.y) * a.M + m) * w.N + n] = v;
-            } else {
-                if (a.act == HT_ACT_RELU) v = v > 0.0f ? v : 0.0f;
-                if (a.ybf) a.ybf[int64_t(m) * a.ldy + n] = f32_to_bf16_rne(v);
-                else a.y[int64_t(m) * a.ldy + n] = v;
+            for (int e = 0; e < 4; ++e) red[(wave * (MG * 4) + g * 4 + e) * 64 + lane] = acc[i][g][e];
+        __syncthreads();
+        const uint32_t o = threadIdx.x;
+        if (o < 256u * MG) {
+            const uint32_t m = o >> 4, r = o & 15u;
+            const uint32_t g = m >> 4, qq = (m >> 2) & 3u, e = m & 3u;
+            float v = 0.0f;
+#pragma unroll
+            for (uint32_t k = 0; k < kDecWaves; ++k) v += red[(k * (MG * 4) + g * 4 + e) * 64 + r + 16u * qq];
+            const uint32_t n = t * 16u + r;
+            if (m < a.M && n < w.N) {
+                if (a.partial) {
+                    a.partial[(uint64_t(blockIdx.y) * a.M + m) * w.N + n] = v;
+                } else {
+                    if (a.act == HT_ACT_RELU) v = v > 0.0f ? v : 0.0f;
+                    if (a.ybf) a.ybf[int64_t(m) * a.ldy + n] = f32_to_bf16_rne(v);
+                    else a.y[int64_t(m) * a.ldy + n] = v;
+                }
             }
         }
     }
@@ -352,9 +401,23 @@ DecShape dec_shape(const ht_packed_weight *w) {
     return d;
 }
 
+// Row tiles per workgroup: one while the tiles fit one workgroup per compute
+// unit (the LDS of a workgroup allows one per compute unit), else up to
+// kDecMaxTPW, so that x is copied once for several tiles instead of the
+// launch running in several waves of workgroups.
+uint32_t dec_tpw(uint32_t T) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    if (T <= uint32_t(cus)) return 1;
+    const uint32_t tpw = (T + uint32_t(cus) - 1) / uint32_t(cus);
+    return tpw < kDecMaxTPW ? tpw : kDecMaxTPW;
+}
+
 template <int MG>
-void launch_dec(const DecArgs &a, uint32_t T, uint32_t S, hipStream_t s) {
-    hipLaunchKernelGGL(gemv_mfma_kernel<MG>, dim3(T, S), dim3(kDecThreads), 0, s, a);
+void launch_dec(const DecArgs &a, uint32_t G, uint32_t S, hipStream_t s) {
+    hipLaunchKernelGGL(gemv_mfma_kernel<MG>, dim3(G, S), dim3(kDecThreads), 0, s, a);
 }
 
 }  // namespace
@@ -376,6 +439,9 @@ ht_status run_dec(const ht_packed_weight *w, const uint16_t *x, int64_t M, int64
     a.ldy = ldy;
     a.act = act;
     a.KBs = d.KBs;
+    const uint32_t T = uint32_t(w->n_tiles);
+    a.TPW = dec_tpw(T);
+    const uint32_t G = (T + a.TPW - 1) / a.TPW;
     for (int64_t m0 = 0; m0 < M; m0 += kDecMaxM) {
         const int64_t Mt = M - m0 < kDecMaxM ? M - m0 : kDecMaxM;
         a.x = x + m0 * ldx;
@@ -391,9 +457,8 @@ ht_status run_dec(const ht_packed_weight *w, const uint16_t *x, int64_t M, int64
             a.y = yo;
             a.ybf = yb;
         }
-        const uint32_t T = uint32_t(w->n_tiles);
-        if (Mt <= 16) launch_dec<1>(a, T, d.S, s);
-        else launch_dec<2>(a, T, d.S, s);
+        if (Mt <= 16) launch_dec<1>(a, G, d.S, s);
+        else launch_dec<2>(a, G, d.S, s);
         HT_LAUNCH_CHECK();
         if (d.S > 1) {
             const ht_status st = launch_split_reduce(static_cast<const float *>(ws), d.S, uint32_t(Mt), a.w.N, yo,
