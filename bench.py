@@ -231,7 +231,7 @@ def main() -> int:
         for M in (16, 32):
             xm, ym = xbf(M), torch.empty((M, D), dtype=torch.float32, device=dev)
             gm = graph_of(mlp_fn(xm, ym), C)
-            tm = replay_timed(gm, max(2, reps // 4), 1) / C
+            tm = replay_timed(gm, 10, 2) / C
             bm = sum(layer_bytes(counts[l], M, D, D, 2 if l + 1 < L else 4) for l in range(L))
             out[f"mlp_batch{M}"] = {"us_per_forward": round(tm * 1e6, 2), "GBps": round(bm / tm / 1e9, 1)}
             del gm
@@ -285,7 +285,7 @@ def main() -> int:
     gp = graph_of(mlp_fn(x1, y1, path=B.HT_PATH_GEMV), G)
     t_perlayer = replay_timed(gp, reps, 1) / G
     g32 = graph_of(mlp_fn(x32, y32), C)
-    t32 = replay_timed(g32, max(2, reps // 4), 1) / C
+    t32 = replay_timed(g32, 10, 2) / C
     gw = graph_of(mlp_fn(x1, y1, rotate=False), G)
     t_warm = replay_timed(gw, reps, 1) / G
     del gp, g32, gw

@@ -70,11 +70,15 @@ constexpr uint32_t kDecChunk = 64;                    // K-blocks per round at M
 constexpr uint32_t kDecMaxTPW = 4;                    // row tiles per workgroup at most
 template <int MG> constexpr uint32_t dec_row() { return (kDecChunk / MG) * 64u + 8u; }   // bfloat16 entries
 
-template <int MG>
+// ROLL: the workgroup has more than one (round, tile) step, so columns are
+// refilled as they are consumed; without it each wavefront loads its columns
+// once.
+template <int MG, bool ROLL>
 __global__ __launch_bounds__(kDecThreads) void gemv_mfma_kernel(DecArgs a) {
     constexpr uint32_t CK = kDecChunk / MG;           // K-blocks per round
     constexpr uint32_t CW = CK / kDecWaves;           // K-blocks per wavefront per round (4 or 2)
     constexpr uint32_t XR = dec_row<MG>();
+    constexpr uint32_t NT = ROLL ? kDecMaxTPW : 1u;   // row tiles a workgroup can hold
     __shared__ __align__(16) uint16_t xs[16 * MG * XR];
     float *red = reinterpret_cast<float *>(xs);       // [wave][MG * 4][64] after the last round
     const LayerDev &w = a.w;
@@ -159,9 +163,9 @@ __global__ __launch_bounds__(kDecThreads) void gemv_mfma_kernel(DecArgs a) {
         return d;
     };
 
-    f32x4 acc[kDecMaxTPW][MG];
+    f32x4 acc[NT][MG];
 #pragma unroll
-    for (int i = 0; i < int(kDecMaxTPW); ++i)
+    for (int i = 0; i < int(NT); ++i)
 #pragma unroll
         for (int g = 0; g < MG; ++g) acc[i][g] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -313,16 +317,23 @@ __global__ __launch_bounds__(kDecThreads) void gemv_mfma_kernel(DecArgs a) {
     stage_x(kbs0);                                        // in flight together with the first window
     window(kv, kv4);
     DecLoad d[CW];
+    if (ROLL) {
 #pragma unroll
-    for (uint32_t c = 0; c < CW; ++c) d[c] = load_col(kv, kv4, c);
-    advance();
-    if (MG == 1 || pk < kbs1) window(kv, kv4);
+        for (uint32_t c = 0; c < CW; ++c) d[c] = load_col(kv, kv4, c);
+        advance();
+        if (MG == 1 || pk < kbs1) window(kv, kv4);
+    }
     for (uint32_t kc = kbs0; kc < kbs1; kc += CK) {
         const uint32_t nkc = min(CK, kbs1 - kc);
         const uint32_t nc = min(nkc, wave * CW + CW) - min(nkc, wave * CW);   // columns of this wavefront
 #pragma unroll
-        for (uint32_t i = 0; i < kDecMaxTPW; ++i) {
+        for (uint32_t i = 0; i < NT; ++i) {
             if (!tile_ok(i)) continue;                    // workgroup-uniform
+            if (!ROLL) {                                  // one tile: load its columns now
+#pragma unroll
+                for (uint32_t c = 0; c < CW; ++c) d[c] = load_col(kv, kv4, c);
+                kbidx_window(blockIdx.x, kc + CK, kv, kv4);   // the next round's window (clamped past the end)
+            }
             if (i == 0) {
                 __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): this wavefront's x pieces are in LDS
                 __syncthreads();
@@ -335,10 +346,12 @@ __global__ __launch_bounds__(kDecThreads) void gemv_mfma_kernel(DecArgs a) {
 #pragma unroll
             for (uint32_t c = 0; c < CW; ++c) {
                 if (c < nc) compute(d[c], wave * CW + c, acc[i]);
-                if (more) d[c] = load_col(kv, kv4, c);
+                if (ROLL && more) d[c] = load_col(kv, kv4, c);
             }
-            advance();
-            if (MG == 1 || pk < kbs1) window(kv, kv4);
+            if (ROLL) {
+                advance();
+                if (MG == 1 || pk < kbs1) window(kv, kv4);
+            }
         }
         __syncthreads();
         if (kc + CK < kbs1) stage_x(kc + CK);
@@ -347,7 +360,7 @@ __global__ __launch_bounds__(kDecThreads) void gemv_mfma_kernel(DecArgs a) {
     // Per tile: lane (r, q) holds rows m = 16g + 4q + e of output row
     // t*16 + r; the 16 wavefronts' sums are added in wavefront order.
 #pragma unroll
-    for (uint32_t i = 0; i < kDecMaxTPW; ++i) {
+    for (uint32_t i = 0; i < NT; ++i) {
         if (!tile_ok(i)) continue;                        // workgroup-uniform
         const uint32_t t = blockIdx.x + i * gridDim.x;
         if (i) __syncthreads();                           // the previous tile's sums are read
@@ -416,8 +429,9 @@ uint32_t dec_tpw(uint32_t T) {
 }
 
 template <int MG>
-void launch_dec(const DecArgs &a, uint32_t G, uint32_t S, hipStream_t s) {
-    hipLaunchKernelGGL(gemv_mfma_kernel<MG>, dim3(G, S), dim3(kDecThreads), 0, s, a);
+void launch_dec(const DecArgs &a, uint32_t G, uint32_t S, bool roll, hipStream_t s) {
+    if (roll) hipLaunchKernelGGL((gemv_mfma_kernel<MG, true>), dim3(G, S), dim3(kDecThreads), 0, s, a);
+    else hipLaunchKernelGGL((gemv_mfma_kernel<MG, false>), dim3(G, S), dim3(kDecThreads), 0, s, a);
 }
 
 }  // namespace
@@ -457,8 +471,12 @@ ht_status run_dec(const ht_packed_weight *w, const uint16_t *x, int64_t M, int64
             a.y = yo;
             a.ybf = yb;
         }
-        if (Mt <= 16) launch_dec<1>(a, G, d.S, s);
-        else launch_dec<2>(a, G, d.S, s);
+        // more than one (round, tile) step per workgroup: several tiles, or
+        // a K range longer than one round (64 K-blocks at MG = 1, 32 at 2)
+        const uint32_t ck = Mt <= 16 ? kDecChunk : kDecChunk / 2;
+        const bool roll = a.TPW > 1 || d.KBs > ck;
+        if (Mt <= 16) launch_dec<1>(a, G, d.S, roll, s);
+        else launch_dec<2>(a, G, d.S, roll, s);
         HT_LAUNCH_CHECK();
         if (d.S > 1) {
             const ht_status st = launch_split_reduce(static_cast<const float *>(ws), d.S, uint32_t(Mt), a.w.N, yo,
