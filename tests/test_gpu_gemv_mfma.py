@@ -177,3 +177,17 @@ def test_dec_random_shapes(orc, seed):
     x = wl.to_bf16_bits(rng.normal(size=(M, 64 * KB)).astype(np.float32))
     y_or = orc.linear(W, fmt, x)
     check_close(run_dec(W, fmt, x, act=act), relu(y_or) if act else y_or, f"N={N} KB={KB} M={M} act={act}")
+
+
+@pytest.mark.parametrize("N,K,M", [(5632, 2048, 16), (5632, 2048, 24), (4112, 1024, 9), (4112, 4160, 20)])
+def test_dec_several_tiles_per_workgroup(orc, N, K, M):
+    """More row tiles than compute units: 352 tiles (TinyLlama-shaped gate,
+    two tiles per workgroup) and 257 tiles (two per workgroup, the last
+    workgroup with one), over one round and over several rounds of K
+    (4160 = 65 K-blocks: a second round of one K-block), with the column
+    refills between tiles and rounds."""
+    rng = np.random.default_rng(N + K + M)
+    W = (rng.standard_t(4, size=(N, K)) * 0.02).astype(np.float32)
+    fmt = rng.integers(0, 5, size=(N, K // 64)).astype(np.uint8)
+    x = wl.to_bf16_bits(rng.normal(size=(M, K)).astype(np.float32))
+    check_close(run_dec(W, fmt, x), orc.linear(W, fmt, x), f"N={N} K={K} M={M}")
