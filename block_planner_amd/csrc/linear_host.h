@@ -39,11 +39,11 @@ ht_status run_dec(const ht_packed_weight *w, const uint16_t *x, int64_t M, int64
                   int64_t ldy, int act, void *ws, hipStream_t s);
 
 // The path HT_PATH_AUTO resolves to for one linear over M rows: the MFMA
-// decode path for 5..32 rows (row tile 16), otherwise the LDS-staged MFMA path
-// from 16 rows and the register path below (1..4 rows stay on the register
-// path, which the single-launch MLP shares).
+// decode path for 4..32 rows (row tile 16), otherwise the LDS-staged MFMA path
+// from 16 rows and the register path below (1 to 3 rows stay on the register
+// path, fastest there; from 4 rows its fp32 copy of x needs a K-split).
 inline int32_t auto_linear_path(const ht_packed_weight *w, int64_t M) {
-    if (M >= 5 && M <= 32 && w->row_tile == 16) return HT_PATH_GEMV_MFMA;
+    if (M >= 4 && M <= 32 && w->row_tile == 16) return HT_PATH_GEMV_MFMA;
     return M >= 16 ? HT_PATH_GEMM : HT_PATH_GEMV;
 }
 

@@ -188,7 +188,7 @@ ht_status ht_linear_workspace(const ht_packed_weight *w, int64_t M, int32_t path
  *          (row tile 16 only, else HT_EINVAL): each block is dequantised
  *          in registers straight into the operands of bf16 MFMAs (the same
  *          bfloat16 planes as HT_PATH_GEMM), 32 rows of x per launch;
- *          HT_PATH_AUTO: GEMV_MFMA for 5 <= M <= 32 with row tile 16;
+ *          HT_PATH_AUTO: GEMV_MFMA for 4 <= M <= 32 with row tile 16;
  *          otherwise GEMM when M >= 16, else GEMV.
  *   ws     workspace of ws_bytes >= ht_linear_workspace(w, M, path): K-split
  *          partial sums, added in split order by a second kernel. */
@@ -210,8 +210,10 @@ ht_status ht_workspace_init(void *ws, size_t ws_bytes, ht_stream stream);
 /* ht_mlp_forward -- the page's BenchmarkMLP ("Usage Example": HyperLinear then
  * ReLU, repeated; no bias):  h_0 = x;  h_l = bf16_rne(relu(h_{l-1} . W_l^T))
  * for l < L;  y = relu(h_{L-1} . W_L^T) in fp32.  Each layer computes exactly
- * what ht_linear_forward computes (the same fixed-order sums), whichever path
- * runs.
+ * what ht_linear_forward computes on the matching path (the same fixed-order
+ * sums): the single launch what HT_PATH_GEMV computes, a per-layer launch
+ * what its path computes (for HT_PATH_AUTO, the path a single linear of M
+ * rows takes).
  *   layers    (host) array of n_layers descriptors; layer l's K must equal
  *             layer l-1's N; hidden widths must be multiples of 8.
  *   x         bfloat16 [M, ldx];  y fp32 [M, ldy] (ldy >= last layer's N).

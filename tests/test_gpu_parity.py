@@ -225,10 +225,10 @@ def run_linear(W, fmt, xbits, R=16, act=0, ldx_pad=0, ldy_pad=0, path=B.HT_PATH_
 
 
 @pytest.mark.parametrize("path", [B.HT_PATH_GEMV, B.HT_PATH_AUTO])
-@pytest.mark.parametrize("M", [1, 2, 5, 8, 13])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 13])
 def test_linear_small_weight(orc, M, path):
     """The register path at 1 to 13 rows (up to 8 rows per launch, so 13 is
-    two launches), and what AUTO picks (the MFMA decode path from 5 rows)."""
+    two launches), and what AUTO picks (the MFMA decode path from 4 rows)."""
     W = wl.small_weight()
     fmt = orc.plan(W)
     x = wl.to_bf16_bits(wl.small_activation(m=M))
