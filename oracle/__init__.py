@@ -76,6 +76,8 @@ def _load():
     lib.oracle_linear_sampled.argtypes = [P, I64, I64, P, P, I64, P, P, I64, P]
     lib.oracle_relu_bf16.restype = None
     lib.oracle_relu_bf16.argtypes = [P, I64, P]
+    lib.oracle_x_planes.restype = None
+    lib.oracle_x_planes.argtypes = [P, I64, I64, I64, P, P, P]
     lib.oracle_pack_layout.restype = I64
     lib.oracle_pack_layout.argtypes = [I64, I64, I64, P, P]
     lib.oracle_pack.restype = None
@@ -230,6 +232,38 @@ def mlp(weights, fmts, x_bf16: np.ndarray):
         else:
             return np.maximum(z, 0.0), hs
     raise ValueError("no layers")
+
+
+# --- integer encoding of x (int8 matrix-core path) -------------------------
+XEXP_NONFINITE = -1000
+
+
+def x_planes(x_bf16: np.ndarray):
+    """(hi, lo, sexp): x[m, k] ~ (256 * hi + lo) * 2^sexp[m], two int8 planes
+    per token (the encoding's definition is in ht_oracle.c)."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    assert x.ndim == 2
+    M, K = x.shape
+    hi = np.zeros((M, K), np.int8)
+    lo = np.zeros((M, K), np.int8)
+    sexp = np.zeros(M, np.int32)
+    _load().oracle_x_planes(_ptr(x), M, K, K, _ptr(hi), _ptr(lo), _ptr(sexp))
+    return hi, lo, sexp
+
+
+def x_hat(hi: np.ndarray, lo: np.ndarray, sexp: np.ndarray) -> np.ndarray:
+    """The encoded x in double; rows marked non-finite are NaN."""
+    v = 256.0 * hi.astype(np.float64) + lo.astype(np.float64)
+    ok = sexp != XEXP_NONFINITE
+    out = np.ldexp(v, np.where(ok, sexp, 0)[:, None])
+    out[~ok] = np.nan
+    return out
+
+
+def linear_xplanes(W: np.ndarray, fmt: np.ndarray, x_bf16: np.ndarray) -> np.ndarray:
+    """y [M, N] (double) = x_hat . W_hat^T with x_hat the two-plane encoding of
+    x: what the int8 matrix-core path computes, before fp32 rounding."""
+    return x_hat(*x_planes(x_bf16)) @ dequant(W, fmt).T
 
 
 def pack_layout(N: int, K: int, R: int, counts) -> tuple[int, list[int]]:

@@ -326,6 +326,53 @@ void oracle_relu_bf16(const double *z, int64_t count, uint16_t *h)
 }
 
 /* ------------------------------------------------------------------------ */
+/* Integer encoding of x for the int8 matrix-core path.  The block planner's */
+/* page fixes no encoding of activations for integer arithmetic; the only    */
+/* integer cast of activations the pages show (HyperQuant page,              */
+/* convert_linears, the int8 LatticeLinear path, another method) is a       */
+/* per-token row-absmax int8 cast.  Reading used here, that cast widened to  */
+/* two int8 planes:                                                          */
+/*   per token (row) m, amax = max_k |x[m,k]| = f * 2^E with f in [0.5, 1);  */
+/*   v = round_half_even(x * 2^(14-E)), so |v| <= 2^14 (exact: a power-of-   */
+/*       two scaling of a bfloat16 value, rounded once);                     */
+/*   hi = floor((v + 128) / 256) in [-64, 64], lo = v - 256*hi in [-128,127];*/
+/*   x_hat = v * 2^(E-14), within 2^(E-15) <= amax * 2^-14 of x.             */
+/* An all-zero row has v = 0 and exponent 0.  A row holding an Inf or NaN    */
+/* gets the exponent OR_XEXP_NONFINITE and zero planes (its outputs are NaN).*/
+/* hi, lo: int8 [M][K]; sexp: int32 [M], the exponent E - 14 of x_hat.       */
+/* ------------------------------------------------------------------------ */
+#define OR_XEXP_NONFINITE (-1000)
+
+void oracle_x_planes(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                     int8_t *hi, int8_t *lo, int32_t *sexp)
+{
+    for (int64_t m = 0; m < M; ++m) {
+        double amax = 0.0;
+        int finite = 1;
+        for (int64_t k = 0; k < K; ++k) {
+            double v = bf16_widen(x[m * ldx + k]);
+            if (!isfinite(v)) finite = 0;
+            else if (fabs(v) > amax) amax = fabs(v);
+        }
+        if (!finite) {
+            sexp[m] = OR_XEXP_NONFINITE;
+            for (int64_t k = 0; k < K; ++k) hi[m * K + k] = lo[m * K + k] = 0;
+            continue;
+        }
+        int E = 0;
+        if (amax > 0.0) frexp(amax, &E);
+        sexp[m] = amax > 0.0 ? E - 14 : 0;
+        for (int64_t k = 0; k < K; ++k) {
+            double v = rint(ldexp(bf16_widen(x[m * ldx + k]), 14 - E));
+            int32_t iv = (int32_t)v;
+            int32_t h = (int32_t)floor((iv + 128) / 256.0);
+            hi[m * K + k] = (int8_t)h;
+            lo[m * K + k] = (int8_t)(iv - 256 * h);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Execution buffers: the packed layout (version 1), written out directly    */
 /* from its specification.                                                   */
 /*                                                                           */

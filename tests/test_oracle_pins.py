@@ -512,3 +512,112 @@ def test_mlp_composes_layers(orc):
             np.testing.assert_array_equal(h, hs[li])
         else:
             np.testing.assert_allclose(y, np.maximum(z, 0), rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Two-plane int8 encoding of x (int8 matrix-core path)
+# ---------------------------------------------------------------------------
+def _bf16_row(vals):
+    return wl.to_bf16_bits(np.array([float(v) for v in vals], np.float32))
+
+
+def test_x_planes_golden_rows():
+    """Hand-worked rows (tests/golden/x_planes.json): catches a wrong exponent
+    (off by one at powers of two), a wrong rounding mode (the ties), a hi/lo
+    split that truncates instead of flooring (negative entries) and the
+    all-zero / non-finite / subnormal special cases."""
+    import json
+    import os
+    import oracle
+
+    data = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "x_planes.json")))
+    for row in data["rows"]:
+        xb = _bf16_row(row["x"])[None, :]
+        assert np.array_equal(wl.bf16_bits_to_f32(xb[0]).astype(np.float64),
+                              np.array([float(v) for v in row["x"]])), row["name"]   # inputs are exact bf16
+        hi, lo, se = oracle.x_planes(xb)
+        assert hi[0].tolist() == row["hi"], row["name"]
+        assert lo[0].tolist() == row["lo"], row["name"]
+        assert int(se[0]) == row["sexp"], row["name"]
+
+
+def test_x_planes_properties_random():
+    """Properties that fix the encoding on random rows over a wide range of
+    magnitudes: the exponent brackets amax (2^(E-1) <= amax < 2^E), v is the
+    nearest integer to x * 2^(14-E) with ties to even (checked in exact
+    rational arithmetic on a sample), the planes stay in range and combine to
+    v, and every entry with |x| >= 2^(E-7) is reproduced exactly."""
+    import oracle
+
+    rng = np.random.default_rng(5)
+    rows = []
+    for scale in (1e-38, 3e-20, 1e-3, 1.0, 7.0, 1e5, 1e30):
+        rows.append(rng.standard_t(3, size=192) * scale)
+    X = wl.to_bf16_bits(np.array(rows, np.float32))
+    hi, lo, se = oracle.x_planes(X)
+    xf = wl.bf16_bits_to_f32(X).astype(np.float64)
+    assert hi.min() >= -64 and hi.max() <= 64 and lo.min() >= -128 and lo.max() <= 127
+    v = 256 * hi.astype(np.int64) + lo.astype(np.int64)
+    for m in range(X.shape[0]):
+        amax = np.max(np.abs(xf[m]))
+        E = int(se[m]) + 14
+        assert 2.0 ** (E - 1) <= amax < 2.0 ** E
+        xh = np.ldexp(v[m].astype(np.float64), int(se[m]))
+        assert np.all(np.abs(xh - xf[m]) <= np.ldexp(0.5, int(se[m])))
+        big = np.abs(xf[m]) >= 2.0 ** (E - 7)
+        assert np.array_equal(xh[big], xf[m][big])
+        for k in range(0, 192, 7):   # exact nearest-even check
+            t = Fraction(float(xf[m, k])) * Fraction(2) ** (14 - E)
+            fl = t.numerator // t.denominator
+            d = t - fl
+            want = fl + 1 if d > Fraction(1, 2) or (d == Fraction(1, 2) and fl % 2) else fl
+            assert int(v[m, k]) == want, (m, k)
+
+
+
+def test_x_planes_scale_and_sign_symmetry():
+    """x * 2^j keeps v and moves the exponent by j; -x negates v (round half
+    even is symmetric).  Catches an encoding that depends on more than the
+    row's exponent, or a floor where a round belongs."""
+    import oracle
+
+    rng = np.random.default_rng(6)
+    x = rng.normal(size=(3, 128)).astype(np.float32)
+    X = wl.to_bf16_bits(x)
+    base = wl.bf16_bits_to_f32(X)
+    hi, lo, se = oracle.x_planes(X)
+    v = 256 * hi.astype(np.int64) + lo
+    for j in (-20, -1, 3, 40):
+        h2, l2, s2 = oracle.x_planes(wl.to_bf16_bits(base * np.float32(2.0 ** j)))
+        assert np.array_equal(256 * h2.astype(np.int64) + l2, v)
+        assert np.array_equal(s2, se + j)
+    h3, l3, s3 = oracle.x_planes(wl.to_bf16_bits(-base))
+    assert np.array_equal(256 * h3.astype(np.int64) + l3, -v)
+    assert np.array_equal(s3, se)
+
+
+def test_linear_xplanes_exact_and_bounded():
+    """x_hat . W_hat^T equals the exact linear when every x is representable
+    (all |x| >= 2^(E-7)), and otherwise differs by at most
+    2^(sexp-1) * sum_k |w_hat[n, k]| per output.  Catches a transposed or
+    mis-scaled x_hat in the oracle of the int8 path."""
+    import oracle
+
+    rng = np.random.default_rng(7)
+    W = (rng.normal(size=(48, 256)) * 0.02).astype(np.float32)
+    fmt = oracle.plan(W)
+    # representable: entries in {+-1, +-1.5, +-2, ..., +-4}: |x| >= 1 >= 2^(E-7) with E = 3
+    xr = rng.choice(np.array([-4, -3, -2, -1.5, -1, 1, 1.5, 2, 3, 4], np.float32), size=(5, 256))
+    Xr = wl.to_bf16_bits(xr)
+    assert np.allclose(oracle.linear_xplanes(W, fmt, Xr), oracle.linear(W, fmt, Xr), rtol=1e-13, atol=1e-13)
+    X = wl.to_bf16_bits(rng.normal(size=(6, 256)).astype(np.float32) * np.float32(3.0))
+    yx = oracle.linear_xplanes(W, fmt, X)
+    y = oracle.linear(W, fmt, X)
+    _, _, se = oracle.x_planes(X)
+    bound = np.ldexp(0.5, se)[:, None] * np.abs(oracle.dequant(W, fmt)).sum(axis=1)[None, :]
+    assert np.all(np.abs(yx - y) <= bound * (1 + 1e-12))
+    assert np.max(np.abs(yx - y)) > 0          # the encoding is not the identity here
+    Xn = X.copy()
+    Xn[2, 5] = 0x7F80                          # +Inf in row 2
+    yn = oracle.linear_xplanes(W, fmt, Xn)
+    assert np.all(np.isnan(yn[2])) and np.all(np.isfinite(np.delete(yn, 2, axis=0)))
