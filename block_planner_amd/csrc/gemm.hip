@@ -24,7 +24,7 @@
 // from memory into LDS (global_load_lds) two steps ahead; four waves load
 // the packed blocks two steps ahead into registers and dequantise the next
 // step's into the other LDS stage.  One barrier per step.
-#include "gemv_common.h"
+#include "int8_tile.h"
 #include "linear_host.h"
 
 namespace ht {
@@ -47,6 +47,7 @@ struct GemmArgs {
     uint32_t M;
     uint32_t KBs;             // K-blocks per split
     uint32_t MT, NT;          // row tiles of x, column tiles of the weight
+    uint32_t skip_int8;       // leave all-INT8 column tiles to the int8 matrix-core kernel
     int act;
 };
 
@@ -103,6 +104,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
     const uint32_t KB = w.KB, R = w.R;
     const uint32_t kb0 = zs * a.KBs, kb1 = min(KB, kb0 + a.KBs);   // this split's K-blocks (non-empty)
     const uint32_t nsteps = kb1 - kb0;
+    if (a.skip_int8 && int8_tile(w, n0 / kI8TileRows, kb0, kb1)) return;   // the whole workgroup
 
     if (wave < 4) {
         // ================= MFMA waves =================
@@ -459,6 +461,34 @@ uint32_t gemm_splits(const ht_packed_weight *w, int64_t M) {
 
 }  // namespace
 
+uint32_t gemm_split_count(const ht_packed_weight *w, int64_t Mt) { return gemm_splits(w, Mt); }
+
+ht_status gemm_tiles(const ht_packed_weight *w, const uint16_t *x, int64_t Mt, int64_t ldx, float *y, uint16_t *ybf,
+                     int64_t ldy, int act, float *partial, uint32_t S, bool skip_int8, hipStream_t s) {
+    GemmArgs a;
+    a.w = layer_dev(w);
+    a.x = x;
+    a.ldx = ldx;
+    a.y = S > 1 ? nullptr : y;
+    a.ybf = S > 1 ? nullptr : ybf;
+    a.partial = S > 1 ? partial : nullptr;
+    a.ldy = ldy;
+    a.act = act;
+    a.M = uint32_t(Mt);
+    a.KBs = (a.w.KB + S - 1) / S;
+    const uint32_t BM = gemm_bm(Mt);
+    a.MT = uint32_t((Mt + BM - 1) / BM);
+    a.NT = uint32_t((a.w.N + kGemmBN - 1) / kGemmBN);
+    a.skip_int8 = skip_int8 ? 1u : 0u;
+    switch (BM) {
+    case 256: launch_gemm<4>(a, S, s); break;
+    case 128: launch_gemm<2>(a, S, s); break;
+    default: launch_gemm<1>(a, S, s); break;
+    }
+    HT_LAUNCH_CHECK();
+    return HT_OK;
+}
+
 size_t gemm_ws(const ht_packed_weight *w, int64_t M) {
     const int64_t Mt = M < kGemmChunkRows ? M : kGemmChunkRows;
     const uint32_t S = gemm_splits(w, Mt);
@@ -467,32 +497,16 @@ size_t gemm_ws(const ht_packed_weight *w, int64_t M) {
 
 ht_status run_gemm(const ht_packed_weight *w, const uint16_t *x, int64_t M, int64_t ldx, float *y, uint16_t *ybf,
                    int64_t ldy, int act, void *ws, hipStream_t s) {
-    GemmArgs a;
-    a.w = layer_dev(w);
-    a.ldx = ldx;
-    a.ldy = ldy;
-    a.act = act;
     for (int64_t m0 = 0; m0 < M; m0 += kGemmChunkRows) {
         const int64_t Mt = M - m0 < kGemmChunkRows ? M - m0 : kGemmChunkRows;
         const uint32_t S = gemm_splits(w, Mt);
-        const uint32_t BM = gemm_bm(Mt);
-        a.x = x + m0 * ldx;
-        a.y = y ? y + m0 * ldy : nullptr;
-        a.ybf = ybf ? ybf + m0 * ldy : nullptr;
-        a.partial = S > 1 ? static_cast<float *>(ws) : nullptr;
-        a.M = uint32_t(Mt);
-        a.KBs = (a.w.KB + S - 1) / S;
-        a.MT = uint32_t((Mt + BM - 1) / BM);
-        a.NT = uint32_t((a.w.N + kGemmBN - 1) / kGemmBN);
-        switch (BM) {
-        case 256: launch_gemm<4>(a, S, s); break;
-        case 128: launch_gemm<2>(a, S, s); break;
-        default: launch_gemm<1>(a, S, s); break;
-        }
-        HT_LAUNCH_CHECK();
+        float *yc = y ? y + m0 * ldy : nullptr;
+        uint16_t *ybc = ybf ? ybf + m0 * ldy : nullptr;
+        ht_status st = gemm_tiles(w, x + m0 * ldx, Mt, ldx, yc, ybc, ldy, act, static_cast<float *>(ws), S, false, s);
+        if (st != HT_OK) return st;
         if (S > 1) {
-            const ht_status st = launch_split_reduce(static_cast<const float *>(ws), S, uint32_t(Mt), a.w.N, a.y,
-                                                     a.ybf, ldy, act, s);
+            st = launch_split_reduce(static_cast<const float *>(ws), S, uint32_t(Mt), uint32_t(w->N), yc, ybc, ldy,
+                                     act, s);
             if (st != HT_OK) return st;
         }
     }

@@ -26,6 +26,23 @@ size_t gemm_ws(const ht_packed_weight *w, int64_t M);
 ht_status run_gemm(const ht_packed_weight *w, const uint16_t *x, int64_t M, int64_t ldx, float *y, uint16_t *ybf,
                    int64_t ldy, int act, void *ws, hipStream_t s);
 
+// The MFMA path's K-splits for Mt rows (one launch), and its main kernel
+// alone over Mt rows: with S > 1 it writes partial[S][Mt][N] (for
+// launch_split_reduce), else y or ybf; skip_int8 leaves the column tiles that
+// are all INT8 over a split to the int8 matrix-core kernel.
+uint32_t gemm_split_count(const ht_packed_weight *w, int64_t Mt);
+ht_status gemm_tiles(const ht_packed_weight *w, const uint16_t *x, int64_t Mt, int64_t ldx, float *y, uint16_t *ybf,
+                     int64_t ldy, int act, float *partial, uint32_t S, bool skip_int8, hipStream_t s);
+
+// The int8 matrix-core path (row tile 16 only): whether it takes this weight,
+// its workspace bytes for M rows (x's int8 planes and row scales, K-split
+// partials), and one linear on it (fp32 y or bfloat16 ybf; arguments assumed
+// checked).
+bool i8_ok(const ht_packed_weight *w);
+size_t i8_ws(const ht_packed_weight *w, int64_t M);
+ht_status run_gemm_i8(const ht_packed_weight *w, const uint16_t *x, int64_t M, int64_t ldx, float *y, uint16_t *ybf,
+                      int64_t ldy, int act, void *ws, hipStream_t s);
+
 // y[m, n] = act(sum over s in order of partial[s][m][n]), fp32 y or bfloat16 ybf.
 ht_status launch_split_reduce(const float *partial, uint32_t S, uint32_t M, uint32_t N, float *y, uint16_t *ybf,
                               int64_t ldy, int act, hipStream_t s);

@@ -113,7 +113,8 @@ enum {
     HT_PATH_GEMV = 1,   /* one fused GEMV launch per layer                          */
     HT_PATH_FUSED = 2,  /* ht_mlp_forward only: all layers in one persistent launch */
     HT_PATH_GEMM = 3,   /* ht_linear_forward only: LDS dequantisation + bf16 MFMA   */
-    HT_PATH_GEMV_MFMA = 4 /* ht_linear_forward only: register dequantisation + bf16 MFMA (row tile 16) */
+    HT_PATH_GEMV_MFMA = 4, /* ht_linear_forward only: register dequantisation + bf16 MFMA (row tile 16) */
+    HT_PATH_GEMM_I8 = 5    /* ht_linear_forward only: int8 MFMA for all-INT8 tiles, else as GEMM (row tile 16) */
 };
 
 /* Human-readable name of a status code (static storage; never NULL). */
@@ -164,8 +165,9 @@ ht_status ht_pack(const float *W, int64_t N, int64_t K, int64_t ldw,
                   void *buf, size_t buf_bytes, ht_packed_weight *desc, ht_stream stream);
 
 /* ht_linear_workspace -- workspace bytes ht_linear_forward needs for M rows
- * on `path` (HT_PATH_AUTO, HT_PATH_GEMV, HT_PATH_GEMM or HT_PATH_GEMV_MFMA;
- * HT_EINVAL for HT_PATH_GEMV_MFMA with a row tile other than 16). */
+ * on `path` (HT_PATH_AUTO, HT_PATH_GEMV, HT_PATH_GEMM, HT_PATH_GEMV_MFMA or
+ * HT_PATH_GEMM_I8; HT_EINVAL for HT_PATH_GEMV_MFMA and HT_PATH_GEMM_I8 with a
+ * row tile other than 16). */
 ht_status ht_linear_workspace(const ht_packed_weight *w, int64_t M, int32_t path,
                               size_t *bytes);
 
@@ -188,6 +190,17 @@ ht_status ht_linear_workspace(const ht_packed_weight *w, int64_t M, int32_t path
  *          (row tile 16 only, else HT_EINVAL): each block is dequantised
  *          in registers straight into the operands of bf16 MFMAs (the same
  *          bfloat16 planes as HT_PATH_GEMM), 32 rows of x per launch;
+ *          HT_PATH_GEMM_I8: for prefill with INT8-heavy plans (row tile 16
+ *          only, else HT_EINVAL): a 64-column weight tile whose blocks are
+ *          all INT8 over the K range of a split runs on the int8 matrix
+ *          cores, every other tile exactly as HT_PATH_GEMM.  The page fixes
+ *          no integer encoding of x; here each row m of x is encoded as
+ *          x_hat = (256 hi + lo) 2^(E-14) with int8 planes hi, lo,
+ *          round-half-even, 2^(E-1) <= max_k |x[m,k]| < 2^E, so
+ *          |x_hat - x| <= 2^-14 max_k |x[m,k]|; such a tile computes
+ *          x_hat . W_hat^T with exact int32 block sums (a row holding Inf or
+ *          NaN gives NaN there).  The workspace holds the encoded x;
+ *          HT_PATH_AUTO never picks this path;
  *          HT_PATH_AUTO: GEMV_MFMA for 4 <= M <= 32 with row tile 16;
  *          otherwise GEMM when M >= 16, else GEMV.
  *   ws     workspace of ws_bytes >= ht_linear_workspace(w, M, path): K-split

@@ -136,10 +136,42 @@ def test_linear_argument_checks():
         with pytest.raises(B.HTError):
             B.ht_linear_workspace(_desc(N=256, K=4096, R=R), 8, B.HT_PATH_GEMV_MFMA)
         assert f(ctypes.byref(_desc(R=R)), x, 8, 256, y, 256, 0, B.HT_PATH_GEMV_MFMA, None, 0, None) == 1
+    wide = _desc(N=16384, K=4096, R=16)
+    # the int8 matrix-core path, 8192 rows per launch (sized for 8192 at most),
+    # decided by the weight's INT8 count: none (too few for any 256-row tile)
+    # -> exactly the MFMA path's workspace; mixed -> x's two int8 planes
+    # (2 bytes per entry, rows in groups of 16) and 16 fp32 row scales per
+    # group, each region 256-byte aligned, then the MFMA path's partials; all
+    # INT8 -> planes, scales and partials for the int8 kernel's own K-splits
+    # (128 x 256 tiles, split when fewer than 192, at least 8 K-blocks each)
+    def a256(v):
+        return (v + 255) // 256 * 256
+    for dsc, M in ((wide, 2048), (wide, 20000), (big, 1), (big, 33)):
+        Mt = min(M, 8192)
+        G, KB = (Mt + 15) // 16, dsc.K // 64
+        extra = a256(G * KB * 2048) + a256(G * 16 * 4)
+        dsc.counts[1] = 0
+        assert B.ht_linear_workspace(dsc, M, B.HT_PATH_GEMM_I8) == B.ht_linear_workspace(dsc, Mt, B.HT_PATH_GEMM)
+        dsc.counts[1] = dsc.N * KB - 1
+        assert B.ht_linear_workspace(dsc, M, B.HT_PATH_GEMM_I8) == extra + B.ht_linear_workspace(dsc, Mt, B.HT_PATH_GEMM)
+        dsc.counts[1] = dsc.N * KB
+        tiles = (Mt + 127) // 128 * ((dsc.N + 255) // 256)
+        S = 1
+        if tiles * 4 < 3 * 256 and KB >= 16:
+            S = min(-(-256 // tiles), KB // 8)
+            KBs = -(-KB // S)
+            S = -(-KB // KBs)
+        assert B.ht_linear_workspace(dsc, M, B.HT_PATH_GEMM_I8) == extra + (S * Mt * dsc.N * 4 if S > 1 else 0)
+        dsc.counts[1] = 0
+    for R in (1, 2, 4, 8):
+        with pytest.raises(B.HTError):
+            B.ht_linear_workspace(_desc(N=256, K=4096, R=R), 64, B.HT_PATH_GEMM_I8)
+        assert f(ctypes.byref(_desc(R=R)), x, 64, 256, y, 256, 0, B.HT_PATH_GEMM_I8, None, 0, None) == 1
+    with pytest.raises(B.HTError):
+        B.ht_linear_workspace(big, 1, 6)                                        # no such path
     # AUTO on a row tile other than 16 keeps to the other two paths
     assert B.ht_linear_workspace(_desc(N=256, K=64 * 1024, R=8), 8, B.HT_PATH_AUTO) == \
         B.ht_linear_workspace(_desc(N=256, K=64 * 1024, R=8), 8, B.HT_PATH_GEMV)
-    wide = _desc(N=16384, K=4096, R=16)
     assert B.ht_linear_workspace(wide, 2048, B.HT_PATH_GEMM) == 0                 # 4096 tiles: no split
     with pytest.raises(B.HTError):
         B.ht_linear_workspace(big, 1, B.HT_PATH_FUSED)                        # MLP-only path
