@@ -81,7 +81,7 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=6)
     ap.add_argument("--cpu-steps", type=int, default=20, help="oracle MLP forwards timed for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "gemv", "mlp", "gemm", "decode"], default="all",
+    ap.add_argument("--only", choices=["all", "gemv", "mlp", "gemm", "decode", "i8"], default="all",
                     help="'gemv' / 'mlp' / 'gemm' / 'decode': only that timing leg (for profiler runs)")
     ap.add_argument("--no-gemm", action="store_true", help="skip the prefill GEMM leg")
     args = ap.parse_args()
@@ -145,8 +145,51 @@ def main() -> int:
             torch.cuda.empty_cache()
         return {"kernel": "gemm_kernel<4>", "peak_TFLOPs": 2500.0, "shapes": out}
 
+    def i8_leg():
+        """The int8 matrix-core path (HT_PATH_GEMM_I8) against the MFMA path
+        at M = 2048 on the same Llama-8B shapes: once on weights forced to
+        INT8 everywhere (every 256-column tile takes the int8 kernel) and
+        once on the planned weights (no tile is all INT8: the path adds the
+        encoding of x and an empty int8 launch).  TFLOP/s of 2*M*N*K; the
+        int8 kernel's fraction is of the 5.0 POP/s dense int8 MFMA peak (it
+        issues two int8 MFMAs per product, one per plane of x)."""
+        out = {}
+        M = 2048
+        for name in ("q", "gate", "down"):
+            shp = [t for t in wl.llama8b_shapes() if t.name == name][0]
+            W = torch.from_numpy(wl.llama8b_weight(0, shp)).to(dev)
+            xg = torch.from_numpy(wl.to_bf16_bits(wl.activation("llama8b", M, shp.k)).view(np.int16)).to(dev)
+            xg = xg.view(torch.bfloat16)
+            yg = torch.empty((M, shp.n), dtype=torch.float32, device=dev)
+            fl = 2.0 * M * shp.n * shp.k
+            row = {}
+            for kind in ("all_int8", "planned"):
+                fmt = (torch.full((shp.n, shp.k // 64), 1, dtype=torch.uint8, device=dev) if kind == "all_int8"
+                       else api.plan(W))
+                pw = api.pack(W, fmt)
+                r = {}
+                for pname, path in (("GEMM", B.HT_PATH_GEMM), ("GEMM_I8", B.HT_PATH_GEMM_I8)):
+                    ws = api.workspace(B.ht_linear_workspace(pw.desc, M, path), dev)
+                    for _ in range(2):
+                        api.linear(pw, xg, out=yg, ws=ws, path=path)
+                    t = timed(lambda i: api.linear(pw, xg, out=yg, ws=ws, path=path), 10)
+                    r[pname + "_us"] = round(t * 1e6, 1)
+                    r[pname + "_TFLOPs"] = round(fl / t / 1e12, 1)
+                    del ws
+                r["speedup"] = round(r["GEMM_us"] / r["GEMM_I8_us"], 3)
+                row[kind] = r
+                del pw
+            row["all_int8"]["int8_peak_frac"] = round(fl / (row["all_int8"]["GEMM_I8_us"] * 1e-6) / 5.0e15, 4)
+            out[name] = row
+            del W, xg, yg
+            torch.cuda.empty_cache()
+        return {"kernel": "gemm_i8_kernel + xq_kernel", "peak_int8_TOPs": 5000.0, "M": M, "shapes": out}
+
     if args.only == "gemm":
         print(json.dumps(gemm_leg()))
+        return 0
+    if args.only == "i8":
+        print(json.dumps(i8_leg()))
         return 0
 
     log("generating weights")
@@ -296,6 +339,8 @@ def main() -> int:
         del copies, arrays, descs
         torch.cuda.empty_cache()
         gemm = gemm_leg()
+        log("int8 matrix-core path (Llama-8B shapes, M = 2048)")
+        gemm["int8_path"] = i8_leg()
 
     # ---- CPU baseline: the oracle as it stands ----------------------------
     cpu = None
