@@ -81,7 +81,7 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=6)
     ap.add_argument("--cpu-steps", type=int, default=20, help="oracle MLP forwards timed for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "gemv", "mlp", "gemm", "decode", "i8"], default="all",
+    ap.add_argument("--only", choices=["all", "gemv", "mlp", "gemm", "decode", "i8", "configs"], default="all",
                     help="'gemv' / 'mlp' / 'gemm' / 'decode': only that timing leg (for profiler runs)")
     ap.add_argument("--no-gemm", action="store_true", help="skip the prefill GEMM leg")
     args = ap.parse_args()
@@ -185,6 +185,116 @@ def main() -> int:
             torch.cuda.empty_cache()
         return {"kernel": "gemm_i8_kernel + xq_kernel", "peak_int8_TOPs": 5000.0, "M": M, "shapes": out}
 
+    def configs_leg():
+        """The transformer-shaped configurations, on seeded device-drawn
+        weights (workloads.*_weight_gpu):
+          * TinyLlama-1.1B shapes (22 layers x 7 linears = 154): decode at
+            batch 1 over all of them, back to back;
+          * Llama-3.1-8B shapes (32 x 7 = 224 linears, 7.0e9 parameters):
+            the planner and packer streamed layer by layer over the whole set
+            for eps_int4 in {0.04, 0.08, 0.16} and forced all-INT4 / all-INT8
+            plans (kernel time from events around each call), then decode at
+            batch 1, 4 and 16 over all 224 linears packed at the default eps.
+        Each decode pass is one HIP graph of every linear in order (AUTO
+        path, each with its own input and output), replayed; GB/s counts the
+        packed bytes plus activations and outputs."""
+        res = {}
+
+        def decode_pass(pws, M, reps):
+            xs, ys, wss = [], [], []
+            for pw in pws:
+                xs.append(torch.randn(M, pw.K, device=dev).to(torch.bfloat16))
+                ys.append(torch.empty(M, pw.N, dtype=torch.float32, device=dev))
+                wss.append(api.workspace(B.ht_linear_workspace(pw.desc, M, B.HT_PATH_AUTO), dev))
+
+            def run_all():   # on the current stream (the capture stream inside the graph)
+                for pw, xg, yg, ws in zip(pws, xs, ys, wss):
+                    api.linear(pw, xg, out=yg, ws=ws)
+            run_all()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run_all()
+            g.replay()
+            torch.cuda.synchronize()
+            t = timed(lambda i: g.replay(), reps)
+            nbytes = sum(pw.nbytes + 2 * M * pw.K + 4 * M * pw.N for pw in pws)
+            del g, xs, ys, wss
+            return {"M": M, "linears": len(pws), "us_per_pass": round(t * 1e6, 1),
+                    "GBps": round(nbytes / t / 1e9, 1), "pct_hbm_peak": round(100 * nbytes / t / 1e9 / HBM_PEAK_GBS, 2),
+                    "bytes_per_pass": int(nbytes)}
+
+        # TinyLlama: decode at batch 1 over the 154 linears
+        log("configs: TinyLlama stack")
+        pws = []
+        for layer in range(wl.TINYLLAMA_LAYERS):
+            for shp in wl.tinyllama_shapes():
+                W = wl.tinyllama_weight_gpu(layer, shp, dev)
+                pws.append(api.pack(W, api.plan(W)))
+                del W
+        res["tinyllama_decode_b1"] = decode_pass(pws, 1, 20)
+        del pws
+        torch.cuda.empty_cache()
+
+        # Llama-8B: planner / packer sweep, then decode
+        log("configs: Llama-8B planner / packer sweep")
+        settings = [("eps_int4=0.04", {"eps_int4": 0.04}), ("eps_int4=0.08", {}), ("eps_int4=0.16", {"eps_int4": 0.16}),
+                    ("all INT4", {"force_format": 0}), ("all INT8", {"force_format": 1})]
+        acc = {name: {"plan_s": 0.0, "pack_s": 0.0, "read": 0, "map": 0, "packed": 0, "counts": [0] * 5}
+               for name, _ in settings}
+        keep = []
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for layer in range(wl.LLAMA8B_LAYERS):
+            for shp in wl.llama8b_shapes():
+                W = wl.llama8b_weight_gpu(layer, shp, dev)
+                for name, kw in settings:
+                    a = acc[name]
+                    fmt = torch.empty((shp.n, shp.k // 64), dtype=torch.uint8, device=dev)
+                    ev0.record(stream)
+                    B.ht_plan(W, fmt, api.plan_params(**kw), stream=stream)
+                    ev1.record(stream)
+                    ev1.synchronize()
+                    a["plan_s"] += ev0.elapsed_time(ev1) / 1e3
+                    cnt = api.counts(fmt)
+                    nb = B.ht_pack_bytes(shp.n, shp.k, 16, cnt)
+                    buf = api._aligned_empty(nb, dev)
+                    ev0.record(stream)
+                    desc = B.ht_pack(W, fmt, 16, cnt, buf, stream=stream)
+                    ev1.record(stream)
+                    ev1.synchronize()
+                    a["pack_s"] += ev0.elapsed_time(ev1) / 1e3
+                    a["read"] += 4 * shp.n * shp.k
+                    a["map"] += shp.n * shp.k // 64
+                    a["packed"] += nb
+                    a["counts"] = [u + v for u, v in zip(a["counts"], cnt)]
+                    if name == "eps_int4=0.08":
+                        keep.append(api.PackedLinear(buf, desc, cnt))
+                    else:
+                        del buf
+                    del fmt
+                del W
+        sweep = {}
+        for name, _ in settings:
+            a = acc[name]
+            tot = sum(a["counts"])
+            sweep[name] = {"planner_GBps": round((a["read"] + a["map"]) / a["plan_s"] / 1e9, 1),
+                           "packer_GBps": round((a["read"] + a["map"] + a["packed"]) / a["pack_s"] / 1e9, 1),
+                           "plan_s": round(a["plan_s"], 4), "pack_s": round(a["pack_s"], 4),
+                           "packed_GB": round(a["packed"] / 1e9, 3),
+                           "format_mix": {f: round(c / tot, 5) for f, c in
+                                          zip(("INT4", "INT8", "BF16", "FP16", "FP32"), a["counts"])}}
+        res["llama8b_plan_pack_sweep"] = {"params": 32 * sum(s_.n * s_.k for s_ in wl.llama8b_shapes()),
+                                          "settings": sweep}
+        log("configs: Llama-8B decode")
+        for M in (1, 4, 16):
+            res[f"llama8b_decode_b{M}"] = decode_pass(keep, M, 5)
+        del keep
+        torch.cuda.empty_cache()
+        return res
+
+    if args.only == "configs":
+        print(json.dumps(configs_leg()))
+        return 0
     if args.only == "gemm":
         print(json.dumps(gemm_leg()))
         return 0

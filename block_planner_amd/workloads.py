@@ -210,3 +210,39 @@ def edge_blocks(seed: int = 0) -> np.ndarray:
     one = np.zeros(64, np.float32); one[63] = 1e-30
     rows.append(one)
     return np.stack(rows).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Device-side generators for the full-size stacks (billions of entries, too
+# many to draw on the host).  Same distributions as the numpy generators
+# above, drawn with torch's device generator seeded through ``seed_for``; the
+# outlier positions are Bernoulli(frac) per entry rather than an exact count.
+# ---------------------------------------------------------------------------
+def torch_generator(device, *parts):
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed_for(*parts))
+    return g
+
+
+def tinyllama_weight_gpu(layer: int, shape: LinearShape, device, seed: int = 0):
+    """fp32 [n, k] on `device`: N(0, 0.02), 0.1% of the entries times 30."""
+    import torch
+
+    g = torch_generator(device, "tinyllama-gpu", seed, layer, shape.name)
+    w = torch.randn(shape.n, shape.k, generator=g, device=device) * 0.02
+    hit = torch.rand(shape.n, shape.k, generator=g, device=device) < 0.001
+    return torch.where(hit, w * 30.0, w)
+
+
+def llama8b_weight_gpu(layer: int, shape: LinearShape, device, seed: int = 0):
+    """fp32 [n, k] on `device`: N(0, 0.02) times a per-row log-normal(0, 0.5)
+    factor, 0.1% of the entries times 30."""
+    import torch
+
+    g = torch_generator(device, "llama8b-gpu", seed, layer, shape.name)
+    w = torch.randn(shape.n, shape.k, generator=g, device=device) * 0.02
+    w *= torch.exp(torch.randn(shape.n, 1, generator=g, device=device) * 0.5)
+    hit = torch.rand(shape.n, shape.k, generator=g, device=device) < 0.001
+    return torch.where(hit, w * 30.0, w)
