@@ -146,12 +146,21 @@ uint32_t lds_bytes(uint32_t Mt, uint32_t nkb, uint32_t R) {
     return Mt * nkb * 64u * 4u + Mt * R * (nkb + 1u) * 4u;
 }
 
-// K-split choice: enough workgroups to cover the chip, LDS within 64 KiB,
-// and every split non-empty.
+// Packed bytes per workgroup below which a further K-split does not pay: the
+// split adds a reduction launch of a few microseconds, about what one
+// workgroup needs to stream this much (measured on decode passes over
+// transformer-shaped stacks, where splitting smaller layers made them slower).
+constexpr uint64_t kSplitBytes = 128 * 1024;
+
+// K-split choice: LDS within 64 KiB; beyond that, more workgroups while there
+// are fewer than the chip's compute units and each still streams more than
+// kSplitBytes; every split at least 8 K-blocks and non-empty.
 uint32_t choose_splits(const ht_packed_weight *w, uint32_t Mt) {
     const uint32_t KB = uint32_t(w->K / kBlockK), T = uint32_t(w->n_tiles), R = uint32_t(w->row_tile);
+    const uint64_t per_tile = uint64_t(w->bytes) / T;
     uint32_t S = 1;
-    while (S < KB && (lds_bytes(Mt, (KB + S - 1) / S, R) > kMaxLds || (uint64_t(T) * S < 256 && (KB + S) / (S + 1) >= 8)))
+    while (S < KB && (lds_bytes(Mt, (KB + S - 1) / S, R) > kMaxLds ||
+                      (uint64_t(T) * S < 256 && per_tile / S > kSplitBytes && (KB + S) / (S + 1) >= 8)))
         ++S;
     const uint32_t KBs = (KB + S - 1) / S;
     return (KB + KBs - 1) / KBs;

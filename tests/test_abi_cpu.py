@@ -97,6 +97,7 @@ def test_plan_counts_argument_checks():
 def _desc(N=256, K=256, R=16, base=0x100000):
     d = B.PackedWeight()
     d.N, d.K, d.row_tile, d.n_tiles = N, K, R, (N + R - 1) // R
+    d.bytes = N * K            # about one byte per weight, as for an INT8-heavy plan
     d.layout_version = 1
     d.base = base
     return d
