@@ -49,7 +49,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(LinArgs a) {
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
     // x for these K-blocks: at most two 16-byte loads per thread (the host
-    // keeps M * nkb * 64 * 4 bytes of x within 64 KiB of LDS), issued first
+    // keeps the M * nkb * 64 * 4 bytes of fp32 x within 64 KiB), issued first
     const uint32_t per_row = nkb * 8;   // 8 bf16 per 16-byte load
     uint4 xr[2];
 #pragma unroll
@@ -139,12 +139,13 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *partial,
 // ---------------------------------------------------------------------------
 namespace {
 
-constexpr uint32_t kMaxLds = 64 * 1024;
+constexpr uint32_t kMaxX = 64 * 1024;     // fp32 copy of x: at most two 16-byte loads of bf16 x per thread
+constexpr uint32_t kMaxLds = 96 * 1024;   // x plus the block partials (long K at M = 1 then needs no split)
 constexpr int kMaxM = 8;   // rows per launch of the register path; larger M is tiled
 
-uint32_t lds_bytes(uint32_t Mt, uint32_t nkb, uint32_t R) {
-    return Mt * nkb * 64u * 4u + Mt * R * (nkb + 1u) * 4u;
-}
+uint32_t x_bytes(uint32_t Mt, uint32_t nkb) { return Mt * nkb * 64u * 4u; }
+
+uint32_t lds_bytes(uint32_t Mt, uint32_t nkb, uint32_t R) { return x_bytes(Mt, nkb) + Mt * R * (nkb + 1u) * 4u; }
 
 // Packed bytes per workgroup below which a further K-split does not pay: the
 // split adds a reduction launch of a few microseconds, about what one
@@ -152,14 +153,15 @@ uint32_t lds_bytes(uint32_t Mt, uint32_t nkb, uint32_t R) {
 // transformer-shaped stacks, where splitting smaller layers made them slower).
 constexpr uint64_t kSplitBytes = 128 * 1024;
 
-// K-split choice: LDS within 64 KiB; beyond that, more workgroups while there
-// are fewer than the chip's compute units and each still streams more than
-// kSplitBytes; every split at least 8 K-blocks and non-empty.
+// K-split choice: x within kMaxX and x plus partials within kMaxLds; beyond
+// that, more workgroups while there are fewer than the chip's compute units
+// and each still streams more than kSplitBytes; every split at least 8
+// K-blocks and non-empty.
 uint32_t choose_splits(const ht_packed_weight *w, uint32_t Mt) {
     const uint32_t KB = uint32_t(w->K / kBlockK), T = uint32_t(w->n_tiles), R = uint32_t(w->row_tile);
     const uint64_t per_tile = uint64_t(w->bytes) / T;
     uint32_t S = 1;
-    while (S < KB && (lds_bytes(Mt, (KB + S - 1) / S, R) > kMaxLds ||
+    while (S < KB && (x_bytes(Mt, (KB + S - 1) / S) > kMaxX || lds_bytes(Mt, (KB + S - 1) / S, R) > kMaxLds ||
                       (uint64_t(T) * S < 256 && per_tile / S > kSplitBytes && (KB + S) / (S + 1) >= 8)))
         ++S;
     const uint32_t KBs = (KB + S - 1) / S;
@@ -170,6 +172,11 @@ int m_tile(int64_t M) { return int(M < kMaxM ? M : kMaxM); }
 
 template <int M>
 void launch_gemv(const LinArgs &a, uint32_t T, uint32_t lds, hipStream_t s) {
+    // more than 64 KiB of dynamic LDS is requested explicitly (a failure
+    // shows up as the launch error the caller checks)
+    if (lds > 64u * 1024u)
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_kernel<M>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxLds));
     hipLaunchKernelGGL(gemv_kernel<M>, dim3(T, a.S), dim3(kThreads), lds, s, a);
 }
 

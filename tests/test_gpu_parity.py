@@ -406,7 +406,7 @@ def test_mlp_end_to_end_info(orc, mlp4096):
 # Transformer-shaped layers at full size (sampled outputs)
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("cfg,name", [("tinyllama", "k"), ("tinyllama", "down"), ("llama8b", "gate"),
-                                      ("llama8b", "v")])
+                                      ("llama8b", "v"), ("llama8b", "down")])
 def test_full_size_layers_sampled(orc, cfg, name):
     shapes = wl.tinyllama_shapes() if cfg == "tinyllama" else wl.llama8b_shapes()
     shp = [s for s in shapes if s.name == name][0]
@@ -432,6 +432,23 @@ def test_full_size_layers_sampled(orc, cfg, name):
     # scale: the largest sampled oracle value (a lower bound of max|y|, so
     # the bound is at least as strict as the full-output one)
     assert np.max(np.abs(y.cpu().numpy()[mi, ni] - ys)) <= TOL * np.max(np.abs(ys)), (cfg, name, M)
+
+
+@pytest.mark.parametrize("M", [4, 2])
+def test_register_path_large_lds(orc, M):
+    """The register path without a K-split where x plus the block partials
+    need more than 64 KiB of LDS: 4 rows over K = 4096 (x alone is exactly
+    the 64 KiB limit) and 2 rows over K = 14336."""
+    K = 4096 if M == 4 else 14336
+    rng = np.random.default_rng(50 + M)
+    W = (rng.standard_t(4, size=(512, K)) * 0.02).astype(np.float32)
+    fmt = orc.plan(W)
+    pw = api.pack(gpu(W), gpu(fmt))
+    assert B.ht_linear_workspace(pw.desc, M, B.HT_PATH_GEMV) == 0 or K == 14336
+    x = wl.to_bf16_bits(rng.normal(size=(M, K)).astype(np.float32))
+    y = api.linear(pw, bf16_gpu(x), path=B.HT_PATH_GEMV)
+    torch.cuda.synchronize()
+    check_close(y.cpu().numpy(), orc.linear(W, fmt, x), f"M={M} K={K}")
 
 
 def test_decode_batch4_full_layer(orc):
