@@ -191,16 +191,20 @@ ht_status ht_linear_workspace(const ht_packed_weight *w, int64_t M, int32_t path
  *          in registers straight into the operands of bf16 MFMAs (the same
  *          bfloat16 planes as HT_PATH_GEMM), 32 rows of x per launch;
  *          HT_PATH_GEMM_I8: for prefill with INT8-heavy plans (row tile 16
- *          only, else HT_EINVAL): a 64-column weight tile whose blocks are
- *          all INT8 over the K range of a split runs on the int8 matrix
- *          cores, every other tile exactly as HT_PATH_GEMM.  The page fixes
+ *          only, else HT_EINVAL): a 256-column weight tile (weight rows
+ *          [256 i, +256)) whose blocks are all INT8 over the K range of a
+ *          split runs on the int8 matrix cores, every other tile exactly as
+ *          HT_PATH_GEMM (the same K-splits, unless every block of the
+ *          weight is INT8: then the int8 kernel alone, with K-splits of its
+ *          own).  The page fixes
  *          no integer encoding of x; here each row m of x is encoded as
  *          x_hat = (256 hi + lo) 2^(E-14) with int8 planes hi, lo,
  *          round-half-even, 2^(E-1) <= max_k |x[m,k]| < 2^E, so
  *          |x_hat - x| <= 2^-14 max_k |x[m,k]|; such a tile computes
  *          x_hat . W_hat^T with exact int32 block sums (a row holding Inf or
- *          NaN gives NaN there).  The workspace holds the encoded x;
- *          HT_PATH_AUTO never picks this path;
+ *          NaN gives NaN there).  The workspace holds the encoded x
+ *          (unless the weight has too few INT8 blocks for any tile, when
+ *          the call is HT_PATH_GEMM's); HT_PATH_AUTO never picks this path;
  *          HT_PATH_AUTO: GEMV_MFMA for 4 <= M <= 32 with row tile 16;
  *          otherwise GEMM when M >= 16, else GEMV.
  *   ws     workspace of ws_bytes >= ht_linear_workspace(w, M, path): K-split
