@@ -257,3 +257,25 @@ def test_i8_too_few_int8_blocks_is_gemm(orc):
     y = run(pw, x, I8)
     assert np.array_equal(y, run(pw, x, GEMM))
     assert np.max(np.abs(y - orc.linear(W, fmt, x))) <= TOL * np.max(np.abs(orc.linear(W, fmt, x)))
+
+
+def test_i8_strides_and_tiny(orc):
+    """Row strides on x and y (the padding of y untouched), a weight narrower
+    than one row tile, and a single row of x."""
+    rng = np.random.default_rng(48)
+    for N, K, M in ((8, 192, 1), (40, 512, 37)):
+        W = (rng.normal(size=(N, K)) * 0.05).astype(np.float32)
+        fmt = np.full((N, K // 64), INT8, np.uint8)
+        x = wl.to_bf16_bits(rng.normal(size=(M, K)).astype(np.float32))
+        pw = api.pack(gpu(W), gpu(fmt), row_tile=16)
+        xs = torch.zeros((M, K + 24), dtype=torch.bfloat16, device=dev())
+        xs[:, :K] = bf16_gpu(x)
+        ys = torch.full((M, N + 12), 7.0, dtype=torch.float32, device=dev())
+        ws = api.workspace(B.ht_linear_workspace(pw.desc, M, I8), dev())
+        api.linear(pw, xs[:, :K], out=ys[:, :N], ws=ws, path=I8)
+        torch.cuda.synchronize()
+        assert torch.all(ys[:, N:] == 7.0)
+        y = ys[:, :N].cpu().numpy().astype(np.float64)
+        y_ref = orc.linear_xplanes(W, fmt, x)
+        mag = np.abs(orc.x_hat(*orc.x_planes(x))) @ np.abs(orc.dequant(W, fmt)).T
+        assert np.all(np.abs(y - y_ref) <= 5e-6 * mag + 1e-30), (N, K, M)
