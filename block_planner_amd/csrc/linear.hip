@@ -171,13 +171,15 @@ uint32_t choose_splits(const ht_packed_weight *w, uint32_t Mt) {
 int m_tile(int64_t M) { return int(M < kMaxM ? M : kMaxM); }
 
 template <int M>
-void launch_gemv(const LinArgs &a, uint32_t T, uint32_t lds, hipStream_t s) {
-    // more than 64 KiB of dynamic LDS is requested explicitly (a failure
-    // shows up as the launch error the caller checks)
-    if (lds > 64u * 1024u)
-        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_kernel<M>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxLds));
+ht_status launch_gemv(const LinArgs &a, uint32_t T, uint32_t lds, hipStream_t s) {
+    // more than 64 KiB of dynamic LDS is requested explicitly
+    if (lds > 64u * 1024u &&
+        hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_kernel<M>), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            int(kMaxLds)) != hipSuccess)
+        return HT_EHIP;
     hipLaunchKernelGGL(gemv_kernel<M>, dim3(T, a.S), dim3(kThreads), lds, s, a);
+    HT_LAUNCH_CHECK();
+    return HT_OK;
 }
 
 }  // namespace
@@ -229,20 +231,20 @@ ht_status run_linear(const ht_packed_weight *w, const uint16_t *x, int64_t M, in
         const uint32_t lds = lds_bytes(uint32_t(Mt), a.KBs, a.w.R);
         LinArgs g = a;
         if (S > 1) { g.y = nullptr; g.ybf = nullptr; }
+        ht_status st;
         switch (Mt) {
-        case 1: launch_gemv<1>(g, T, lds, s); break;
-        case 2: launch_gemv<2>(g, T, lds, s); break;
-        case 3: launch_gemv<3>(g, T, lds, s); break;
-        case 4: launch_gemv<4>(g, T, lds, s); break;
-        case 5: launch_gemv<5>(g, T, lds, s); break;
-        case 6: launch_gemv<6>(g, T, lds, s); break;
-        case 7: launch_gemv<7>(g, T, lds, s); break;
-        default: launch_gemv<8>(g, T, lds, s); break;
+        case 1: st = launch_gemv<1>(g, T, lds, s); break;
+        case 2: st = launch_gemv<2>(g, T, lds, s); break;
+        case 3: st = launch_gemv<3>(g, T, lds, s); break;
+        case 4: st = launch_gemv<4>(g, T, lds, s); break;
+        case 5: st = launch_gemv<5>(g, T, lds, s); break;
+        case 6: st = launch_gemv<6>(g, T, lds, s); break;
+        case 7: st = launch_gemv<7>(g, T, lds, s); break;
+        default: st = launch_gemv<8>(g, T, lds, s); break;
         }
-        HT_LAUNCH_CHECK();
+        if (st != HT_OK) return st;
         if (S > 1) {
-            const ht_status st = launch_split_reduce(static_cast<const float *>(ws), S, uint32_t(Mt), a.w.N, a.y,
-                                                     a.ybf, ldy, act, s);
+            st = launch_split_reduce(static_cast<const float *>(ws), S, uint32_t(Mt), a.w.N, a.y, a.ybf, ldy, act, s);
             if (st != HT_OK) return st;
         }
     }
