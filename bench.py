@@ -79,7 +79,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=240)
     ap.add_argument("--warmup", type=int, default=24)
     ap.add_argument("--copies", type=int, default=6)
-    ap.add_argument("--cpu-steps", type=int, default=20, help="oracle MLP forwards timed for the CPU baseline")
+    ap.add_argument("--cpu-steps", type=int, default=100,
+                    help="oracle MLP forwards timed for the CPU baseline (about 14 s of CPU work)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["all", "gemv", "mlp", "gemm", "decode", "i8", "configs"], default="all",
                     help="'gemv' / 'mlp' / 'gemm' / 'decode': only that timing leg (for profiler runs)")
