@@ -211,6 +211,14 @@ def linear_sampled(W: np.ndarray, fmt: np.ndarray, x_bf16: np.ndarray, m_idx, n_
     return y
 
 
+def linear_backward_data(W: np.ndarray, fmt: np.ndarray, dy: np.ndarray) -> np.ndarray:
+    """dX [M, K] (double) = dY . W_hat: the input gradient of y = x . W_hat^T
+    (the pages' training support), dY given in fp32 and widened exactly."""
+    dy = np.ascontiguousarray(dy, dtype=np.float32).astype(np.float64)
+    assert dy.ndim == 2 and dy.shape[1] == W.shape[0]
+    return dy @ dequant(W, fmt)
+
+
 def relu_bf16(z: np.ndarray) -> np.ndarray:
     """bfloat16 bits of max(z, 0), round to nearest even."""
     z = np.ascontiguousarray(z, dtype=np.float64)

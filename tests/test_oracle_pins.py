@@ -621,3 +621,46 @@ def test_linear_xplanes_exact_and_bounded():
     Xn[2, 5] = 0x7F80                          # +Inf in row 2
     yn = oracle.linear_xplanes(W, fmt, Xn)
     assert np.all(np.isnan(yn[2])) and np.all(np.isfinite(np.delete(yn, 2, axis=0)))
+
+
+# ---------------------------------------------------------------------------
+# Input gradient of the linear (training backward)
+# ---------------------------------------------------------------------------
+def test_backward_data_is_the_adjoint():
+    """<dX, x> = <dY, W_hat x> for every x and dY, with W_hat x taken from the
+    oracle's forward (its own C dot products): catches a transposed or
+    mis-indexed backward."""
+    import oracle
+
+    rng = np.random.default_rng(60)
+    W = (rng.standard_t(4, size=(80, 320)) * 0.02).astype(np.float32)
+    fmt = rng.integers(0, 5, size=(80, 5)).astype(np.uint8)
+    xb = wl.to_bf16_bits(rng.normal(size=(3, 320)).astype(np.float32))
+    dy = rng.normal(size=(3, 80)).astype(np.float32)
+    dx = oracle.linear_backward_data(W, fmt, dy)
+    y = oracle.linear(W, fmt, xb)
+    x = wl.bf16_bits_to_f32(xb).astype(np.float64)
+    for m in range(3):
+        lhs = float(dx[m] @ x[m])
+        rhs = float(dy[m].astype(np.float64) @ y[m])
+        assert abs(lhs - rhs) <= 1e-12 * (np.abs(dx[m]) @ np.abs(x[m]) + 1e-300)
+
+
+def test_backward_data_dense_and_grid_cases():
+    """All-FP32 blocks: dX = dY W exactly as a dense product of the fp32
+    weight; INT8-grid blocks (w = integer * 2^-10): the same, since those
+    blocks reconstruct exactly."""
+    import oracle
+
+    rng = np.random.default_rng(61)
+    W = (rng.normal(size=(48, 192)) * 0.1).astype(np.float32)
+    dy = rng.normal(size=(2, 48)).astype(np.float32)
+    fmt = np.full((48, 3), FP32, np.uint8)
+    np.testing.assert_allclose(oracle.linear_backward_data(W, fmt, dy),
+                               dy.astype(np.float64) @ W.astype(np.float64), rtol=1e-13, atol=1e-13)
+    G = rng.integers(-127, 128, size=(48, 192)).astype(np.float32)
+    G[:, ::64] = 127.0                                   # every block reaches the full range
+    Wg = G * np.float32(2.0 ** -10)
+    fmt8 = np.full((48, 3), INT8, np.uint8)
+    np.testing.assert_allclose(oracle.linear_backward_data(Wg, fmt8, dy),
+                               dy.astype(np.float64) @ Wg.astype(np.float64), rtol=1e-13, atol=1e-13)
