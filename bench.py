@@ -82,7 +82,8 @@ def main() -> int:
     ap.add_argument("--cpu-steps", type=int, default=100,
                     help="oracle MLP forwards timed for the CPU baseline (about 14 s of CPU work)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "gemv", "mlp", "gemm", "decode", "i8", "configs"], default="all",
+    ap.add_argument("--only", choices=["all", "gemv", "mlp", "gemm", "decode", "i8", "configs", "backward"],
+                    default="all",
                     help="'gemv' / 'mlp' / 'gemm' / 'decode': only that timing leg (for profiler runs)")
     ap.add_argument("--no-gemm", action="store_true", help="skip the prefill GEMM leg")
     args = ap.parse_args()
@@ -293,6 +294,42 @@ def main() -> int:
         torch.cuda.empty_cache()
         return res
 
+    def backward_leg():
+        """The input gradient dX = dY . W_hat (ht_linear_backward_data) at 1
+        and 4 rows of fp32 dY: the 4096x4096 MLP layer (default thresholds)
+        and the Llama-8B q / gate / down shapes.  Graph replays of 10 calls on
+        one packed copy; GB/s counts packed bytes + dY + dX."""
+        res = {}
+        cases = [("mlp4096", None)] + [(s_.name, s_) for s_ in wl.llama8b_shapes() if s_.name in ("q", "gate", "down")]
+        for name, shp in cases:
+            W = (torch.from_numpy(wl.mlp_weight(0)).to(dev) if shp is None else wl.llama8b_weight_gpu(0, shp, dev))
+            pw = api.pack(W, api.plan(W))
+            del W
+            row = {}
+            for M in (1, 4):
+                dy = torch.randn(M, pw.N, device=dev)
+                dx = torch.empty(M, pw.K, device=dev)
+                ws = api.workspace(B.ht_linear_backward_workspace(pw.desc, M), dev)
+                fn = lambda: api.linear_backward_data(pw, dy, out=dx, ws=ws)
+                fn()
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for _ in range(10):
+                        fn()
+                g.replay()
+                torch.cuda.synchronize()
+                t = timed(lambda i: g.replay(), 5) / 10
+                nb = pw.nbytes + 4 * M * (pw.N + pw.K)
+                row[f"M{M}"] = {"us": round(t * 1e6, 2), "GBps": round(nb / t / 1e9, 1)}
+                del g
+            res[name] = row
+            del pw
+        return {"kernel": "linear_bwd_kernel<M>", "shapes": res}
+
+    if args.only == "backward":
+        print(json.dumps(backward_leg()))
+        return 0
     if args.only == "configs":
         print(json.dumps(configs_leg()))
         return 0

@@ -87,6 +87,17 @@ def linear(pw: PackedLinear, x: torch.Tensor, act: int = B.HT_ACT_NONE, out: tor
     return y
 
 
+def linear_backward_data(pw: PackedLinear, dy: torch.Tensor, out: torch.Tensor | None = None,
+                         ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """dX = dY . W_hat (fp32 dY [M, N] -> fp32 dX [M, K])."""
+    M = dy.shape[0]
+    dx = torch.empty((M, pw.K), dtype=torch.float32, device=dy.device) if out is None else out
+    if ws is None:
+        ws = workspace(B.ht_linear_backward_workspace(pw.desc, M), dy.device)
+    B.ht_linear_backward_data(pw.desc, dy, dx, ws=ws, stream=stream)
+    return dx
+
+
 def mlp_workspace(layers: list, M: int, device, stream=None) -> torch.Tensor:
     """An initialised workspace for mlp() over these layers at batch M."""
     ws = workspace(B.ht_mlp_workspace([pw.desc for pw in layers], M), device)

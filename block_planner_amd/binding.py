@@ -25,6 +25,7 @@ STATUS = {0: "HT_OK", 1: "HT_EINVAL", 2: "HT_ESHAPE", 3: "HT_EALIGN", 4: "HT_ESM
 # Every symbol include/ht.h declares.
 EXPORTS = ("ht_status_string", "ht_plan_params_default", "ht_plan", "ht_plan_counts",
            "ht_pack_bytes", "ht_pack", "ht_linear_workspace", "ht_linear_forward",
+           "ht_linear_backward_workspace", "ht_linear_backward_data",
            "ht_mlp_workspace", "ht_workspace_init", "ht_mlp_forward")
 
 
@@ -80,6 +81,10 @@ def load() -> ctypes.CDLL:
     lib.ht_linear_forward.restype = St
     lib.ht_linear_forward.argtypes = [ctypes.POINTER(PackedWeight), P, I64, I64, P, I64, I32, I32, P,
                                       ctypes.c_size_t, P]
+    lib.ht_linear_backward_workspace.restype = St
+    lib.ht_linear_backward_workspace.argtypes = [ctypes.POINTER(PackedWeight), I64, ctypes.POINTER(ctypes.c_size_t)]
+    lib.ht_linear_backward_data.restype = St
+    lib.ht_linear_backward_data.argtypes = [ctypes.POINTER(PackedWeight), P, I64, I64, P, I64, P, ctypes.c_size_t, P]
     lib.ht_mlp_workspace.restype = St
     lib.ht_mlp_workspace.argtypes = [ctypes.POINTER(ctypes.POINTER(PackedWeight)), I32, I64,
                                      ctypes.POINTER(ctypes.c_size_t)]
@@ -173,6 +178,23 @@ def ht_linear_forward(desc: PackedWeight, x, y, act: int = HT_ACT_NONE, path: in
     wsb = (ws.numel() * ws.element_size() if ws is not None else 0) if ws_bytes is None else ws_bytes
     _check("ht_linear_forward", load().ht_linear_forward(ctypes.byref(desc), _ptr(x), M, ldx, _ptr(y), ldy, act,
                                                          path, _ptr(ws), wsb, _stream(stream)))
+
+
+def ht_linear_backward_workspace(desc: PackedWeight, M: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check("ht_linear_backward_workspace", load().ht_linear_backward_workspace(ctypes.byref(desc), M,
+                                                                               ctypes.byref(out)))
+    return out.value
+
+
+def ht_linear_backward_data(desc: PackedWeight, dy, dx, ws=None, stream=None, M=None, lddy=None, lddx=None,
+                            ws_bytes=None) -> None:
+    M = dy.shape[0] if M is None else M
+    lddy = dy.stride(0) if lddy is None else lddy
+    lddx = dx.stride(0) if lddx is None else lddx
+    wsb = (ws.numel() * ws.element_size() if ws is not None else 0) if ws_bytes is None else ws_bytes
+    _check("ht_linear_backward_data", load().ht_linear_backward_data(ctypes.byref(desc), _ptr(dy), M, lddy, _ptr(dx),
+                                                                     lddx, _ptr(ws), wsb, _stream(stream)))
 
 
 def _desc_array(descs):

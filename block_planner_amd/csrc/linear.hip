@@ -300,3 +300,23 @@ extern "C" ht_status ht_linear_forward(const ht_packed_weight *w, const uint16_t
     if (path == HT_PATH_GEMM_I8) return run_gemm_i8(w, x, M, ldx, y, nullptr, ldy, act, ws, s);
     return run_linear(w, x, M, ldx, y, nullptr, ldy, act, ws, s);
 }
+
+extern "C" ht_status ht_linear_backward_workspace(const ht_packed_weight *w, int64_t M, size_t *bytes) {
+    if (!bytes || !desc_ok(w)) return HT_EINVAL;
+    if (M <= 0) return HT_ESHAPE;
+    if (!bwd_ok(w)) return HT_EINVAL;
+    *bytes = bwd_ws(w, M);
+    return HT_OK;
+}
+
+extern "C" ht_status ht_linear_backward_data(const ht_packed_weight *w, const float *dy, int64_t M, int64_t lddy,
+                                             float *dx, int64_t lddx, void *ws, size_t ws_bytes, ht_stream stream) {
+    if (!desc_ok(w) || !dy || !dx) return HT_EINVAL;
+    if (!bwd_ok(w)) return HT_EINVAL;
+    if (M <= 0 || lddy < w->N || lddx < w->K) return HT_ESHAPE;
+    if (!al16(dy) || !al16(dx)) return HT_EALIGN;
+    const size_t need = bwd_ws(w, M);
+    if (need && (!ws || ws_bytes < need)) return HT_ESMALL;
+    if (ws && !al16(ws)) return HT_EALIGN;
+    return run_bwd(w, dy, M, lddy, dx, lddx, ws, reinterpret_cast<hipStream_t>(stream));
+}

@@ -55,6 +55,14 @@ size_t dec_ws(const ht_packed_weight *w, int64_t M);
 ht_status run_dec(const ht_packed_weight *w, const uint16_t *x, int64_t M, int64_t ldx, float *y, uint16_t *ybf,
                   int64_t ldy, int act, void *ws, hipStream_t s);
 
+// The input gradient dX = dY . W_hat (row tile 16 only): whether it takes
+// this weight, its workspace bytes for M rows of dY (per-tile-group sums),
+// and one call (arguments assumed checked).
+bool bwd_ok(const ht_packed_weight *w);
+size_t bwd_ws(const ht_packed_weight *w, int64_t M);
+ht_status run_bwd(const ht_packed_weight *w, const float *dy, int64_t M, int64_t lddy, float *dx, int64_t lddx,
+                  void *ws, hipStream_t s);
+
 // The path HT_PATH_AUTO resolves to for one linear over M rows: the MFMA
 // decode path for 4..32 rows (row tile 16), otherwise the LDS-staged MFMA path
 // from 16 rows and the register path below (1 to 3 rows stay on the register

@@ -213,6 +213,24 @@ ht_status ht_linear_forward(const ht_packed_weight *w, const uint16_t *x, int64_
                             int64_t ldx, float *y, int64_t ldy, int32_t act, int32_t path,
                             void *ws, size_t ws_bytes, ht_stream stream);
 
+/* ht_linear_backward_workspace -- workspace bytes ht_linear_backward_data
+ * needs for M rows of dY (HT_EINVAL for a row tile other than 16). */
+ht_status ht_linear_backward_workspace(const ht_packed_weight *w, int64_t M, size_t *bytes);
+
+/* ht_linear_backward_data -- the input gradient of the linear
+ * ("Key Features": training support; "Design Philosophy": custom backward
+ * kernels): dX = dY . W_hat over the packed buffers.
+ *   w      (host) descriptor from ht_pack; row tile 16 only, else HT_EINVAL.
+ *   dy     fp32 [M, lddy], lddy >= N (the gradient of y).
+ *   dx     fp32 [M, lddx] out, lddx >= K: dx[m, k] = sum_n dy[m, n] *
+ *          w_hat[n, k], in fp32 (integer blocks as (dy * s) * q), summed in
+ *          a fixed order (bitwise reproducible); columns k >= K untouched.
+ *   ws     workspace of ws_bytes >= ht_linear_backward_workspace(w, M):
+ *          per-tile-group sums, added in group order by a second kernel.
+ * Forward-only state is not needed: W may have been freed after packing. */
+ht_status ht_linear_backward_data(const ht_packed_weight *w, const float *dy, int64_t M, int64_t lddy,
+                                  float *dx, int64_t lddx, void *ws, size_t ws_bytes, ht_stream stream);
+
 /* ht_mlp_workspace -- workspace bytes ht_mlp_forward needs for M rows. */
 ht_status ht_mlp_workspace(const ht_packed_weight *const *layers, int32_t n_layers,
                            int64_t M, size_t *bytes);

@@ -194,3 +194,21 @@ def test_mlp_argument_checks():
     assert lib.ht_mlp_forward(arr, 0, 0x200000, 1, 256, 0x300000, 128, None, 0, None, 0, None) == 1
     assert lib.ht_workspace_init(None, 256, None) == 1
     assert lib.ht_workspace_init(0x400004, 256, None) == 3
+
+
+def test_backward_argument_checks():
+    lib = B.load()
+    d = _desc(N=256, K=512)
+    out = ctypes.c_size_t(0)
+    assert lib.ht_linear_backward_workspace(ctypes.byref(d), 0, ctypes.byref(out)) == 2          # M <= 0
+    assert lib.ht_linear_backward_workspace(ctypes.byref(_desc(R=8)), 1, ctypes.byref(out)) == 1   # row tile 8
+    assert lib.ht_linear_backward_workspace(ctypes.byref(d), 3, ctypes.byref(out)) == 0
+    # 16 row tiles: at most 4 tile groups of at least 4 tiles -> [G][min(M, 4)][K] fp32 partials
+    assert out.value == 4 * 3 * 512 * 4
+    f = lib.ht_linear_backward_data
+    dy, dx = 0x200000, 0x300000
+    assert f(ctypes.byref(d), dy, 3, 255, dx, 512, None, 0, None) == 2       # lddy < N
+    assert f(ctypes.byref(d), dy, 3, 256, dx, 511, None, 0, None) == 2       # lddx < K
+    assert f(ctypes.byref(d), dy + 4, 3, 256, dx, 512, None, 0, None) == 3   # misaligned dy
+    assert f(ctypes.byref(d), dy, 3, 256, dx, 512, None, 0, None) == 4       # workspace missing
+    assert f(ctypes.byref(d), None, 3, 256, dx, 512, None, 0, None) == 1
