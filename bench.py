@@ -481,7 +481,7 @@ def main() -> int:
     t_warm = replay_timed(gw, reps, 1) / G
     del gp, g32, gw
 
-    gemm = None
+    gemm = bwd = None
     if not args.no_gemm:
         log("prefill gemm (Llama-8B shapes, M = 2048)")
         del copies, arrays, descs
@@ -489,6 +489,8 @@ def main() -> int:
         gemm = gemm_leg()
         log("int8 matrix-core path (Llama-8B shapes, M = 2048)")
         gemm["int8_path"] = i8_leg()
+        log("input gradient dX = dY . W_hat (4096x4096 and Llama-8B shapes, M = 1 and 4)")
+        bwd = backward_leg()
 
     # ---- CPU baseline: the oracle as it stands ----------------------------
     cpu = None
@@ -547,6 +549,7 @@ def main() -> int:
         "format_mix": {n: round(v, 5) for n, v in zip(("INT4", "INT8", "BF16", "FP16", "FP32"), mix)},
         "packed_MB_per_mlp": round(packed_mb, 2),
         "prefill_gemm": gemm,
+        "backward_data": bwd,
     }
     print(json.dumps(out))
     return 0

@@ -122,13 +122,30 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(LinArgs a) {
 }
 
 // y[m, n] = act(sum over s in order of partial[s][m][n])
-__global__ __launch_bounds__(256) void split_reduce_kernel(const float *partial, uint32_t S, uint32_t M, uint32_t N,
-                                                           float *y, uint16_t *ybf, int64_t ldy, int act) {
-    const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+// One thread per output; small workgroups so that short outputs still reach
+// many compute units.  The partials are loaded 16 at a time (independent
+// loads in flight) and added in split order, the same order as one load at
+// a time.
+constexpr uint32_t kReduceThreads = 64;
+
+__global__ __launch_bounds__(kReduceThreads) void split_reduce_kernel(const float *partial, uint32_t S, uint32_t M,
+                                                                      uint32_t N, float *y, uint16_t *ybf,
+                                                                      int64_t ldy, int act) {
+    const uint32_t i = blockIdx.x * kReduceThreads + threadIdx.x;
     if (i >= M * N) return;
     const uint32_t m = i / N, n = i - m * N;
+    const uint64_t stride = uint64_t(M) * N;
+    const float *p = partial + uint64_t(m) * N + n;
     float v = 0.0f;
-    for (uint32_t s = 0; s < S; ++s) v += partial[(uint64_t(s) * M + m) * N + n];
+    uint32_t s = 0;
+    for (; s + 16 <= S; s += 16) {
+        float t[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) t[u] = p[(s + u) * stride];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v += t[u];
+    }
+    for (; s < S; ++s) v += p[s * stride];
     if (act == HT_ACT_RELU) v = v > 0.0f ? v : 0.0f;
     if (ybf) ybf[int64_t(m) * ldy + n] = f32_to_bf16_rne(v);
     else y[int64_t(m) * ldy + n] = v;
@@ -203,8 +220,8 @@ size_t linear_ws(const ht_packed_weight *w, int64_t M) {
 ht_status launch_split_reduce(const float *partial, uint32_t S, uint32_t M, uint32_t N, float *y, uint16_t *ybf,
                               int64_t ldy, int act, hipStream_t s) {
     const uint32_t tot = M * N;
-    hipLaunchKernelGGL(split_reduce_kernel, dim3((tot + 255) / 256), dim3(256), 0, s, partial, S, M, N, y, ybf, ldy,
-                       act);
+    hipLaunchKernelGGL(split_reduce_kernel, dim3((tot + kReduceThreads - 1) / kReduceThreads), dim3(kReduceThreads), 0,
+                       s, partial, S, M, N, y, ybf, ldy, act);
     HT_LAUNCH_CHECK();
     return HT_OK;
 }
