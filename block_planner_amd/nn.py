@@ -15,8 +15,10 @@ Scope, as built:
     are and reported in the plan's "skipped" list with the reason.
   * The output is fp32 (the path's accumulation type); the input is cast to
     bfloat16 (round to nearest even) as the path defines.
-  * Forward only: no gradient flows through HyperLinear (training backward is
-    not built).
+  * Gradients flow to the input only: dX = dY . W_hat by the library's
+    backward kernel (ht_linear_backward_data), in fp32; the rounding of x to
+    bfloat16 in the forward is passed straight through.  The packed weight
+    is frozen: no weight gradient and no update of the master weight.
   * The planner modes named on the page (LOWEST ... BEST) have no definition
     there; only the per-block rule is accepted (option None or "PER_BLOCK").
   * refresh_every > 0 with a master weight re-plans and re-packs every that
@@ -38,6 +40,20 @@ _DESC_FIELDS = ("N", "K", "row_tile", "n_tiles", "off_kbidx", "bytes", "layout_v
 def _eps(eps_int4=0.08, eps_int8=0.01, eps_bf16=0.0, eps_fp16=0.0, prefer_bf16=True) -> dict:
     return dict(eps_int4=float(eps_int4), eps_int8=float(eps_int8), eps_bf16=float(eps_bf16),
                 eps_fp16=float(eps_fp16), prefer_bf16=bool(prefer_bf16))
+
+
+class _PackedLinearFn(torch.autograd.Function):
+    """y = bf16(x) . W_hat^T forward; dX = dY . W_hat backward (fp32)."""
+
+    @staticmethod
+    def forward(ctx, x2: torch.Tensor, packed: api.PackedLinear) -> torch.Tensor:
+        ctx.packed = packed
+        return api.linear(packed, x2.to(torch.bfloat16).contiguous())
+
+    @staticmethod
+    def backward(ctx, dy: torch.Tensor):
+        dx = api.linear_backward_data(ctx.packed, dy.to(torch.float32).contiguous())
+        return dx, None
 
 
 class HyperLinear(torch.nn.Module):
@@ -120,10 +136,13 @@ class HyperLinear(torch.nn.Module):
         if x.shape[-1] != self.in_features:
             raise ValueError(f"expected {self.in_features} input features, got {x.shape[-1]}")
         lead = x.shape[:-1]
-        xb = x.reshape(-1, self.in_features).to(torch.bfloat16).contiguous()
-        if xb.shape[0] == 0:
+        x2 = x.reshape(-1, self.in_features)
+        if x2.shape[0] == 0:
             return torch.empty(*lead, self.out_features, dtype=torch.float32, device=x.device)
-        y = api.linear(self.packed, xb)
+        if torch.is_grad_enabled() and x2.requires_grad:
+            y = _PackedLinearFn.apply(x2, self.packed)
+        else:
+            y = api.linear(self.packed, x2.to(torch.bfloat16).contiguous())
         return y.reshape(*lead, self.out_features)
 
     def extra_repr(self) -> str:

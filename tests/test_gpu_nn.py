@@ -1,7 +1,8 @@
 """The PyTorch layer (block_planner_amd.nn) on the GPU: scan_model and
 wrap_model_with_hypertensor on a small BenchmarkMLP-shaped model, against the
 oracle and against ht_mlp_forward's per-layer path; skipped layers;
-inference-only memory; refresh; save / load round trip."""
+inference-only memory; refresh; save / load round trip; the input gradient
+through HyperLinear."""
 import numpy as np
 import pytest
 import torch
@@ -130,3 +131,23 @@ def test_save_load_round_trip(tmp_path):
         y2 = fresh(x)
     torch.cuda.synchronize()
     assert torch.equal(y, y2)
+
+
+@pytest.mark.parametrize("N,K,lead", [(320, 512, (6,)), (200, 192, (2, 3))])
+def test_input_gradient_through_hyperlinear(orc, N, K, lead):
+    """x.grad after backward through a HyperLinear equals dY . W_hat of the
+    oracle (fp64) within the bar; the weight gets no gradient."""
+    lin = torch.nn.Linear(K, N, bias=False).to(dev())
+    m = htnn.HyperLinear.from_linear(lin, inference_only=False)
+    x = torch.randn(*lead, K, device=dev(), requires_grad=True)
+    y = m(x)
+    g = torch.randn(*lead, N, device=dev())
+    (y * g).sum().backward()
+    assert x.grad is not None and x.grad.shape == x.shape and m.weight.grad is None
+    W = lin.weight.detach().cpu().numpy()
+    ref = orc.linear_backward_data(W, m.fmt.cpu().numpy(), g.reshape(-1, N).cpu().numpy())
+    got = x.grad.reshape(-1, K).cpu().numpy()
+    assert np.max(np.abs(got - ref)) <= 1e-3 * np.max(np.abs(ref))
+    # the forward under autograd is the same as without it
+    with torch.no_grad():
+        assert torch.equal(m(x), y.detach())
