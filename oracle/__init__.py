@@ -219,6 +219,19 @@ def linear_backward_data(W: np.ndarray, fmt: np.ndarray, dy: np.ndarray) -> np.n
     return dy @ dequant(W, fmt)
 
 
+def linear_backward_weight(dy: np.ndarray, x_bf16: np.ndarray) -> np.ndarray:
+    """dW [N, K] (double) = dY^T . x: the gradient for the fp32 master weight
+    under the straight-through estimator (the gradient of W_hat passed to W
+    unchanged), x being the bf16 activations the forward consumed and dY the
+    fp32 output gradient, both widened exactly (the pages' training support
+    with an STE)."""
+    dy = np.ascontiguousarray(dy, dtype=np.float32).astype(np.float64)
+    xb = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    assert dy.ndim == 2 and xb.ndim == 2 and dy.shape[0] == xb.shape[0]
+    x = (xb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return dy.T @ x
+
+
 def relu_bf16(z: np.ndarray) -> np.ndarray:
     """bfloat16 bits of max(z, 0), round to nearest even."""
     z = np.ascontiguousarray(z, dtype=np.float64)

@@ -664,3 +664,44 @@ def test_backward_data_dense_and_grid_cases():
     fmt8 = np.full((48, 3), INT8, np.uint8)
     np.testing.assert_allclose(oracle.linear_backward_data(Wg, fmt8, dy),
                                dy.astype(np.float64) @ Wg.astype(np.float64), rtol=1e-13, atol=1e-13)
+
+
+def test_backward_weight_is_the_adjoint():
+    """<dW, V> = <dY, x V^T> for random V, with x V^T from the oracle's
+    forward over all-FP32 blocks of V (its own C dot products, exact for
+    fp32 V): catches a transposed or mis-indexed weight gradient."""
+    import oracle
+
+    rng = np.random.default_rng(62)
+    M, N, K = 5, 48, 192
+    xb = wl.to_bf16_bits(rng.normal(size=(M, K)).astype(np.float32))
+    dy = rng.normal(size=(M, N)).astype(np.float32)
+    dw = oracle.linear_backward_weight(dy, xb)
+    assert dw.shape == (N, K)
+    for _ in range(3):
+        V = rng.normal(size=(N, K)).astype(np.float32)
+        xv = oracle.linear(V, np.full((N, K // 64), FP32, np.uint8), xb)
+        lhs = float(np.sum(dw * V.astype(np.float64)))
+        rhs = float(np.sum(dy.astype(np.float64) * xv))
+        assert abs(lhs - rhs) <= 1e-12 * np.sum(np.abs(dw * V.astype(np.float64)))
+
+
+def test_backward_weight_brute_force():
+    """Tiny case by plain loops, decoding bf16 bits with struct."""
+    import struct
+
+    import oracle
+
+    rng = np.random.default_rng(63)
+    M, N, K = 3, 4, 5
+    xb = rng.integers(0, 1 << 16, size=(M, K)).astype(np.uint16)
+    xb[(xb & 0x7F80) == 0x7F80] = 0x3F80            # no Inf / NaN
+    dy = rng.normal(size=(M, N)).astype(np.float32)
+    f = lambda b: struct.unpack("<f", struct.pack("<I", int(b) << 16))[0]
+    dw = oracle.linear_backward_weight(dy, xb)
+    for n in range(N):
+        for k in range(K):
+            ref = 0.0
+            for m in range(M):
+                ref += float(dy[m, n]) * f(xb[m, k])
+            assert dw[n, k] == pytest.approx(ref, rel=1e-12, abs=1e-300)
