@@ -325,7 +325,27 @@ def main() -> int:
                 del g
             res[name] = row
             del pw
-        return {"kernel": "linear_bwd_kernel<M>", "shapes": res}
+        # STE weight gradient dW = dY^T . x (fp32 [N, K] written): 4096 x 4096
+        wg = {}
+        for M in (1, 32):
+            dy = torch.randn(M, 4096, device=dev)
+            xb = torch.randn(M, 4096, device=dev).to(torch.bfloat16)
+            dw = torch.empty(4096, 4096, device=dev)
+            fn = lambda: api.linear_backward_weight(dy, xb, out=dw)
+            fn()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(10):
+                    fn()
+            g.replay()
+            torch.cuda.synchronize()
+            t = timed(lambda i: g.replay(), 5) / 10
+            nb = 4 * 4096 * 4096 + M * (2 * 4096 + 4 * 4096)
+            wg[f"M{M}"] = {"us": round(t * 1e6, 2), "GBps": round(nb / t / 1e9, 1)}
+            del g, dw
+        return {"kernel": "linear_bwd_kernel<M>", "shapes": res,
+                "weight_grad_4096": {"kernel": "linear_dw_kernel", **wg}}
 
     if args.only == "backward":
         print(json.dumps(backward_leg()))

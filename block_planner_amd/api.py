@@ -98,6 +98,17 @@ def linear_backward_data(pw: PackedLinear, dy: torch.Tensor, out: torch.Tensor |
     return dx
 
 
+def linear_backward_weight(dy: torch.Tensor, x_bf16: torch.Tensor, out: torch.Tensor | None = None,
+                           accumulate: bool = False, stream=None) -> torch.Tensor:
+    """dW = dY^T . x (STE gradient of the fp32 master; fp32 [N, K]); with
+    accumulate the product is added to `out`."""
+    M, N = dy.shape
+    K = x_bf16.shape[1]
+    dw = torch.empty((N, K), dtype=torch.float32, device=dy.device) if out is None else out
+    B.ht_linear_backward_weight(dy, x_bf16, dw, accumulate=accumulate, stream=stream)
+    return dw
+
+
 def mlp_workspace(layers: list, M: int, device, stream=None) -> torch.Tensor:
     """An initialised workspace for mlp() over these layers at batch M."""
     ws = workspace(B.ht_mlp_workspace([pw.desc for pw in layers], M), device)

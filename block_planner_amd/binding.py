@@ -25,7 +25,7 @@ STATUS = {0: "HT_OK", 1: "HT_EINVAL", 2: "HT_ESHAPE", 3: "HT_EALIGN", 4: "HT_ESM
 # Every symbol include/ht.h declares.
 EXPORTS = ("ht_status_string", "ht_plan_params_default", "ht_plan", "ht_plan_counts",
            "ht_pack_bytes", "ht_pack", "ht_linear_workspace", "ht_linear_forward",
-           "ht_linear_backward_workspace", "ht_linear_backward_data",
+           "ht_linear_backward_workspace", "ht_linear_backward_data", "ht_linear_backward_weight",
            "ht_mlp_workspace", "ht_workspace_init", "ht_mlp_forward")
 
 
@@ -85,6 +85,8 @@ def load() -> ctypes.CDLL:
     lib.ht_linear_backward_workspace.argtypes = [ctypes.POINTER(PackedWeight), I64, ctypes.POINTER(ctypes.c_size_t)]
     lib.ht_linear_backward_data.restype = St
     lib.ht_linear_backward_data.argtypes = [ctypes.POINTER(PackedWeight), P, I64, I64, P, I64, P, ctypes.c_size_t, P]
+    lib.ht_linear_backward_weight.restype = St
+    lib.ht_linear_backward_weight.argtypes = [P, I64, I64, P, I64, I64, I64, P, I64, I32, P]
     lib.ht_mlp_workspace.restype = St
     lib.ht_mlp_workspace.argtypes = [ctypes.POINTER(ctypes.POINTER(PackedWeight)), I32, I64,
                                      ctypes.POINTER(ctypes.c_size_t)]
@@ -195,6 +197,20 @@ def ht_linear_backward_data(desc: PackedWeight, dy, dx, ws=None, stream=None, M=
     wsb = (ws.numel() * ws.element_size() if ws is not None else 0) if ws_bytes is None else ws_bytes
     _check("ht_linear_backward_data", load().ht_linear_backward_data(ctypes.byref(desc), _ptr(dy), M, lddy, _ptr(dx),
                                                                      lddx, _ptr(ws), wsb, _stream(stream)))
+
+
+def ht_linear_backward_weight(dy, x, dw, accumulate=False, stream=None, M=None, N=None, K=None, lddy=None,
+                              ldx=None, lddw=None) -> None:
+    """x: bf16 (or its uint16 bits) [M, K]; dy fp32 [M, N]; dw fp32 [N, K]."""
+    M = dy.shape[0] if M is None else M
+    N = dw.shape[0] if N is None else N
+    K = dw.shape[1] if K is None else K
+    lddy = dy.stride(0) if lddy is None else lddy
+    ldx = x.stride(0) if ldx is None else ldx
+    lddw = dw.stride(0) if lddw is None else lddw
+    _check("ht_linear_backward_weight", load().ht_linear_backward_weight(_ptr(dy), M, lddy, _ptr(x), ldx, N, K,
+                                                                         _ptr(dw), lddw, 1 if accumulate else 0,
+                                                                         _stream(stream)))
 
 
 def _desc_array(descs):

@@ -279,3 +279,84 @@ ht_status run_bwd(const ht_packed_weight *w, const float *dy, int64_t M, int64_t
 }
 
 }  // namespace ht
+
+// ---------------------------------------------------------------------------
+// Weight gradient for the fp32 master weight under the straight-through
+// estimator (HyperTensor 1.0.1 page, "Design Philosophy": STE for the
+// backward pass): the gradient of W_hat is passed to W unchanged, so
+// dW[n, k] = sum over m of dY[m, n] * x[m, k], x being the bf16 activations
+// the forward consumed.  At training batch sizes the N x K fp32 output is
+// the traffic, so this is a plain coalesced kernel: workgroup (kc, nr) owns
+// columns [256 kc, 256 kc + 256) and rows [16 nr, 16 nr + 16); lane l of
+// wavefront v keeps 4 consecutive columns of rows v, v + 4, v + 8, v + 12,
+// adding the rows of dY / x in order (fixed order: bitwise reproducible).
+// ---------------------------------------------------------------------------
+namespace ht {
+
+constexpr uint32_t kDwCols = 256;
+constexpr uint32_t kDwRows = 16;
+
+__global__ __launch_bounds__(256) void linear_dw_kernel(const float *dy, int64_t lddy, const uint16_t *x, int64_t ldx,
+                                                        float *dw, int64_t lddw, uint32_t M, uint32_t N, uint32_t K,
+                                                        int accumulate) {
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t k = blockIdx.x * kDwCols + 4u * lane;
+    const uint32_t n0 = blockIdx.y * kDwRows + wave;
+    if (k >= K) return;                                     // K is a multiple of 4; no barrier below
+    uint32_t nc[4];                                         // row index clamped for the loads
+    bool live[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t n = n0 + 4u * r;
+        live[r] = n < N;
+        nc[r] = live[r] ? n : N - 1u;
+    }
+    float acc[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[r][c] = 0.0f;
+#pragma unroll 4
+    for (uint32_t m = 0; m < M; ++m) {
+        const uint2 xv = *reinterpret_cast<const uint2 *>(x + int64_t(m) * ldx + k);
+        const float xf[4] = {__uint_as_float(xv.x << 16), __uint_as_float(xv.x & 0xFFFF0000u),
+                             __uint_as_float(xv.y << 16), __uint_as_float(xv.y & 0xFFFF0000u)};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float g = live[r] ? dy[int64_t(m) * lddy + nc[r]] : 0.0f;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[r][c] = __builtin_fmaf(g, xf[c], acc[r][c]);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        if (!live[r]) continue;
+        float4 *p = reinterpret_cast<float4 *>(dw + int64_t(n0 + 4u * r) * lddw + k);
+        float4 o = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
+        if (accumulate) {
+            const float4 v = *p;
+            o = make_float4(v.x + o.x, v.y + o.y, v.z + o.z, v.w + o.w);
+        }
+        *p = o;
+    }
+}
+
+}  // namespace ht
+
+extern "C" ht_status ht_linear_backward_weight(const float *dy, int64_t M, int64_t lddy, const uint16_t *x,
+                                               int64_t ldx, int64_t N, int64_t K, float *dw, int64_t lddw,
+                                               int32_t accumulate, ht_stream stream) {
+    using namespace ht;
+    auto al16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+    if (!dw || (M > 0 && (!dy || !x))) return HT_EINVAL;
+    if (M < 0 || N <= 0 || K <= 0 || K % 4 || M > 0x7FFFFFFF || N > 0x7FFFFFFF || K > 0x7FFFFFFF) return HT_ESHAPE;
+    if ((M > 0 && (lddy < N || ldx < K || ldx % 4)) || lddw < K || lddw % 4) return HT_ESHAPE;
+    if ((N + kDwRows - 1) / kDwRows > 65535) return HT_ESHAPE;
+    if (!al16(dw) || (M > 0 && (!al16(dy) || !al16(x)))) return HT_EALIGN;
+    const dim3 grid(uint32_t((K + kDwCols - 1) / kDwCols), uint32_t((N + kDwRows - 1) / kDwRows));
+    hipLaunchKernelGGL(linear_dw_kernel, grid, dim3(256), 0, reinterpret_cast<hipStream_t>(stream), dy, lddy, x, ldx,
+                       dw, lddw, uint32_t(M), uint32_t(N), uint32_t(K), accumulate ? 1 : 0);
+    HT_LAUNCH_CHECK();
+    return HT_OK;
+}

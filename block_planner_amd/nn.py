@@ -15,10 +15,12 @@ Scope, as built:
     are and reported in the plan's "skipped" list with the reason.
   * The output is fp32 (the path's accumulation type); the input is cast to
     bfloat16 (round to nearest even) as the path defines.
-  * Gradients flow to the input only: dX = dY . W_hat by the library's
-    backward kernel (ht_linear_backward_data), in fp32; the rounding of x to
-    bfloat16 in the forward is passed straight through.  The packed weight
-    is frozen: no weight gradient and no update of the master weight.
+  * Backward: dX = dY . W_hat by the library's backward kernel
+    (ht_linear_backward_data), in fp32, the rounding of x to bfloat16 passed
+    straight through; and, when the module keeps a trainable fp32 master
+    weight, its straight-through gradient dW = dY^T . x_bf16
+    (ht_linear_backward_weight).  An optimizer updates the master; the packed
+    buffers follow it at the next refresh (refresh_every) or pack().
   * The planner modes named on the page (LOWEST ... BEST) have no definition
     there; only the per-block rule is accepted (option None or "PER_BLOCK").
   * refresh_every > 0 with a master weight re-plans and re-packs every that
@@ -43,17 +45,23 @@ def _eps(eps_int4=0.08, eps_int8=0.01, eps_bf16=0.0, eps_fp16=0.0, prefer_bf16=T
 
 
 class _PackedLinearFn(torch.autograd.Function):
-    """y = bf16(x) . W_hat^T forward; dX = dY . W_hat backward (fp32)."""
+    """y = bf16(x) . W_hat^T forward; backward dX = dY . W_hat and the STE
+    gradient of the master, dW = dY^T . bf16(x) (fp32)."""
 
     @staticmethod
-    def forward(ctx, x2: torch.Tensor, packed: api.PackedLinear) -> torch.Tensor:
+    def forward(ctx, x2: torch.Tensor, weight, packed: api.PackedLinear) -> torch.Tensor:
+        xb = x2.to(torch.bfloat16).contiguous()
         ctx.packed = packed
-        return api.linear(packed, x2.to(torch.bfloat16).contiguous())
+        if ctx.needs_input_grad[1]:
+            ctx.save_for_backward(xb)
+        return api.linear(packed, xb)
 
     @staticmethod
     def backward(ctx, dy: torch.Tensor):
-        dx = api.linear_backward_data(ctx.packed, dy.to(torch.float32).contiguous())
-        return dx, None
+        dy = dy.to(torch.float32).contiguous()
+        dx = api.linear_backward_data(ctx.packed, dy) if ctx.needs_input_grad[0] else None
+        dw = api.linear_backward_weight(dy, ctx.saved_tensors[0]) if ctx.needs_input_grad[1] else None
+        return dx, dw, None
 
 
 class HyperLinear(torch.nn.Module):
@@ -79,7 +87,7 @@ class HyperLinear(torch.nn.Module):
         dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
         w = torch.empty(out_features, in_features, dtype=torch.float32, device=dev)
         torch.nn.init.kaiming_uniform_(w, a=math.sqrt(5))      # nn.Linear's initialisation
-        self.weight = torch.nn.Parameter(w, requires_grad=False)
+        self.weight = torch.nn.Parameter(w, requires_grad=not self.inference_only)
         self.packed: api.PackedLinear | None = None
         self.fmt: torch.Tensor | None = None
         self._calls = 0
@@ -93,7 +101,8 @@ class HyperLinear(torch.nn.Module):
         m.in_features, m.out_features = lin.in_features, lin.out_features
         m.refresh_every, m.row_tile, m.inference_only = 0, int(row_tile), bool(inference_only)
         m.eps = _eps(**eps)
-        m.weight = torch.nn.Parameter(lin.weight.detach().to(torch.float32).contiguous(), requires_grad=False)
+        m.weight = torch.nn.Parameter(lin.weight.detach().to(torch.float32).contiguous(),
+                                      requires_grad=not m.inference_only)
         m.packed, m.fmt, m._calls = None, None, 0
         m.pack(fmt)
         return m
@@ -139,8 +148,9 @@ class HyperLinear(torch.nn.Module):
         x2 = x.reshape(-1, self.in_features)
         if x2.shape[0] == 0:
             return torch.empty(*lead, self.out_features, dtype=torch.float32, device=x.device)
-        if torch.is_grad_enabled() and x2.requires_grad:
-            y = _PackedLinearFn.apply(x2, self.packed)
+        w_grad = self.weight is not None and self.weight.requires_grad
+        if torch.is_grad_enabled() and (x2.requires_grad or w_grad):
+            y = _PackedLinearFn.apply(x2, self.weight if w_grad else None, self.packed)
         else:
             y = api.linear(self.packed, x2.to(torch.bfloat16).contiguous())
         return y.reshape(*lead, self.out_features)

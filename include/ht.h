@@ -231,6 +231,24 @@ ht_status ht_linear_backward_workspace(const ht_packed_weight *w, int64_t M, siz
 ht_status ht_linear_backward_data(const ht_packed_weight *w, const float *dy, int64_t M, int64_t lddy,
                                   float *dx, int64_t lddx, void *ws, size_t ws_bytes, ht_stream stream);
 
+/* ht_linear_backward_weight -- the gradient for the fp32 master weight under
+ * the straight-through estimator ("Design Philosophy": STE for the backward
+ * pass; "Key Features": training support): the gradient of W_hat is passed
+ * to W unchanged, so dw = dY^T . x.
+ *   dy     fp32 [M, lddy], lddy >= N (the gradient of y); M >= 0.
+ *   x      bf16 bits [M, ldx], ldx >= K, ldx % 4 == 0: the activations the
+ *          forward consumed.
+ *   dw     fp32 [N, lddw] out, lddw >= K, lddw % 4 == 0, K % 4 == 0:
+ *          dw[n, k] = sum_m dy[m, n] * x[m, k] in fp32, m in order (bitwise
+ *          reproducible); with accumulate != 0 that sum is added to dw
+ *          (gradient accumulation); M == 0 writes zeros (or leaves dw).
+ *   No workspace; dy, x and dw 16-byte aligned (HT_EALIGN), ceil(N / 16) at
+ *   most 65535 (HT_ESHAPE).  Needs no packed weight: the plan and the packed
+ *   buffers are rebuilt from the updated master by ht_plan / ht_pack. */
+ht_status ht_linear_backward_weight(const float *dy, int64_t M, int64_t lddy, const uint16_t *x, int64_t ldx,
+                                    int64_t N, int64_t K, float *dw, int64_t lddw, int32_t accumulate,
+                                    ht_stream stream);
+
 /* ht_mlp_workspace -- workspace bytes ht_mlp_forward needs for M rows. */
 ht_status ht_mlp_workspace(const ht_packed_weight *const *layers, int32_t n_layers,
                            int64_t M, size_t *bytes);

@@ -212,3 +212,19 @@ def test_backward_argument_checks():
     assert f(ctypes.byref(d), dy + 4, 3, 256, dx, 512, None, 0, None) == 3   # misaligned dy
     assert f(ctypes.byref(d), dy, 3, 256, dx, 512, None, 0, None) == 4       # workspace missing
     assert f(ctypes.byref(d), None, 3, 256, dx, 512, None, 0, None) == 1
+
+
+def test_backward_weight_argument_checks():
+    """Argument checks of ht_linear_backward_weight (return before any GPU
+    call): 1 EINVAL, 2 ESHAPE, 3 EALIGN."""
+    f = B.load().ht_linear_backward_weight
+    dy, x, dw = 0x200000, 0x300000, 0x400000
+    assert f(dy, 2, 64, x, 128, 64, 128, None, 128, 0, None) == 1            # no dw
+    assert f(None, 2, 64, x, 128, 64, 128, dw, 128, 0, None) == 1            # no dy with M > 0
+    assert f(dy, -1, 64, x, 128, 64, 128, dw, 128, 0, None) == 2             # M < 0
+    assert f(dy, 2, 64, x, 126, 64, 126, dw, 128, 0, None) == 2              # K % 4
+    assert f(dy, 2, 63, x, 128, 64, 128, dw, 128, 0, None) == 2              # lddy < N
+    assert f(dy, 2, 64, x, 130, 64, 128, dw, 128, 0, None) == 2              # ldx % 4
+    assert f(dy, 2, 64, x, 128, 64, 128, dw, 124, 0, None) == 2              # lddw < K
+    assert f(dy, 2, 64, x, 128, 16 * 65536, 128, dw, 128, 0, None) == 2      # too many row groups
+    assert f(dy, 2, 64, x + 8, 128, 64, 128, dw, 128, 0, None) == 3          # misaligned x

@@ -1,7 +1,9 @@
 """GPU parity of the input gradient (ht_linear_backward_data) against the
 oracle: dX = dY . W_hat within 1e-3 * max|dX_oracle| (oracle in fp64 from the
 same fp32 dY), over mixed and forced formats, ragged N, several launches of
-4 rows, row strides, full-size Llama-shaped weights, and bitwise determinism."""
+4 rows, row strides, full-size Llama-shaped weights, and bitwise determinism;
+and the STE weight gradient (ht_linear_backward_weight) against the oracle's
+dY^T . x."""
 import numpy as np
 import pytest
 import torch
@@ -91,3 +93,55 @@ def test_backward_row_tile_restriction():
     pw = api.pack(gpu(W), fmt, row_tile=8)
     with pytest.raises(B.HTError):
         B.ht_linear_backward_workspace(pw.desc, 1)
+
+
+# ---------------------------------------------------------------------------
+# STE weight gradient dW = dY^T . x
+# ---------------------------------------------------------------------------
+def _dw_case(M, N, K, seed, lddy=None, ldx=None, lddw=None):
+    rng = np.random.default_rng(seed)
+    dy = rng.normal(size=(M, lddy or N)).astype(np.float32)
+    xb = wl.to_bf16_bits(rng.normal(size=(M, ldx or K)).astype(np.float32))
+    return dy, xb
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 64), (5, 200, 192), (33, 96, 320), (3, 17, 1028)])
+def test_weight_grad_matches_oracle(orc, M, N, K):
+    dy, xb = _dw_case(M, N, K, 70 + M)
+    dw = torch.full((N, K), float("nan"), device=dev())
+    B.ht_linear_backward_weight(gpu(dy), gpu(xb.view(np.int16)), dw)
+    torch.cuda.synchronize()
+    check(dw.cpu().numpy(), orc.linear_backward_weight(dy, xb), f"dW M={M} N={N} K={K}")
+
+
+def test_weight_grad_accumulate_strides_determinism_and_empty(orc):
+    M, N, K = 7, 80, 256
+    dy, xb = _dw_case(M, N, K, 80, lddy=96, ldx=260)
+    ref = orc.linear_backward_weight(dy[:, :N], xb[:, :K])
+    base = torch.randn(N, 264, device=dev())
+    dw = base.clone()
+    args = dict(M=M, N=N, K=K, lddy=96, ldx=260, lddw=264)
+    B.ht_linear_backward_weight(gpu(dy), gpu(xb.view(np.int16)), dw, accumulate=True, **args)
+    torch.cuda.synchronize()
+    got = dw.cpu().numpy().astype(np.float64)
+    check(got[:, :K] - base.cpu().numpy()[:, :K], ref, "accumulate")
+    assert torch.equal(dw[:, K:], base[:, K:])                           # columns past K untouched
+    d1 = torch.empty(N, 264, device=dev())
+    d2 = torch.empty(N, 264, device=dev())
+    for d in (d1, d2):
+        B.ht_linear_backward_weight(gpu(dy), gpu(xb.view(np.int16)), d, **args)
+    torch.cuda.synchronize()
+    assert torch.equal(d1[:, :K], d2[:, :K])
+    z = torch.full((N, K), 5.0, device=dev())                            # M = 0: zeros, or left as is
+    B.ht_linear_backward_weight(gpu(dy), gpu(xb.view(np.int16)), z, M=0)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(z).item() == 0
+
+
+def test_weight_grad_full_size(orc):
+    """A 4096 x 4096 layer at 32 rows of dY, whole output against fp64."""
+    dy, xb = _dw_case(32, 4096, 4096, 90)
+    dw = torch.empty(4096, 4096, device=dev())
+    B.ht_linear_backward_weight(gpu(dy), gpu(xb.view(np.int16)), dw)
+    torch.cuda.synchronize()
+    check(dw.cpu().numpy(), orc.linear_backward_weight(dy, xb), "dW 4096x4096 M=32")

@@ -143,11 +143,33 @@ def test_input_gradient_through_hyperlinear(orc, N, K, lead):
     y = m(x)
     g = torch.randn(*lead, N, device=dev())
     (y * g).sum().backward()
-    assert x.grad is not None and x.grad.shape == x.shape and m.weight.grad is None
+    assert x.grad is not None and x.grad.shape == x.shape and m.weight.grad is not None
     W = lin.weight.detach().cpu().numpy()
-    ref = orc.linear_backward_data(W, m.fmt.cpu().numpy(), g.reshape(-1, N).cpu().numpy())
+    g2 = g.reshape(-1, N).cpu().numpy()
+    ref = orc.linear_backward_data(W, m.fmt.cpu().numpy(), g2)
     got = x.grad.reshape(-1, K).cpu().numpy()
     assert np.max(np.abs(got - ref)) <= 1e-3 * np.max(np.abs(ref))
+    # STE gradient of the master: dY^T . bf16(x)
+    xb = wl.to_bf16_bits(x.detach().reshape(-1, K).cpu().numpy())
+    refw = orc.linear_backward_weight(g2, xb)
+    assert np.max(np.abs(m.weight.grad.cpu().numpy() - refw)) <= 1e-3 * np.max(np.abs(refw))
     # the forward under autograd is the same as without it
     with torch.no_grad():
         assert torch.equal(m(x), y.detach())
+    # an optimizer step on the master, then a re-pack: the forward follows the new weight
+    torch.optim.SGD([m.weight], lr=0.5).step()
+    m.pack()
+    with torch.no_grad():
+        y2 = m(x).reshape(-1, N).cpu().numpy()
+    W2 = m.weight.detach().cpu().numpy()
+    assert not np.array_equal(W2, W)
+    yo = orc.linear(W2, orc.plan(W2), xb)
+    assert np.max(np.abs(y2 - yo)) <= 1e-3 * np.max(np.abs(yo))
+
+
+def test_inference_only_module_takes_no_weight_gradient():
+    lin = torch.nn.Linear(128, 64, bias=False).to(dev())
+    m = htnn.HyperLinear.from_linear(lin, inference_only=True)
+    x = torch.randn(3, 128, device=dev(), requires_grad=True)
+    m(x).sum().backward()
+    assert m.weight is None and x.grad is not None and torch.all(torch.isfinite(x.grad))
