@@ -286,15 +286,16 @@ ht_status run_bwd(const ht_packed_weight *w, const float *dy, int64_t M, int64_t
 // backward pass): the gradient of W_hat is passed to W unchanged, so
 // dW[n, k] = sum over m of dY[m, n] * x[m, k], x being the bf16 activations
 // the forward consumed.  At training batch sizes the N x K fp32 output is
-// the traffic, so this is a plain coalesced kernel: workgroup (kc, nr) owns
-// columns [256 kc, 256 kc + 256) and rows [16 nr, 16 nr + 16); lane l of
-// wavefront v keeps 4 consecutive columns of rows v, v + 4, v + 8, v + 12,
+// the traffic, so this is a plain coalesced kernel: workgroup (cx, ry) owns
+// columns [256 kc, 256 kc + 256) and kDwRows rows; lane l of wavefront v
+// keeps 4 consecutive columns of rows v, v + 4, v + 8, ... of that group,
 // adding the rows of dY / x in order (fixed order: bitwise reproducible).
 // ---------------------------------------------------------------------------
 namespace ht {
 
 constexpr uint32_t kDwCols = 256;
-constexpr uint32_t kDwRows = 16;
+constexpr int kDwRpt = 4;                        // rows per thread (one in 4: the wavefronts interleave)
+constexpr uint32_t kDwRows = 4 * kDwRpt;
 
 __global__ __launch_bounds__(256) void linear_dw_kernel(const float *dy, int64_t lddy, const uint16_t *x, int64_t ldx,
                                                         float *dw, int64_t lddw, uint32_t M, uint32_t N, uint32_t K,
@@ -304,17 +305,17 @@ __global__ __launch_bounds__(256) void linear_dw_kernel(const float *dy, int64_t
     const uint32_t k = blockIdx.x * kDwCols + 4u * lane;
     const uint32_t n0 = blockIdx.y * kDwRows + wave;
     if (k >= K) return;                                     // K is a multiple of 4; no barrier below
-    uint32_t nc[4];                                         // row index clamped for the loads
-    bool live[4];
+    uint32_t nc[kDwRpt];                                    // row index clamped for the loads
+    bool live[kDwRpt];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < kDwRpt; ++r) {
         const uint32_t n = n0 + 4u * r;
         live[r] = n < N;
         nc[r] = live[r] ? n : N - 1u;
     }
-    float acc[4][4];
+    float acc[kDwRpt][4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < kDwRpt; ++r)
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[r][c] = 0.0f;
 #pragma unroll 4
@@ -323,14 +324,14 @@ __global__ __launch_bounds__(256) void linear_dw_kernel(const float *dy, int64_t
         const float xf[4] = {__uint_as_float(xv.x << 16), __uint_as_float(xv.x & 0xFFFF0000u),
                              __uint_as_float(xv.y << 16), __uint_as_float(xv.y & 0xFFFF0000u)};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float g = live[r] ? dy[int64_t(m) * lddy + nc[r]] : 0.0f;
+        for (int r = 0; r < kDwRpt; ++r) {
+            const float g = live[r] ? dy[int64_t(m) * lddy + nc[r]] : 0.0f;   // wave-uniform
 #pragma unroll
             for (int c = 0; c < 4; ++c) acc[r][c] = __builtin_fmaf(g, xf[c], acc[r][c]);
         }
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < kDwRpt; ++r) {
         if (!live[r]) continue;
         float4 *p = reinterpret_cast<float4 *>(dw + int64_t(n0 + 4u * r) * lddw + k);
         float4 o = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
