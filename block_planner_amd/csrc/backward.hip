@@ -286,9 +286,11 @@ ht_status run_bwd(const ht_packed_weight *w, const float *dy, int64_t M, int64_t
 // backward pass): the gradient of W_hat is passed to W unchanged, so
 // dW[n, k] = sum over m of dY[m, n] * x[m, k], x being the bf16 activations
 // the forward consumed.  At training batch sizes the N x K fp32 output is
-// the traffic, so this is a plain coalesced kernel: workgroup (cx, ry) owns
-// columns [256 kc, 256 kc + 256) and kDwRows rows; lane l of wavefront v
-// keeps 4 consecutive columns of rows v, v + 4, v + 8, ... of that group,
+// the traffic, so this is a plain coalesced kernel of one-wavefront
+// workgroups (independent waves fill a compute unit's slots better than
+// 4-wave groups: 31.9 against 35.0 us at 32 rows of 4096 x 4096): workgroup
+// (cx, y) owns columns [256 cx, 256 cx + 256) and rows
+// 16 (y >> 2) + (y & 3) + 4 r, r < kDwRpt, lane l 4 consecutive columns,
 // adding the rows of dY / x in order (fixed order: bitwise reproducible).
 // ---------------------------------------------------------------------------
 namespace ht {
@@ -297,13 +299,13 @@ constexpr uint32_t kDwCols = 256;
 constexpr int kDwRpt = 4;                        // rows per thread (one in 4: the wavefronts interleave)
 constexpr uint32_t kDwRows = 4 * kDwRpt;
 
-__global__ __launch_bounds__(256) void linear_dw_kernel(const float *dy, int64_t lddy, const uint16_t *x, int64_t ldx,
+__global__ __launch_bounds__(64) void linear_dw_kernel(const float *dy, int64_t lddy, const uint16_t *x, int64_t ldx,
                                                         float *dw, int64_t lddw, uint32_t M, uint32_t N, uint32_t K,
                                                         int accumulate) {
     const uint32_t lane = threadIdx.x & 63;
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t wave = blockIdx.y & 3u;                  // one wavefront per workgroup
     const uint32_t k = blockIdx.x * kDwCols + 4u * lane;
-    const uint32_t n0 = blockIdx.y * kDwRows + wave;
+    const uint32_t n0 = (blockIdx.y >> 2) * kDwRows + wave;
     if (k >= K) return;                                     // K is a multiple of 4; no barrier below
     uint32_t nc[kDwRpt];                                    // row index clamped for the loads
     bool live[kDwRpt];
@@ -353,10 +355,10 @@ extern "C" ht_status ht_linear_backward_weight(const float *dy, int64_t M, int64
     if (!dw || (M > 0 && (!dy || !x))) return HT_EINVAL;
     if (M < 0 || N <= 0 || K <= 0 || K % 4 || M > 0x7FFFFFFF || N > 0x7FFFFFFF || K > 0x7FFFFFFF) return HT_ESHAPE;
     if ((M > 0 && (lddy < N || ldx < K || ldx % 4)) || lddw < K || lddw % 4) return HT_ESHAPE;
-    if ((N + kDwRows - 1) / kDwRows > 65535) return HT_ESHAPE;
+    if (4 * ((N + kDwRows - 1) / kDwRows) > 65535) return HT_ESHAPE;
     if (!al16(dw) || (M > 0 && (!al16(dy) || !al16(x)))) return HT_EALIGN;
-    const dim3 grid(uint32_t((K + kDwCols - 1) / kDwCols), uint32_t((N + kDwRows - 1) / kDwRows));
-    hipLaunchKernelGGL(linear_dw_kernel, grid, dim3(256), 0, reinterpret_cast<hipStream_t>(stream), dy, lddy, x, ldx,
+    const dim3 grid(uint32_t((K + kDwCols - 1) / kDwCols), 4u * uint32_t((N + kDwRows - 1) / kDwRows));
+    hipLaunchKernelGGL(linear_dw_kernel, grid, dim3(64), 0, reinterpret_cast<hipStream_t>(stream), dy, lddy, x, ldx,
                        dw, lddw, uint32_t(M), uint32_t(N), uint32_t(K), accumulate ? 1 : 0);
     HT_LAUNCH_CHECK();
     return HT_OK;

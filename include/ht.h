@@ -242,8 +242,8 @@ ht_status ht_linear_backward_data(const ht_packed_weight *w, const float *dy, in
  *          dw[n, k] = sum_m dy[m, n] * x[m, k] in fp32, m in order (bitwise
  *          reproducible); with accumulate != 0 that sum is added to dw
  *          (gradient accumulation); M == 0 writes zeros (or leaves dw).
- *   No workspace; dy, x and dw 16-byte aligned (HT_EALIGN), ceil(N / 16) at
- *   most 65535 (HT_ESHAPE).  Needs no packed weight: the plan and the packed
+ *   No workspace; dy, x and dw 16-byte aligned (HT_EALIGN), 4 * ceil(N / 16)
+ *   at most 65535 (HT_ESHAPE).  Needs no packed weight: the plan and the packed
  *   buffers are rebuilt from the updated master by ht_plan / ht_pack. */
 ht_status ht_linear_backward_weight(const float *dy, int64_t M, int64_t lddy, const uint16_t *x, int64_t ldx,
                                     int64_t N, int64_t K, float *dw, int64_t lddw, int32_t accumulate,

@@ -226,5 +226,5 @@ def test_backward_weight_argument_checks():
     assert f(dy, 2, 63, x, 128, 64, 128, dw, 128, 0, None) == 2              # lddy < N
     assert f(dy, 2, 64, x, 130, 64, 128, dw, 128, 0, None) == 2              # ldx % 4
     assert f(dy, 2, 64, x, 128, 64, 128, dw, 124, 0, None) == 2              # lddw < K
-    assert f(dy, 2, 64, x, 128, 16 * 65536, 128, dw, 128, 0, None) == 2      # too many row groups
+    assert f(dy, 2, 64, x, 128, 4 * 65536, 128, dw, 128, 0, None) == 2       # too many row groups
     assert f(dy, 2, 64, x + 8, 128, 64, 128, dw, 128, 0, None) == 3          # misaligned x
