@@ -74,6 +74,8 @@ def _load():
     lib.oracle_linear.argtypes = [P, I64, I64, I64, P, P, I64, I64, P, I64]
     lib.oracle_linear_sampled.restype = None
     lib.oracle_linear_sampled.argtypes = [P, I64, I64, P, P, I64, P, P, I64, P]
+    lib.oracle_relu.restype = None
+    lib.oracle_relu.argtypes = [P, I64, P]
     lib.oracle_relu_bf16.restype = None
     lib.oracle_relu_bf16.argtypes = [P, I64, P]
     lib.oracle_x_planes.restype = None
@@ -232,6 +234,14 @@ def linear_backward_weight(dy: np.ndarray, x_bf16: np.ndarray) -> np.ndarray:
     return dy.T @ x
 
 
+def relu(z: np.ndarray) -> np.ndarray:
+    """max(z, 0) in double with zero, negative values and NaN all giving +0."""
+    z = np.ascontiguousarray(z, dtype=np.float64)
+    out = np.zeros(z.shape, np.float64)
+    _load().oracle_relu(_ptr(z), z.size, _ptr(out))
+    return out
+
+
 def relu_bf16(z: np.ndarray) -> np.ndarray:
     """bfloat16 bits of max(z, 0), round to nearest even."""
     z = np.ascontiguousarray(z, dtype=np.float64)
@@ -251,7 +261,7 @@ def mlp(weights, fmts, x_bf16: np.ndarray):
             h = relu_bf16(z)
             hs.append(h)
         else:
-            return np.maximum(z, 0.0), hs
+            return relu(z), hs
     raise ValueError("no layers")
 
 

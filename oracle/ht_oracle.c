@@ -4,10 +4,10 @@
  * the tests, the smoke check and the benchmark's CPU-baseline leg load it.
  *
  * What it follows (HyperTensor 1.0.1 project page):
- *   - "What it does" / "Why HyperTensor?": every weight is analysed on its
- *     own, its reconstruction error is measured, and the lowest precision that
- *     stays safe is kept; the format set is INT4, INT8, FP16, BF16, FP32
- *     ("Design Philosophy": format-minimal).
+ *   - "What it does" / "Why HyperTensor?": each weight block is judged on
+ *     its own from the error every candidate format would leave, and the
+ *     cheapest format within its threshold is kept; the format set is INT4,
+ *     INT8, FP16, BF16, FP32 ("Design Philosophy": format-minimal).
  *   - "Key Features": per-block precision selection (PER_BLOCK).
  *   - "Convert model": eps_fp16 = eps_bf16 = 0 and prefer_bf16 = True are the
  *     defaults of the scan.
@@ -315,8 +315,18 @@ void oracle_linear_sampled(const float *W, int64_t K, int64_t ldw, const uint8_t
     }
 }
 
+/* ReLU in double, the last MLP layer's output (the page's BenchmarkMLP is
+ * Linear + ReLU, repeated): z where z > 0, else +0, so zero (of either
+ * sign), negative values and NaN all give +0.  The page does not say what
+ * ReLU does with NaN; this is the reading used for every layer. */
+void oracle_relu(const double *z, int64_t count, double *out)
+{
+    for (int64_t i = 0; i < count; ++i) out[i] = z[i] > 0.0 ? z[i] : 0.0;
+}
+
 /* ReLU followed by bfloat16 rounding, the activation handed from one MLP
- * layer to the next (the page's BenchmarkMLP is Linear + ReLU, repeated). */
+ * layer to the next (the page's BenchmarkMLP is Linear + ReLU, repeated);
+ * the same ReLU as oracle_relu. */
 void oracle_relu_bf16(const double *z, int64_t count, uint16_t *h)
 {
     for (int64_t i = 0; i < count; ++i) {

@@ -369,6 +369,49 @@ def test_sign_symmetry(orc):
         np.testing.assert_array_equal(q1, -q2)
 
 
+def test_int_quant_matrix_layout(orc):
+    """The matrix wrapper of the block quantiser: a non-square weight whose
+    every block lies on its own power-of-two INT8 grid with a distinct
+    exponent, so the scale of block (n, kb) is exactly 2^e[n, kb] and its
+    codes are the grid integers (closed form); a transposed or shifted scale
+    or code index fails.  Then the wrapper equals the block function block by
+    block on edge blocks, at every position of a ragged weight."""
+    rng = np.random.default_rng(46)
+    N, KB = 7, 5
+    e = rng.permutation(N * KB).reshape(N, KB) - 20          # distinct exponents
+    k = rng.integers(-127, 128, size=(N, KB, 64))
+    k[:, :, 0] = np.where(rng.random((N, KB)) < 0.5, 127, -127)   # |k| reaches 127 in every block
+    W = (k * np.ldexp(1.0, e)[:, :, None]).reshape(N, KB * 64).astype(np.float32)
+    s, q = orc.int_quant(W, 127)
+    np.testing.assert_array_equal(s, np.ldexp(1.0, e).astype(np.float32))
+    np.testing.assert_array_equal(q, k.reshape(N, KB * 64).astype(np.int8))
+    E = wl.edge_blocks()
+    W2 = np.ascontiguousarray(E[rng.integers(0, E.shape[0], size=(9, 3))].reshape(9, 192))
+    for Q in (7, 127):
+        s2, q2 = orc.int_quant(W2, Q)
+        assert s2.shape == (9, 3) and q2.shape == (9, 192)
+        for n in range(9):
+            for kb in range(3):
+                sb, qb = orc.int_quant_block(W2[n, 64 * kb:64 * kb + 64], Q)
+                assert s2[n, kb].tobytes() == np.float32(sb).tobytes(), (n, kb)
+                np.testing.assert_array_equal(q2[n, 64 * kb:64 * kb + 64], qb)
+
+
+def test_relu_special_values(orc):
+    """The ReLU of the MLP's last layer, by its reading (zero, negative and
+    NaN give +0): special values by hand, and max(z, 0) on finite z."""
+    z = np.array([2.5, -1.0, 0.0, -0.0, np.nan, -np.nan, np.inf, -np.inf, 5e-324, -5e-324, 1e308])
+    r = orc.relu(z)
+    want = np.array([2.5, 0.0, 0.0, 0.0, 0.0, 0.0, np.inf, 0.0, 5e-324, 0.0, 1e308])
+    assert r.tobytes() == want.tobytes()          # bit patterns: every zero is +0
+    zr = np.random.default_rng(47).normal(size=500)
+    np.testing.assert_array_equal(orc.relu(zr), np.maximum(zr, 0.0))
+    # the hidden layers' ReLU is the same map, then bf16 rounding
+    zz = np.concatenate([z, zr])
+    assert np.array_equal(orc.relu_bf16(zz), orc.relu_bf16(orc.relu(zz)))
+    assert orc.relu_bf16(np.array([np.nan]))[0] == 0
+
+
 def test_power_of_two_scaling(orc):
     W = wl.small_weight()
     f1 = orc.plan(W)
