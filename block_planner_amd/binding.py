@@ -24,7 +24,7 @@ STATUS = {0: "HT_OK", 1: "HT_EINVAL", 2: "HT_ESHAPE", 3: "HT_EALIGN", 4: "HT_ESM
 
 # Every symbol include/ht.h declares.
 EXPORTS = ("ht_status_string", "ht_plan_params_default", "ht_plan", "ht_plan_counts",
-           "ht_pack_bytes", "ht_pack", "ht_linear_workspace", "ht_linear_forward",
+           "ht_pack_bytes", "ht_pack", "ht_check_packed", "ht_linear_workspace", "ht_linear_forward",
            "ht_linear_backward_workspace", "ht_linear_backward_data", "ht_linear_backward_weight",
            "ht_mlp_workspace", "ht_workspace_init", "ht_mlp_forward")
 
@@ -76,6 +76,8 @@ def load() -> ctypes.CDLL:
     lib.ht_pack.restype = St
     lib.ht_pack.argtypes = [P, I64, I64, I64, P, I64, ctypes.POINTER(ctypes.c_int64), P, ctypes.c_size_t,
                             ctypes.POINTER(PackedWeight), P]
+    lib.ht_check_packed.restype = St
+    lib.ht_check_packed.argtypes = [ctypes.POINTER(PackedWeight), P, ctypes.c_size_t, P]
     lib.ht_linear_workspace.restype = St
     lib.ht_linear_workspace.argtypes = [ctypes.POINTER(PackedWeight), I64, I32, ctypes.POINTER(ctypes.c_size_t)]
     lib.ht_linear_forward.restype = St
@@ -164,6 +166,13 @@ def ht_pack(W, fmt_map, row_tile: int, counts, buf, stream=None, N=None, K=None,
     _check("ht_pack", load().ht_pack(_ptr(W), N, K, ldw, _ptr(fmt_map), row_tile, c, _ptr(buf), nbytes,
                                      ctypes.byref(desc), _stream(stream)))
     return desc
+
+
+def ht_check_packed(desc: PackedWeight, host_buf, fmt_out=None) -> None:
+    """host_buf, fmt_out: numpy arrays in host memory (uint8 bytes of the
+    packed buffer; uint8 [N, K/64] receiving the map the index describes)."""
+    fp = None if fmt_out is None else fmt_out.ctypes.data
+    _check("ht_check_packed", load().ht_check_packed(ctypes.byref(desc), host_buf.ctypes.data, host_buf.nbytes, fp))
 
 
 def ht_linear_workspace(desc: PackedWeight, M: int, path: int = HT_PATH_AUTO) -> int:

@@ -14,6 +14,7 @@
 // reproducible.  With several K-splits the per-split sums go to the
 // workspace and a second kernel adds them in split order.
 #include "gemv_common.h"
+#include "layout.h"
 #include "linear_host.h"
 
 namespace ht {
@@ -201,15 +202,7 @@ ht_status launch_gemv(const LinArgs &a, uint32_t T, uint32_t lds, hipStream_t s)
 
 }  // namespace
 
-bool desc_ok(const ht_packed_weight *w) {
-    if (!w || !w->base || w->layout_version != HT_LAYOUT_VERSION) return false;
-    if (w->N <= 0 || w->K <= 0 || w->K % kBlockK) return false;
-    const int64_t R = w->row_tile;
-    if (!(R == 1 || R == 2 || R == 4 || R == 8 || R == 16)) return false;
-    if (w->n_tiles != (w->N + R - 1) / R) return false;
-    if (w->bytes > 0xFFFFFFFFull) return false;   // addressed with 32-bit offsets
-    return true;
-}
+bool desc_ok(const ht_packed_weight *w) { return w && w->base && desc_layout_ok(w); }
 
 size_t linear_ws(const ht_packed_weight *w, int64_t M) {
     const int Mt = m_tile(M);
@@ -331,7 +324,7 @@ extern "C" ht_status ht_linear_backward_data(const ht_packed_weight *w, const fl
     if (!desc_ok(w) || !dy || !dx) return HT_EINVAL;
     if (!bwd_ok(w)) return HT_EINVAL;
     if (M <= 0 || lddy < w->N || lddx < w->K) return HT_ESHAPE;
-    if (!al16(dy) || !al16(dx)) return HT_EALIGN;
+    if (!al16(dy) || !al16(dx) || !al16(w->base)) return HT_EALIGN;
     const size_t need = bwd_ws(w, M);
     if (need && (!ws || ws_bytes < need)) return HT_ESMALL;
     if (ws && !al16(ws)) return HT_EALIGN;

@@ -7,7 +7,8 @@
 
 namespace ht {
 
-// A descriptor the kernels can use (layout version, shape, row tile).
+// A descriptor the kernels can use: layout version, shape, row tile, and
+// every region offset and the size equal to the layout of (N, K, R, counts).
 bool desc_ok(const ht_packed_weight *w);
 
 // Workspace bytes of one linear over M rows (the K-split partial sums).

@@ -16,8 +16,12 @@
 // Activation exchange without a barrier or cache flushes: a hidden layer's
 // outputs are ReLU values, so the sign bit of each bfloat16 is free.  Four
 // values are published with one 64-bit atomic store, their four sign bits
-// holding a 4-bit call tag (the workspace keeps a call counter; tags cycle
-// through 1..15, so a zero-initialised word never matches).  The activation
+// holding a 4-bit call tag.  The workspace keeps a call counter c in 0..14;
+// a call's tag is c + 1 (so a zero-initialised word never matches) and the
+// next call's counter is (c + 1) mod 15, so two consecutive calls never
+// share a tag.  The counter is advanced by the last workgroup to read it
+// (an arrival count next to it), so no workgroup of a call can see the next
+// call's value, whichever layers it owns tiles in.  The activation
 // wavefront of every workgroup reads the whole layer with 64-bit atomic
 // loads and re-reads any word whose tag is not yet the current one.  Every
 // word is written exactly once per call, so a matching tag means the word
@@ -29,6 +33,10 @@
 //
 // Per-layer path: one single-layer launch per layer (linear.hip), used when
 // the fused launch does not fit (layer count, batch, LDS, residency, tiles).
+#include <map>
+#include <mutex>
+#include <tuple>
+
 #include "gemv_common.h"
 #include "linear_host.h"
 
@@ -37,7 +45,7 @@ namespace ht {
 constexpr int kMaxLayers = 8;
 constexpr int kMaxFusedM = 4;
 constexpr uint32_t kSpinLimit = 1u << 21;   // x ~64 clocks per poll: ~50 ms
-constexpr uint32_t kSyncBytes = 256;        // [0] call counter, [2] expired-wait flag
+constexpr uint32_t kSyncBytes = 256;        // [0] call counter, [1] arrivals, [2] expired-wait flag
 constexpr uint32_t kLoadWaves = kWaves - 1; // waves streaming weights; the last one stages the input
 constexpr int kSlots = 2;                   // chunks in flight per loading wave
 constexpr uint32_t kLdsBudget = 160 * 1024; // LDS of one compute unit
@@ -106,7 +114,8 @@ __device__ __forceinline__ void stage_input(const uint16_t *x, int64_t ld, uint3
 }
 
 // The tag of a call: bit j of (counter mod 15) + 1 goes to the sign bit of
-// value j of every word.
+// value j of every word.  (The counter stays in 0..14; the reduction only
+// guards a workspace that was not initialised.)
 __device__ __forceinline__ uint64_t tag_bits(uint32_t counter) {
     const uint32_t tag = counter % 15u + 1u;
     return (uint64_t(tag & 1u) << 15) | (uint64_t((tag >> 1) & 1u) << 31) | (uint64_t((tag >> 2) & 1u) << 47) |
@@ -159,11 +168,17 @@ __global__ __launch_bounds__(kThreads) void mlp_fused_kernel(MlpArgs a) {
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t L = a.n_layers;
     const bool xwave = wave == kLoadWaves;
-    // the call counter is read before any word of this call can be written;
-    // workgroup 0 advances it after the last layer
+    // The call counter, then this workgroup's arrival (acquire: the arrival
+    // cannot be performed before the counter is read).  The last workgroup to
+    // arrive resets the arrival count and advances the counter: every
+    // workgroup of this call has read it by then, and the next call starts
+    // after this launch ends.
     const uint32_t epoch =
-        __builtin_amdgcn_readfirstlane(__hip_atomic_load(a.sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        __builtin_amdgcn_readfirstlane(__hip_atomic_load(a.sync, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT));
     const uint64_t tagmask = tag_bits(epoch);
+    uint32_t arrived_before = 0;   // used at the end, so the atomic's return is not waited for here
+    if (threadIdx.x == 0)
+        arrived_before = __hip_atomic_fetch_add(a.sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     // block ranges of this tile in every layer -> LDS (10 values per layer)
     if (threadIdx.x < 10 * L) {
@@ -277,8 +292,10 @@ __global__ __launch_bounds__(kThreads) void mlp_fused_kernel(MlpArgs a) {
             }
         }
     }
-    if (t == 0 && threadIdx.x == 0)
-        __hip_atomic_store(a.sync, epoch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0 && arrived_before + 1u == gridDim.x) {
+        __hip_atomic_store(a.sync + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.sync, (epoch % 15u + 1u) % 15u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 __global__ __launch_bounds__(256) void zero_fill_kernel(uint32_t *p, uint64_t n) {
@@ -297,30 +314,48 @@ struct MlpPlan {
     uint32_t grid = 0, lds = 0, xcap = 0, pcap = 0, rmax = 0;
 };
 
+// Workgroups of mlp_fused_kernel<M> that can be resident at once on the
+// current device with `lds` bytes of LDS each (compute units x occupancy);
+// 0 if a query fails.  Probed once per (device, M, LDS bytes): the probe
+// (and the LDS attribute the launch needs) costs host calls that would
+// otherwise land on every eager decode call.
 template <int M>
-bool fused_fits(uint32_t grid, uint32_t lds) {
-    // all workgroups must be resident at once: occupancy x compute units
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return false;
+uint64_t probe_capacity(int dev, uint32_t lds) {
     if (hipFuncSetAttribute(reinterpret_cast<const void *>(&mlp_fused_kernel<M>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(kLdsBudget)) != hipSuccess)
-        return false;
+        return 0;
     int cus = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&mlp_fused_kernel<M>),
                                                      kThreads, lds) != hipSuccess)
-        return false;
-    return uint64_t(per_cu) * uint64_t(cus) >= grid;
+        return 0;
+    return uint64_t(per_cu) * uint64_t(cus);
 }
 
 bool fused_fits_m(int64_t M, uint32_t grid, uint32_t lds) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return false;
+    static std::mutex mu;
+    static std::map<std::tuple<int, int64_t, uint32_t>, uint64_t> cache;
+    const auto key = std::make_tuple(dev, M, lds);
+    {
+        std::lock_guard<std::mutex> g(mu);
+        const auto it = cache.find(key);
+        if (it != cache.end()) return it->second >= grid;
+    }
+    uint64_t cap = 0;
     switch (M) {
-    case 1: return fused_fits<1>(grid, lds);
-    case 2: return fused_fits<2>(grid, lds);
-    case 3: return fused_fits<3>(grid, lds);
-    case 4: return fused_fits<4>(grid, lds);
+    case 1: cap = probe_capacity<1>(dev, lds); break;
+    case 2: cap = probe_capacity<2>(dev, lds); break;
+    case 3: cap = probe_capacity<3>(dev, lds); break;
+    case 4: cap = probe_capacity<4>(dev, lds); break;
     default: return false;
     }
+    if (cap) {
+        std::lock_guard<std::mutex> g(mu);
+        cache[key] = cap;
+    }
+    return cap >= grid;
 }
 
 // Shapes and buffer sizes; `probe_device` also checks residency (a HIP call).

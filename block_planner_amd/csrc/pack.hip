@@ -17,6 +17,7 @@
 //      with the planner's exact arithmetic.  Stores are 16 bytes per lane.
 //      Its last workgroup zeroes the alignment padding between regions, so
 //      every byte of the buffer is defined.
+#include "layout.h"
 #include "quant.h"
 
 namespace ht {
@@ -279,42 +280,6 @@ __global__ __launch_bounds__(256) void pack_scatter_kernel(PackArgs a, PadArgs p
 
 using namespace ht;
 
-namespace {
-
-struct Layout {
-    uint64_t kbidx, ids[5], scale[2], pay[5], end[12], total;
-    uint64_t used[12];   // bytes in use at the start of each region
-};
-
-ht_status layout_of(int64_t N, int64_t K, int64_t R, const int64_t c[5], Layout *L) {
-    if (N <= 0 || K <= 0 || K % kBlockK != 0) return HT_ESHAPE;
-    if (!(R == 1 || R == 2 || R == 4 || R == 8 || R == 16)) return HT_ESHAPE;
-    const int64_t KB = K / kBlockK;
-    if (KB * R > 65536) return HT_ESHAPE;
-    const int64_t T = (N + R - 1) / R;
-    if (T * KB + 1 > (int64_t(1) << 31)) return HT_ESHAPE;
-    int64_t tot = 0;
-    for (int f = 0; f < 5; ++f) {
-        if (c[f] < 0) return HT_EINVAL;
-        tot += c[f];
-    }
-    if (tot != N * KB) return HT_EINVAL;
-    uint64_t o = 0;
-    int k = 0;
-    L->kbidx = o; L->used[k++] = uint64_t(5) * uint64_t(T * KB + 1) * 4u; o += align256(L->used[0]);
-    for (int f = 0; f < 5; ++f) { L->ids[f] = o; L->used[k++] = 2u * uint64_t(c[f]); o += align256(2u * uint64_t(c[f])); }
-    for (int f = 0; f < 2; ++f) { L->scale[f] = o; L->used[k++] = 4u * uint64_t(c[f]); o += align256(4u * uint64_t(c[f])); }
-    for (int f = 0; f < 5; ++f) {
-        L->pay[f] = o;
-        L->used[k++] = uint64_t(pay_bytes(f)) * uint64_t(c[f]);
-        o += align256(uint64_t(pay_bytes(f)) * uint64_t(c[f]));
-    }
-    L->total = o;
-    if (o > 0xFFFFFFFFull) return HT_ESHAPE;   // the kernels address the buffer with 32-bit offsets
-    return HT_OK;
-}
-
-}  // namespace
 
 extern "C" ht_status ht_pack_bytes(int64_t N, int64_t K, int64_t row_tile, const int64_t counts5[5],
                                    size_t *bytes) {

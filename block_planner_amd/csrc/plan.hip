@@ -1,7 +1,9 @@
 // plan.hip -- the precision planner on gfx950 (HyperTensor 1.0.1 page, "What
-// it does": analyse each weight block on its own, measure its reconstruction
-// error per format, assign the lowest safe precision; "Convert model": the
-// scan's thresholds eps_fp16 = eps_bf16 = 0 and prefer_bf16 by default).
+// it does" and "Key Features": per-block format choice from measured error;
+// "Convert model": zero thresholds for the 16-bit formats and bfloat16 tried
+// first, by default).  For every 64-wide K-block the kernel computes the
+// error each candidate format would leave and keeps the cheapest format
+// whose relative error is within that format's threshold.
 //
 // Work layout: 4 lanes per 64-entry K-block, 16 consecutive fp32 entries per
 // lane held in registers, 16 blocks per wavefront, 64 blocks per 256-thread

@@ -2,9 +2,9 @@
 // packer kernels.  Layout of the work: one 64-entry K-block is held by 4
 // consecutive lanes, lane part p owning entries [16p, 16p+16) in registers.
 //
-// Block rule (HyperTensor 1.0.1 page, "What it does": measure the
-// reconstruction error, keep the lowest safe format; the numeric rule is
-// the method's specification):
+// Block rule (HyperTensor 1.0.1 page, "What it does": the format of a block
+// follows from the error each format leaves; the numeric rule is the
+// method's specification):
 //   s = fl32(max|w| / Q), Q = 7 (INT4) or 127 (INT8), correctly rounded;
 //   q = clamp(round_half_even(fl32(w / s)), -Q, Q); q = 0 if s is 0 or not
 //   finite.

@@ -44,6 +44,15 @@ def _eps(eps_int4=0.08, eps_int8=0.01, eps_bf16=0.0, eps_fp16=0.0, prefer_bf16=T
                 eps_fp16=float(eps_fp16), prefer_bf16=bool(prefer_bf16))
 
 
+def _check_row_tile(row_tile: int, inference_only: bool) -> None:
+    if int(row_tile) not in (1, 2, 4, 8, 16):
+        raise ValueError("row_tile must be one of 1, 2, 4, 8, 16")
+    if not inference_only and int(row_tile) != 16:
+        # the input-gradient kernel reads 16-row tiles; refuse now rather than
+        # in the first backward pass
+        raise ValueError("a trainable HyperLinear needs row_tile 16 (the backward kernels' tile)")
+
+
 class _PackedLinearFn(torch.autograd.Function):
     """y = bf16(x) . W_hat^T forward; backward dX = dY . W_hat and the STE
     gradient of the master, dW = dY^T . bf16(x) (fp32)."""
@@ -79,6 +88,7 @@ class HyperLinear(torch.nn.Module):
             raise ValueError("HyperLinear has no bias (the per-block linear is y = x . W_hat^T)")
         if in_features % 64:
             raise ValueError("in_features must be a multiple of 64 (64-wide K-blocks)")
+        _check_row_tile(row_tile, inference_only)
         self.in_features, self.out_features = int(in_features), int(out_features)
         self.refresh_every = int(refresh_every)
         self.row_tile = int(row_tile)
@@ -96,6 +106,7 @@ class HyperLinear(torch.nn.Module):
     @classmethod
     def from_linear(cls, lin: torch.nn.Linear, fmt: torch.Tensor | None = None, inference_only: bool = True,
                     row_tile: int = 16, **eps) -> "HyperLinear":
+        _check_row_tile(row_tile, inference_only)
         m = cls.__new__(cls)
         torch.nn.Module.__init__(m)
         m.in_features, m.out_features = lin.in_features, lin.out_features
@@ -243,31 +254,64 @@ def save_hypertensor(model: torch.nn.Module, path: str) -> None:
     save_file(tensors, path, metadata={"hypertensor_layers": json.dumps(meta)})
 
 
-def load_hypertensor(model: torch.nn.Module, path: str, device=None) -> torch.nn.Module:
-    """Put the packed layers saved by save_hypertensor into `model` (whose
-    modules of those names are replaced by inference-only HyperLinear).  The
-    packed bytes are copied to a 256-byte aligned device buffer."""
+def read_hypertensor(path: str) -> list:
+    """The packed layers of a file written by save_hypertensor, validated in
+    host memory before anything reaches a device: each descriptor must match
+    the layout of its (N, K, row tile, counts) and each buffer's block index
+    must describe a format map (ht_check_packed), equal to the stored map
+    when one is stored.  Returns [(name, host uint8 tensor, PackedWeight with
+    base unset, counts, host fmt uint8 [N, K/64] or None)]; raises ValueError
+    for a file that fails."""
+    import numpy as np
     from safetensors import safe_open
 
-    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    out = []
     with safe_open(path, framework="pt") as f:
         meta = json.loads(f.metadata()["hypertensor_layers"])
+        keys = set(f.keys())
         for name, m in meta.items():
-            host = f.get_tensor(f"{name}.packed")
-            buf = api._aligned_empty(host.numel(), dev)
-            buf.copy_(host)
-            d = B.PackedWeight()
-            for fld in _DESC_FIELDS:
-                setattr(d, fld, m[fld])
-            for i, v in enumerate(m["counts"]):
-                d.counts[i] = v
-            for i, v in enumerate(m["off_ids"]):
-                d.off_ids[i] = v
-            for i, v in enumerate(m["off_scale"]):
-                d.off_scale[i] = v
-            for i, v in enumerate(m["off_payload"]):
-                d.off_payload[i] = v
-            d.base = buf.data_ptr()
-            fmt = f.get_tensor(f"{name}.fmt").to(dev) if f"{name}.fmt" in f.keys() else None
-            _set_child(model, name, HyperLinear.from_packed(api.PackedLinear(buf, d, list(m["counts"])), fmt))
+            try:
+                host = f.get_tensor(f"{name}.packed")
+                if host.dtype != torch.uint8 or host.dim() != 1:
+                    raise ValueError("packed buffer is not a 1-D uint8 tensor")
+                d = B.PackedWeight()
+                for fld in _DESC_FIELDS:
+                    setattr(d, fld, int(m[fld]))
+                for arr, key, n in ((d.counts, "counts", 5), (d.off_ids, "off_ids", 5),
+                                    (d.off_scale, "off_scale", 2), (d.off_payload, "off_payload", 5)):
+                    vals = [int(v) for v in m[key]]
+                    if len(vals) != n:
+                        raise ValueError(f"{key} has {len(vals)} entries, expected {n}")
+                    for i, v in enumerate(vals):
+                        arr[i] = v
+                if host.numel() != int(d.bytes):
+                    raise ValueError(f"buffer holds {host.numel()} bytes, descriptor says {int(d.bytes)}")
+                hb = host.numpy()
+                fmt_idx = np.zeros((int(d.N), int(d.K) // 64), np.uint8)
+                B.ht_check_packed(d, hb, fmt_idx)
+                fmt = None
+                if f"{name}.fmt" in keys:
+                    fmt = f.get_tensor(f"{name}.fmt")
+                    if tuple(fmt.shape) != fmt_idx.shape or not np.array_equal(fmt.numpy(), fmt_idx):
+                        raise ValueError("stored format map differs from the buffer's block index")
+            except (B.HTError, KeyError, TypeError, OverflowError) as e:
+                raise ValueError(f"{path}: layer {name!r} is not a valid packed weight: {e}") from e
+            except ValueError as e:
+                raise ValueError(f"{path}: layer {name!r} is not a valid packed weight: {e}") from e
+            out.append((name, host, d, [int(c) for c in m["counts"]], fmt))
+    return out
+
+
+def load_hypertensor(model: torch.nn.Module, path: str, device=None) -> torch.nn.Module:
+    """Put the packed layers saved by save_hypertensor into `model` (whose
+    modules of those names are replaced by inference-only HyperLinear).  Every
+    layer is validated on the host first (read_hypertensor); the packed bytes
+    are then copied to a 256-byte aligned device buffer."""
+    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    for name, host, d, counts, fmt in read_hypertensor(path):
+        buf = api._aligned_empty(host.numel(), dev)
+        buf.copy_(host)
+        d.base = buf.data_ptr()
+        fmt_d = fmt.to(dev) if fmt is not None else None
+        _set_child(model, name, HyperLinear.from_packed(api.PackedLinear(buf, d, counts), fmt_d))
     return model

@@ -1,11 +1,12 @@
 /*
  * ht.h -- C ABI of the MI355X (gfx950) per-block mixed-precision linear.
  *
- * The method (HyperTensor 1.0.1 project page): a precision planner measures
- * the reconstruction error of each weight block and keeps the lowest format
- * that stays safe ("What it does", "Key Features": per-block selection among
- * INT4 / INT8 / FP16 / BF16 / FP32); the map it produces becomes packed
- * buffers that fused kernels multiply from (intro paragraph).  The page's user calls map onto this ABI as follows:
+ * The method (HyperTensor 1.0.1 project page): a precision planner computes,
+ * per weight block, the reconstruction error of each candidate format and
+ * keeps the cheapest one within its threshold ("What it does", "Key
+ * Features": per-block selection among INT4 / INT8 / FP16 / BF16 / FP32); the
+ * resulting map becomes packed buffers that fused kernels multiply from
+ * (intro paragraph).  The page's user calls map onto this ABI as follows:
  *   scan_model(...)                    ("Convert model")  -> ht_plan
  *   wrap_model_with_hypertensor(...)   ("Convert model")  -> ht_pack
  *   HyperLinear(...).forward           ("Usage Example")  -> ht_linear_forward
@@ -25,6 +26,9 @@
  *     the format map and the count array (1 and 8 bytes).
  *   - Calls are re-entrant.  Two calls that share a workspace must not
  *     overlap in time (use one stream, or one workspace per stream).
+ *   - A packed-weight descriptor is accepted only when its shape, row tile,
+ *     every region offset and its size equal what ht_pack computes from
+ *     (N, K, row_tile, counts); otherwise the call returns HT_EINVAL.
  */
 #ifndef HT_H
 #define HT_H
@@ -123,8 +127,9 @@ const char *ht_status_string(ht_status s);
 /* Fill *p with the defaults listed in ht_plan_params. */
 void ht_plan_params_default(ht_plan_params *p);
 
-/* ht_plan -- the precision planner ("What it does": analyse each weight,
- * assign the lowest safe precision; "Key Features": per-block selection).
+/* ht_plan -- the precision planner ("What it does", "Key Features": per-block
+ * selection): each block gets the cheapest format whose error is within its
+ * threshold.
  *   W        fp32 [N, ldw], row-major; block (n, kb) = W[n, 64kb .. 64kb+63].
  *   N, K     K % 64 == 0; ldw >= K.
  *   p        (host) thresholds; NULL means the defaults.
@@ -164,6 +169,23 @@ ht_status ht_pack(const float *W, int64_t N, int64_t K, int64_t ldw,
                   const uint8_t *fmt_map, int64_t row_tile, const int64_t counts5[5],
                   void *buf, size_t buf_bytes, ht_packed_weight *desc, ht_stream stream);
 
+/* ht_check_packed -- validate a packed weight held in HOST memory (e.g. one
+ * read from a file) before it is copied to the device and handed to the
+ * kernels.  Host only: no GPU work, nothing enqueued.
+ *   w        (host) descriptor; w->base is not looked at.
+ *   buf      (host) the packed bytes, buf_bytes of them.
+ *   fmt      (host, nullable) uint8 [N, K/64] out: the format map the
+ *            buffer's block index describes.
+ * HT_OK when the descriptor passes the checks every entry point makes (see
+ * the conventions above) and the block index is that of a format map: for
+ * every format, kbidx starts at 0, never decreases and ends at the format's
+ * count; each (tile, K-block) column holds every row of the tile exactly
+ * once over the five formats, rows ascending within a format, each id naming
+ * that K-block.  HT_EINVAL otherwise; HT_ESMALL when buf_bytes < w->bytes.
+ * Payload bytes and scales are not checked (any bytes decode to finite or
+ * non-finite values the kernels handle). */
+ht_status ht_check_packed(const ht_packed_weight *w, const void *buf, size_t buf_bytes, uint8_t *fmt);
+
 /* ht_linear_workspace -- workspace bytes ht_linear_forward needs for M rows
  * on `path` (HT_PATH_AUTO, HT_PATH_GEMV, HT_PATH_GEMM, HT_PATH_GEMV_MFMA or
  * HT_PATH_GEMM_I8; HT_EINVAL for HT_PATH_GEMV_MFMA and HT_PATH_GEMM_I8 with a
@@ -184,8 +206,10 @@ ht_status ht_linear_workspace(const ht_packed_weight *w, int64_t M, int32_t path
  *          (for decode, M of a few rows);
  *          HT_PATH_GEMM: blocks dequantised into LDS as bfloat16 (integer
  *          codes exactly; FP16 and FP32 entries as a hi + lo pair, exact for
- *          FP16 and to 16 significant bits for FP32) and multiplied with
- *          bf16 MFMA, fp32 accumulation (for prefill, many rows);
+ *          FP16 and to 16 significant bits for normal FP32 entries, to
+ *          2^-133 absolute for fp32 subnormals; an Inf or NaN entry gives
+ *          NaN in its output column) and multiplied with bf16 MFMA, fp32
+ *          accumulation (for prefill, many rows);
  *          HT_PATH_GEMV_MFMA: for decode at a few to a few tens of rows
  *          (row tile 16 only, else HT_EINVAL): each block is dequantised
  *          in registers straight into the operands of bf16 MFMAs (the same
@@ -202,7 +226,12 @@ ht_status ht_linear_workspace(const ht_packed_weight *w, int64_t M, int32_t path
  *          round-half-even, 2^(E-1) <= max_k |x[m,k]| < 2^E, so
  *          |x_hat - x| <= 2^-14 max_k |x[m,k]|; such a tile computes
  *          x_hat . W_hat^T with exact int32 block sums (a row holding Inf or
- *          NaN gives NaN there).  The workspace holds the encoded x
+ *          NaN gives NaN there).  Range: those tiles add scale * block sum
+ *          with the row's 2^(E-14) applied to the finished sum, so their
+ *          running sums are 2^(14-E) times the output; an output whose
+ *          2^(14-E) sum_k |w_hat[n,k] x_hat[m,k]| reaches FLT_MAX (weights
+ *          of magnitude ~1e30 and more) may overflow to Inf or NaN, where
+ *          HT_PATH_GEMM would not.  The workspace holds the encoded x
  *          (unless the weight has too few INT8 blocks for any tile, when
  *          the call is HT_PATH_GEMM's); HT_PATH_AUTO never picks this path;
  *          HT_PATH_AUTO: GEMV_MFMA for 4 <= M <= 32 with row tile 16;

@@ -94,13 +94,29 @@ def test_plan_counts_argument_checks():
     assert lib.ht_plan_counts(0x10000, 4, 64, 0x10004, None) == 3
 
 
-def _desc(N=256, K=256, R=16, base=0x100000):
+def _desc(N=256, K=256, R=16, base=0x100000, counts=None):
+    """A descriptor consistent with the layout of (N, K, R, counts) (by
+    default every block INT8), offsets from the oracle's own layout
+    function; no buffer behind it."""
+    import oracle
     d = B.PackedWeight()
     d.N, d.K, d.row_tile, d.n_tiles = N, K, R, (N + R - 1) // R
-    d.bytes = N * K            # about one byte per weight, as for an INT8-heavy plan
+    counts = [0, N * (K // 64), 0, 0, 0] if counts is None else counts
+    size, offs = oracle.pack_layout(N, K, R, counts)
+    for f in range(5):
+        d.counts[f] = counts[f]
+        d.off_ids[f] = offs[1 + f]
+        d.off_payload[f] = offs[8 + f]
+    d.off_kbidx = offs[0]
+    d.off_scale[0], d.off_scale[1] = offs[6], offs[7]
+    d.bytes = size
     d.layout_version = 1
     d.base = base
     return d
+
+
+def _with_counts(d, counts):
+    return _desc(int(d.N), int(d.K), int(d.row_tile), d.base, counts)
 
 
 def test_linear_argument_checks():
@@ -151,11 +167,11 @@ def test_linear_argument_checks():
         Mt = min(M, 8192)
         G, KB = (Mt + 15) // 16, dsc.K // 64
         extra = a256(G * KB * 2048) + a256(G * 16 * 4)
-        dsc.counts[1] = 0
+        dsc = _with_counts(dsc, [0, 0, 0, 0, dsc.N * KB])
         assert B.ht_linear_workspace(dsc, M, B.HT_PATH_GEMM_I8) == B.ht_linear_workspace(dsc, Mt, B.HT_PATH_GEMM)
-        dsc.counts[1] = dsc.N * KB - 1
+        dsc = _with_counts(dsc, [0, dsc.N * KB - 1, 0, 0, 1])
         assert B.ht_linear_workspace(dsc, M, B.HT_PATH_GEMM_I8) == extra + B.ht_linear_workspace(dsc, Mt, B.HT_PATH_GEMM)
-        dsc.counts[1] = dsc.N * KB
+        dsc = _with_counts(dsc, [0, dsc.N * KB, 0, 0, 0])
         tiles = (Mt + 127) // 128 * ((dsc.N + 255) // 256)
         S = 1
         if tiles * 4 < 3 * 256 and KB >= 16:
@@ -163,7 +179,6 @@ def test_linear_argument_checks():
             KBs = -(-KB // S)
             S = -(-KB // KBs)
         assert B.ht_linear_workspace(dsc, M, B.HT_PATH_GEMM_I8) == extra + (S * Mt * dsc.N * 4 if S > 1 else 0)
-        dsc.counts[1] = 0
     for R in (1, 2, 4, 8):
         with pytest.raises(B.HTError):
             B.ht_linear_workspace(_desc(N=256, K=4096, R=R), 64, B.HT_PATH_GEMM_I8)
@@ -228,3 +243,158 @@ def test_backward_weight_argument_checks():
     assert f(dy, 2, 64, x, 128, 64, 128, dw, 124, 0, None) == 2              # lddw < K
     assert f(dy, 2, 64, x, 128, 4 * 65536, 128, dw, 128, 0, None) == 2       # too many row groups
     assert f(dy, 2, 64, x + 8, 128, 64, 128, dw, 128, 0, None) == 3          # misaligned x
+
+
+# ---------------------------------------------------------------------------
+# Descriptors that do not match their layout, and packed buffers whose block
+# index is not that of a format map, are refused on the host.
+# ---------------------------------------------------------------------------
+def _packed_host(orc, N=37, K=320, R=16, seed=3):
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    W = (rng.normal(size=(N, K)) * 0.05).astype(np.float32)
+    fmt = rng.integers(0, 5, size=(N, K // 64)).astype(np.uint8)
+    buf = orc.pack(W, fmt, R)
+    counts = [int(c) for c in np.bincount(fmt.ravel(), minlength=5)]
+    return _desc(N, K, R, counts=counts), buf, fmt
+
+
+@pytest.mark.parametrize("N,K,R", [(37, 320, 16), (64, 256, 4), (5, 64, 1), (33, 192, 8), (16, 128, 2)])
+def test_check_packed_accepts_packer_output(orc, N, K, R):
+    import numpy as np
+    d, buf, fmt = _packed_host(orc, N, K, R)
+    out = np.full_like(fmt, 9)
+    B.ht_check_packed(d, buf, out)
+    np.testing.assert_array_equal(out, fmt)
+
+
+def _kbidx(d, buf):
+    import numpy as np
+    nk = int(d.n_tiles) * (int(d.K) // 64) + 1
+    return buf[int(d.off_kbidx):int(d.off_kbidx) + 20 * nk].view(np.uint32).reshape(5, nk)
+
+
+def _ids(d, buf, f):
+    import numpy as np
+    return buf[int(d.off_ids[f]):int(d.off_ids[f]) + 2 * int(d.counts[f])].view(np.uint16)
+
+
+def _t_kbidx_start(d, buf):
+    _kbidx(d, buf)[1, 0] = 1
+
+
+def _t_kbidx_decreasing(d, buf):
+    k = _kbidx(d, buf)
+    f = int(k[:, -1].argmax())
+    c = int((k[f] > 0).argmax())   # first column with a nonzero prefix
+    k[f, c] = k[f, c + 1] + 1 if c + 1 < k.shape[1] else k[f, c] + 1
+
+
+def _t_kbidx_total(d, buf):
+    _kbidx(d, buf)[4, -1] += 1
+
+
+def _t_id_wrong_kb(d, buf):
+    ids = _ids(d, buf, 1)
+    ids[0] += int(d.row_tile)      # same row, next K-block
+
+
+def _t_id_row_past_ragged_tile(d, buf):
+    # the last tile of N = 37, R = 16 holds rows 0..4: move a block there to row 7
+    k = _kbidx(d, buf)
+    KB = int(d.K) // 64
+    c = (int(d.n_tiles) - 1) * KB
+    for f in range(5):
+        if k[f, c + 1] > k[f, c]:
+            ids = _ids(d, buf, f)
+            j = int(k[f, c])
+            ids[j] = (int(ids[j]) & 0xFFF0) | 7
+            return
+    raise AssertionError("no block in the last column")
+
+
+def _t_duplicate_row(d, buf):
+    k = _kbidx(d, buf)
+    for f in range(5):
+        for c in range(k.shape[1] - 1):
+            if k[f, c + 1] - k[f, c] >= 2:
+                ids = _ids(d, buf, f)
+                ids[int(k[f, c]) + 1] = ids[int(k[f, c])]
+                return
+    raise AssertionError("no column with two blocks of one format")
+
+
+def _t_rows_out_of_order(d, buf):
+    k = _kbidx(d, buf)
+    for f in range(5):
+        for c in range(k.shape[1] - 1):
+            if k[f, c + 1] - k[f, c] >= 2:
+                ids = _ids(d, buf, f)
+                j = int(k[f, c])
+                ids[j], ids[j + 1] = int(ids[j + 1]), int(ids[j])
+                return
+    raise AssertionError("no column with two blocks of one format")
+
+
+def _t_offset(d, buf):
+    d.off_payload[4] += 256
+
+
+def _t_bytes(d, buf):
+    d.bytes += 256
+
+
+def _t_counts_swapped(d, buf):
+    # counts that still add up and give a consistent layout, but not the
+    # index's totals
+    c = [int(v) for v in d.counts]
+    c[0], c[4] = c[0] + 1, c[4] - 1
+    nd = _with_counts(d, c)
+    ctypes.memmove(ctypes.addressof(d), ctypes.addressof(nd), ctypes.sizeof(d))
+
+
+def _t_version(d, buf):
+    d.layout_version = 2
+
+
+@pytest.mark.parametrize("tamper", [_t_kbidx_start, _t_kbidx_decreasing, _t_kbidx_total, _t_id_wrong_kb,
+                                    _t_id_row_past_ragged_tile, _t_duplicate_row, _t_rows_out_of_order,
+                                    _t_offset, _t_bytes, _t_counts_swapped, _t_version])
+def test_check_packed_refuses_tampering(orc, tamper):
+    d, buf, _ = _packed_host(orc)
+    tamper(d, buf)
+    with pytest.raises(B.HTError) as e:
+        B.ht_check_packed(d, buf)
+    assert e.value.code == 1
+
+
+def test_check_packed_short_buffer(orc):
+    d, buf, _ = _packed_host(orc)
+    with pytest.raises(B.HTError) as e:
+        B.ht_check_packed(d, buf[:-1])
+    assert e.value.code == 4
+
+
+@pytest.mark.parametrize("tamper", [_t_offset, _t_bytes, _t_version])
+def test_entry_points_refuse_tampered_descriptors(tamper):
+    """Every entry point that takes a descriptor refuses one whose offsets or
+    size do not match its layout, before anything is launched."""
+    lib = B.load()
+    d = _desc(N=256, K=512)
+    tamper(d, None)
+    out = ctypes.c_size_t(0)
+    x, y, ws = 0x200000, 0x300000, 0x400000
+    assert lib.ht_linear_workspace(ctypes.byref(d), 1, 0, ctypes.byref(out)) == 1
+    assert lib.ht_linear_forward(ctypes.byref(d), x, 1, 512, y, 256, 0, 0, ws, 1 << 20, None) == 1
+    assert lib.ht_linear_backward_workspace(ctypes.byref(d), 1, ctypes.byref(out)) == 1
+    assert lib.ht_linear_backward_data(ctypes.byref(d), y, 1, 256, x, 512, ws, 1 << 20, None) == 1
+    arr = (ctypes.POINTER(B.PackedWeight) * 1)(ctypes.pointer(d))
+    assert lib.ht_mlp_workspace(arr, 1, 1, ctypes.byref(out)) == 1
+    assert lib.ht_mlp_forward(arr, 1, x, 1, 512, y, 256, None, 0, ws, 1 << 20, None) == 1
+
+
+def test_backward_data_requires_aligned_buffer():
+    lib = B.load()
+    d = _desc(N=256, K=512, base=0x100008)
+    assert lib.ht_linear_backward_data(ctypes.byref(d), 0x200000, 1, 256, 0x300000, 512, 0x400000, 1 << 20,
+                                       None) == 3
