@@ -475,3 +475,68 @@ def test_plan_pack_forced_full_layer(orc, force):
     np.testing.assert_array_equal(fmt, orc.plan(W, force=force))
     got, _ = gpu_pack_bytes(W, fmt, 16)
     np.testing.assert_array_equal(got, orc.pack(W, fmt, 16))
+
+
+def _small_stack(orc, dims, seed):
+    rng = np.random.default_rng(seed)
+    Ws = [(rng.standard_t(4, size=(dims[i + 1], dims[i])) * 0.03).astype(np.float32) for i in range(len(dims) - 1)]
+    fmts = [orc.plan(W) for W in Ws]
+    return Ws, fmts, [api.pack(gpu(W), gpu(f)) for W, f in zip(Ws, fmts)]
+
+
+@pytest.mark.parametrize("preset", [0xFFFFFFFE, 14, 0])
+def test_mlp_fused_call_counter_cycle(orc, preset):
+    """Consecutive single-launch calls on one workspace never share a call
+    tag, also across the end of the counter's cycle and from a counter word
+    that was not initialised by the library (preset here): three calls with
+    different x, each equal bitwise to one launch per layer (which uses no
+    tags) and the last layer within the bar of the oracle; no wait expires."""
+    Ws, fmts, pws = _small_stack(orc, [512, 512, 512, 256], 81)
+    M = 2
+    ws = api.mlp_workspace(pws, M, dev())
+    ws[0:4].view(torch.int32).fill_(int(np.array(preset, np.uint32).view(np.int32)))
+    for call in range(3):
+        x = wl.to_bf16_bits(np.random.default_rng(90 + call).normal(size=(M, 512)).astype(np.float32))
+        ref = api.mlp(pws, bf16_gpu(x), path=B.HT_PATH_GEMV)
+        y, d = api.mlp(pws, bf16_gpu(x), dump=True, ws=ws, path=B.HT_PATH_FUSED)
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref), f"call {call} after preset {preset:#x}"
+        h1 = d[-1].cpu().view(torch.int16).numpy().view(np.uint16)
+        check_close(y.cpu().numpy(), np.maximum(orc.linear(Ws[-1], fmts[-1], h1), 0), f"call {call}")
+        assert int(ws[8:12].view(torch.int32).item()) == 0
+        assert 0 <= int(ws[0:4].view(torch.int32).item()) < 15      # the counter stays in its cycle
+        assert int(ws[4:8].view(torch.int32).item()) == 0           # arrivals reset by the last workgroup
+
+
+@pytest.mark.parametrize("M", [1, 2, 4])
+def test_mlp_fused_widening_stack(orc, M):
+    """A stack whose last layer has more row tiles than every hidden layer
+    (256 -> 256 -> 4096: 16 hidden tiles, 256 in the last layer), so most
+    workgroups own a tile only in the last layer: they read the call counter
+    before it advances (no wait expires, the flag word stays 0) and the
+    single launch equals one launch per layer bitwise, call after call."""
+    Ws, fmts, pws = _small_stack(orc, [256, 256, 4096], 83)
+    ws = api.mlp_workspace(pws, M, dev())
+    for call in range(4):
+        x = wl.to_bf16_bits(np.random.default_rng(95 + call).normal(size=(M, 256)).astype(np.float32))
+        ref = api.mlp(pws, bf16_gpu(x), path=B.HT_PATH_GEMV)
+        y, d = api.mlp(pws, bf16_gpu(x), dump=True, ws=ws, path=B.HT_PATH_FUSED)
+        torch.cuda.synchronize()
+        assert int(ws[8:12].view(torch.int32).item()) == 0, f"call {call}: a wait expired"
+        assert torch.equal(y, ref), f"call {call}"
+    h1 = d[-1].cpu().view(torch.int16).numpy().view(np.uint16)
+    check_close(y.cpu().numpy(), np.maximum(orc.linear(Ws[-1], fmts[-1], h1), 0), "last layer")
+
+
+def test_pack_full_mlp_layer_natural_plan(orc):
+    """The benchmark's own plan and pack: a full 4096 x 4096 MLP layer under
+    the default thresholds, map and the whole packed buffer byte for byte."""
+    W = wl.mlp_weight(1)
+    fmt_or = orc.plan(W)
+    Wg = gpu(W)
+    fmt = api.plan(Wg)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(fmt.cpu().numpy(), fmt_or)
+    pw = api.pack(Wg, fmt, row_tile=16)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(pw.buf.cpu().numpy(), orc.pack(W, fmt_or, 16))
