@@ -25,6 +25,7 @@ STATUS = {0: "HT_OK", 1: "HT_EINVAL", 2: "HT_ESHAPE", 3: "HT_EALIGN", 4: "HT_ESM
 # Every symbol include/ht.h declares.
 EXPORTS = ("ht_status_string", "ht_plan_params_default", "ht_plan", "ht_plan_counts",
            "ht_pack_bytes", "ht_pack", "ht_check_packed", "ht_linear_workspace", "ht_linear_forward",
+           "ht_linear_forward_noalloc",
            "ht_linear_backward_workspace", "ht_linear_backward_data", "ht_linear_backward_weight",
            "ht_mlp_workspace", "ht_workspace_init", "ht_mlp_forward")
 
@@ -83,6 +84,8 @@ def load() -> ctypes.CDLL:
     lib.ht_linear_forward.restype = St
     lib.ht_linear_forward.argtypes = [ctypes.POINTER(PackedWeight), P, I64, I64, P, I64, I32, I32, P,
                                       ctypes.c_size_t, P]
+    lib.ht_linear_forward_noalloc.restype = St
+    lib.ht_linear_forward_noalloc.argtypes = [ctypes.POINTER(PackedWeight), P, I64, I64, P, I64, I32, I32, P]
     lib.ht_linear_backward_workspace.restype = St
     lib.ht_linear_backward_workspace.argtypes = [ctypes.POINTER(PackedWeight), I64, ctypes.POINTER(ctypes.c_size_t)]
     lib.ht_linear_backward_data.restype = St
@@ -189,6 +192,15 @@ def ht_linear_forward(desc: PackedWeight, x, y, act: int = HT_ACT_NONE, path: in
     wsb = (ws.numel() * ws.element_size() if ws is not None else 0) if ws_bytes is None else ws_bytes
     _check("ht_linear_forward", load().ht_linear_forward(ctypes.byref(desc), _ptr(x), M, ldx, _ptr(y), ldy, act,
                                                          path, _ptr(ws), wsb, _stream(stream)))
+
+
+def ht_linear_forward_noalloc(desc: PackedWeight, x, y, act: int = HT_ACT_NONE, path: int = HT_PATH_AUTO,
+                              stream=None, M=None, ldx=None, ldy=None) -> None:
+    M = x.shape[0] if M is None else M
+    ldx = x.stride(0) if ldx is None else ldx
+    ldy = y.stride(0) if ldy is None else ldy
+    _check("ht_linear_forward_noalloc", load().ht_linear_forward_noalloc(ctypes.byref(desc), _ptr(x), M, ldx, _ptr(y),
+                                                                         ldy, act, path, _stream(stream)))
 
 
 def ht_linear_backward_workspace(desc: PackedWeight, M: int) -> int:

@@ -242,6 +242,26 @@ ht_status ht_linear_forward(const ht_packed_weight *w, const uint16_t *x, int64_
                             int64_t ldx, float *y, int64_t ldy, int32_t act, int32_t path,
                             void *ws, size_t ws_bytes, ht_stream stream);
 
+/* ht_linear_forward_noalloc -- ht_linear_forward without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, serving loops that run without an allocator, harnesses
+ * that forbid allocation.  The workspace is a fixed array inside the library
+ * of HT_NOALLOC_SCRATCH_BYTES on each GPU it runs on, held until the process
+ * ends; the call allocates and frees nothing.
+ *   Arguments, paths and results as ht_linear_forward (the same kernels:
+ *   the result is bitwise that of ht_linear_forward on the same path).
+ *   The current device must be the device of x, y, the packed buffer and
+ *   `stream`.
+ * HT_ESMALL when the call needs more workspace than the array holds
+ * (ht_linear_workspace gives the need; e.g. the int8 path over thousands of
+ * rows of a long K).  Every call on a GPU shares that GPU's array, whose
+ * contents each call overwrites before reading: calls that overlap in time
+ * on one GPU (other streams, other host threads) race, so serialise them. */
+#define HT_NOALLOC_SCRATCH_BYTES (32u << 20)
+ht_status ht_linear_forward_noalloc(const ht_packed_weight *w, const uint16_t *x, int64_t M,
+                                    int64_t ldx, float *y, int64_t ldy, int32_t act, int32_t path,
+                                    ht_stream stream);
+
 /* ht_linear_backward_workspace -- workspace bytes ht_linear_backward_data
  * needs for M rows of dY (HT_EINVAL for a row tile other than 16). */
 ht_status ht_linear_backward_workspace(const ht_packed_weight *w, int64_t M, size_t *bytes);

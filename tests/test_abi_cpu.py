@@ -398,3 +398,23 @@ def test_backward_data_requires_aligned_buffer():
     d = _desc(N=256, K=512, base=0x100008)
     assert lib.ht_linear_backward_data(ctypes.byref(d), 0x200000, 1, 256, 0x300000, 512, 0x400000, 1 << 20,
                                        None) == 3
+
+
+def test_noalloc_argument_checks():
+    """ht_linear_forward_noalloc refuses on the host what ht_linear_forward
+    refuses, and a call needing more than its fixed array (32 MiB per GPU)
+    with HT_ESMALL, before any HIP call."""
+    lib = B.load()
+    f = lib.ht_linear_forward_noalloc
+    x, y = 0x200000, 0x300000
+    d = _desc(N=512, K=14336)
+    bad = _desc(N=512, K=14336)
+    bad.bytes += 256
+    assert f(None, x, 1, 14336, y, 512, 0, 0, None) == 1
+    assert f(ctypes.byref(bad), x, 1, 14336, y, 512, 0, 0, None) == 1
+    assert f(ctypes.byref(d), x, 0, 14336, y, 512, 0, 0, None) == 2
+    assert f(ctypes.byref(d), x, 1, 14336, y, 512, 0, 9, None) == 1
+    assert f(ctypes.byref(_desc(R=8)), x, 8, 256, y, 256, 0, B.HT_PATH_GEMV_MFMA, None) == 1
+    need = B.ht_linear_workspace(d, 2048, B.HT_PATH_GEMM_I8)      # the encoded x of 2048 x 14336 and more
+    assert need > 32 << 20
+    assert f(ctypes.byref(d), x, 2048, 14336, y, 512, 0, B.HT_PATH_GEMM_I8, None) == 4
