@@ -82,7 +82,8 @@ def main() -> int:
     ap.add_argument("--cpu-steps", type=int, default=100,
                     help="oracle MLP forwards timed for the CPU baseline (about 14 s of CPU work)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "gemv", "mlp", "gemm", "decode", "i8", "configs", "backward"],
+    ap.add_argument("--only", choices=["all", "gemv", "mlp", "gemm", "decode", "i8", "configs", "backward",
+                                       "phases"],
                     default="all",
                     help="'gemv' / 'mlp' / 'gemm' / 'decode': only that timing leg (for profiler runs)")
     ap.add_argument("--no-gemm", action="store_true", help="skip the prefill GEMM leg")
@@ -100,6 +101,8 @@ def main() -> int:
     from block_planner_amd import binding as B
     from block_planner_amd import workloads as wl
 
+    if args.only == "phases":
+        B.use_library(B.PHASES_LIB_PATH)   # the fused MLP with its phase timestamps compiled in
     B.load()   # fails loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -434,6 +437,9 @@ def main() -> int:
     torch.cuda.synchronize()
     y_eager = y1.clone()
 
+    if args.only == "phases":
+        return phases_leg(B, mlp_fn, graph_of, x1, y1, G, step_bytes1, int(copies[0][0].desc.n_tiles), copies[0])
+
     if args.only == "decode":
         # Decode at batch 16 and 32: one launch per layer on the MFMA decode
         # path (gemv_mfma_kernel<1> / <2>; HT_PATH_AUTO takes it for 5..32
@@ -572,6 +578,91 @@ def main() -> int:
         "backward_data": bwd,
     }
     print(json.dumps(out))
+    return 0
+
+
+PHASE_EVENTS = 20
+
+
+def phases_leg(B, mlp_fn, graph_of, x1, y1, G, step_bytes1, T, copies0) -> int:
+    """Where the time of one fused MLP forward goes, from the instrumented
+    build (libht_phases.so): every workgroup's timestamps (100 MHz real-time
+    counter) of the last forward of each graph replay, relative to the
+    earliest workgroup entry of that forward.  Per event: the median over
+    replays of the min / median / max over workgroups, in microseconds."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    lib = B.load()
+    lib.ht_mlp_phases.restype = ctypes.c_int
+    lib.ht_mlp_phases.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    buf = np.zeros(1024 * PHASE_EVENTS, np.uint64)
+    g = graph_of(mlp_fn(x1, y1), G)
+    rows = []
+    for r in range(40):
+        g.replay()
+        if r < 4:
+            continue
+        torch.cuda.synchronize()
+        assert lib.ht_mlp_phases(buf.ctypes.data, buf.size) == 0
+        ts = buf.reshape(1024, PHASE_EVENTS)[:T].astype(np.int64)
+        rows.append((ts - ts[:, 0].min()) * 0.01)   # 10 ns ticks -> us
+    # every replay also times the whole graph: the duration of one forward
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(20):
+        g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    fwd_us = s.elapsed_time(e) * 1e3 / 20 / G
+    a = np.stack(rows)                                  # [replay][wg][event]
+    names = ["entry", "x staged, block ranges read", "wave 0: first chunks consumed"]
+    for l in range(4):
+        names += [f"layer {l}: wave 0 done with its chunks", f"layer {l}: all waves done (barrier)",
+                  f"layer {l}: " + ("y written" if l == 3 else "row sums published"),
+                  f"layer {l}: next x gathered" if l < 3 else "(unused)"]
+    events = {}
+    for ev in range(18):                                # events 0..17 of a 4-layer MLP
+        v = a[:, :, ev]
+        events[f"{ev:2d} {names[ev]}"] = {"min": round(float(np.median(v.min(1))), 2),
+                                          "median": round(float(np.median(np.median(v, 1))), 2),
+                                          "max": round(float(np.median(v.max(1))), 2)}
+    med = lambda ev: float(np.median(np.median(a[:, :, ev], 1)))
+    mx = lambda ev: float(np.median(a[:, :, ev].max(1)))
+    phases = {"launch ramp: entry spread (max entry)": round(mx(0), 2),
+              "to first chunks consumed (median)": round(med(2), 2)}
+    prev = 2
+    for l in range(4):
+        phases[f"layer {l} chunks (median workgroup, from previous phase)"] = round(med(4 + 4 * l) - med(prev), 2)
+        if l < 3:
+            phases[f"layer {l} boundary: row sums + publish + gather (median)"] = round(med(6 + 4 * l) - med(4 + 4 * l), 2)
+            prev = 6 + 4 * l
+    phases["last layer tail (median)"] = round(med(17) - med(16), 2)
+    phases["end of the last workgroup"] = round(mx(17), 2)
+    # per workgroup: median over forwards of the time its waves were all done
+    # with each layer's chunks, and the packed bytes of its row tile per layer
+    done = [np.median(a[:, :, 4 + 4 * l], 0) for l in range(4)]
+    tile_bytes = []
+    for l, pw in enumerate(copies0):
+        d = pw.desc
+        nk = int(d.n_tiles) * (int(d.K) // 64) + 1
+        kb = pw.buf[int(d.off_kbidx):int(d.off_kbidx) + 20 * nk].cpu().numpy().view(np.uint32).reshape(5, nk)
+        per = np.diff(kb[:, ::int(d.K) // 64].astype(np.int64), axis=1)       # blocks per tile and format
+        tile_bytes.append((per * np.array([37, 69, 129, 129, 257])[:, None]).sum(0))
+    corr = [float(np.corrcoef(done[l], tile_bytes[l])[0, 1]) for l in range(4)]
+    spread = {f"layer {l}": {"done_us_min_med_max": [round(float(np.min(done[l])), 2), round(float(np.median(done[l])), 2),
+                                                     round(float(np.max(done[l])), 2)],
+                             "tile_kB_min_med_max": [round(float(np.min(tile_bytes[l])) / 1e3, 1),
+                                                     round(float(np.median(tile_bytes[l])) / 1e3, 1),
+                                                     round(float(np.max(tile_bytes[l])) / 1e3, 1)],
+                             "corr_done_vs_bytes": round(corr[l], 3)} for l in range(4)}
+    print(json.dumps({"kernel": "mlp_fused_kernel<1> (phase build)", "workgroups": T, "forwards_sampled": len(rows),
+                      "workgroup_spread": spread,
+                      "us_per_forward_graph": round(fwd_us, 3),
+                      "GBps_phase_build": round(step_bytes1 / fwd_us / 1e3, 1),
+                      "phases_us": phases, "events_us": events}, indent=1))
     return 0
 
 

@@ -15,6 +15,9 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libht.so")
+# The same library built with the fused MLP's phase timestamps
+# (block_planner_amd.build, -DHT_MLP_PHASES); it also exports ht_mlp_phases.
+PHASES_LIB_PATH = os.path.join(HERE, "libht_phases.so")
 
 HT_INT4, HT_INT8, HT_BF16, HT_FP16, HT_FP32 = range(5)
 HT_ACT_NONE, HT_ACT_RELU = 0, 1
@@ -52,6 +55,15 @@ class PackedWeight(ctypes.Structure):
 
 
 _lib = None
+
+
+def use_library(path: str) -> None:
+    """Load the library from `path` instead (e.g. PHASES_LIB_PATH); must be
+    called before the first load."""
+    global LIB_PATH
+    if _lib is not None and os.path.abspath(path) != os.path.abspath(LIB_PATH):
+        raise RuntimeError("the library is already loaded")
+    LIB_PATH = path
 
 
 def load() -> ctypes.CDLL:

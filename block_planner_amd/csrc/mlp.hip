@@ -19,9 +19,10 @@
 // holding a 4-bit call tag.  The workspace keeps a call counter c in 0..14;
 // a call's tag is c + 1 (so a zero-initialised word never matches) and the
 // next call's counter is (c + 1) mod 15, so two consecutive calls never
-// share a tag.  The counter is advanced by the last workgroup to read it
-// (an arrival count next to it), so no workgroup of a call can see the next
-// call's value, whichever layers it owns tiles in.  The activation
+// share a tag.  Workgroup 0 advances the counter after gathering every
+// hidden layer; the launch is only used when every workgroup owns a row tile
+// of some hidden layer, so each has read the counter (its published words
+// carry the tag) before the advance.  The activation
 // wavefront of every workgroup reads the whole layer with 64-bit atomic
 // loads and re-reads any word whose tag is not yet the current one.  Every
 // word is written exactly once per call, so a matching tag means the word
@@ -45,10 +46,34 @@ namespace ht {
 constexpr int kMaxLayers = 8;
 constexpr int kMaxFusedM = 4;
 constexpr uint32_t kSpinLimit = 1u << 21;   // x ~64 clocks per poll: ~50 ms
-constexpr uint32_t kSyncBytes = 256;        // [0] call counter, [1] arrivals, [2] expired-wait flag
+constexpr uint32_t kSyncBytes = 256;        // [0] call counter, [2] expired-wait flag
 constexpr uint32_t kLoadWaves = kWaves - 1; // waves streaming weights; the last one stages the input
 constexpr int kSlots = 2;                   // chunks in flight per loading wave
 constexpr uint32_t kLdsBudget = 160 * 1024; // LDS of one compute unit
+
+// Phase timestamps, a compile-time variant (built with -DHT_MLP_PHASES, see
+// build.py): thread 0 of each workgroup (lane 0 of loading wave 0) records
+// the 100 MHz real-time counter at fixed points of a call into
+// ht_mlp_phase_ts[workgroup][event]; ht_mlp_phases() copies the table out.
+// Events: 0 entry, 1 x staged and block ranges read, 2 wave 0's first two
+// chunks consumed; per layer l at 3 + 4l: wave 0 done with its chunks,
+// 4 + 4l: all waves done (after the barrier), 5 + 4l: row sums published (or
+// the last layer's y written), 6 + 4l: the next layer's x gathered.  In the
+// ordinary build the macro is empty.
+constexpr int kPhaseEvents = 20;
+constexpr int kPhaseGroups = 1024;
+#ifdef HT_MLP_PHASES
+__device__ uint64_t ht_mlp_phase_ts[kPhaseGroups * kPhaseEvents];
+#define HT_PHASE(ev)                                                                                      \
+    do {                                                                                                  \
+        if (threadIdx.x == 0 && blockIdx.x < kPhaseGroups)                                               \
+            ht_mlp_phase_ts[blockIdx.x * kPhaseEvents + (ev)] = __builtin_amdgcn_s_memrealtime();         \
+    } while (0)
+#else
+#define HT_PHASE(ev) \
+    do {             \
+    } while (0)
+#endif
 
 struct MlpArgs {
     LayerDev layer[kMaxLayers];
@@ -156,6 +181,17 @@ __device__ __forceinline__ void gather_hidden(const uint64_t *words, uint32_t N,
     }
 }
 
+// Workgroup barrier for LDS data only.  __syncthreads() would also wait
+// for every outstanding global load of the wave, i.e. for the next layer's
+// chunks the loaders have already requested; none of the barriers below
+// orders global memory within the workgroup.
+__device__ __forceinline__ void lds_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 template <int M>
 __global__ __launch_bounds__(kThreads) void mlp_fused_kernel(MlpArgs a) {
     extern __shared__ float lds[];
@@ -168,17 +204,15 @@ __global__ __launch_bounds__(kThreads) void mlp_fused_kernel(MlpArgs a) {
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t L = a.n_layers;
     const bool xwave = wave == kLoadWaves;
-    // The call counter, then this workgroup's arrival (acquire: the arrival
-    // cannot be performed before the counter is read).  The last workgroup to
-    // arrive resets the arrival count and advances the counter: every
-    // workgroup of this call has read it by then, and the next call starts
-    // after this launch ends.
+    // The call counter.  Workgroup 0 advances it after its last gather; the
+    // host only runs this launch when every workgroup owns a row tile of some
+    // hidden layer (the last layer has no more tiles than the widest hidden
+    // one), and every published word carries the tag read here, so by then
+    // every workgroup has read the counter.
+    HT_PHASE(0);
     const uint32_t epoch =
-        __builtin_amdgcn_readfirstlane(__hip_atomic_load(a.sync, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT));
+        __builtin_amdgcn_readfirstlane(__hip_atomic_load(a.sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     const uint64_t tagmask = tag_bits(epoch);
-    uint32_t arrived_before = 0;   // used at the end, so the atomic's return is not waited for here
-    if (threadIdx.x == 0)
-        arrived_before = __hip_atomic_fetch_add(a.sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     // block ranges of this tile in every layer -> LDS (10 values per layer)
     if (threadIdx.x < 10 * L) {
@@ -192,7 +226,6 @@ __global__ __launch_bounds__(kThreads) void mlp_fused_kernel(MlpArgs a) {
         meta[threadIdx.x] = v;
     }
     if (xwave) stage_input<M>(a.x, a.ldx, a.layer[0].KB * 64, xs, a.xcap, lane);
-    __syncthreads();
 
     // Layer tail, run by every wave: fixed-order row sums, ReLU, then either
     // y (last layer) or this tile's rows published as tagged words.
@@ -211,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void mlp_fused_kernel(MlpArgs a) {
             }
         });
         if (last) return;
-        __syncthreads();
+        lds_barrier();
         // publish: four rows per 64-bit atomic store, the tag in the sign bits
         const uint32_t qpt = R / 4;
         if (threadIdx.x < M * qpt) {
@@ -232,12 +265,13 @@ __global__ __launch_bounds__(kThreads) void mlp_fused_kernel(MlpArgs a) {
     // barriers (per layer: after the chunks, after the row sums, after the
     // next layer's x is in LDS), so their registers never overlap.
     if (xwave) {
+        lds_barrier();                        // x staged, block ranges in LDS
         for (uint32_t l = 0; l < L; ++l) {
-            __syncthreads();
+            lds_barrier();
             layer_tail(l);
             if (l + 1 < L) {
                 gather_hidden<M>(a.hw[l], a.layer[l].N, tagmask, xs, a.xcap, lane, wave, a.sync);
-                __syncthreads();
+                lds_barrier();
             }
         }
     } else {
@@ -245,7 +279,24 @@ __global__ __launch_bounds__(kThreads) void mlp_fused_kernel(MlpArgs a) {
         // slots; slot u is refilled right after it is consumed, with the same
         // slot of the next group (possibly the next layer's).
         uint32_t ll = 0, gl = 0;             // layer and group to load next
-        ChunkWalker src = layer_src(a, meta, 0);
+        // layer 0's block ranges straight from memory (lanes 0..9), so the
+        // first weight loads wait for neither the x copy nor the barrier
+        ChunkWalker src;
+        {
+            const LayerDev &w0 = a.layer[0];
+            uint32_t v = 0;
+            if (lane < 10 && t < w0.T) {
+                const uint32_t *kbidx = reinterpret_cast<const uint32_t *>(w0.base + w0.off_kbidx);
+                v = kbidx[uint64_t(lane >> 1) * w0.nk + uint64_t(t) * w0.KB + ((lane & 1) ? w0.KB : 0u)];
+            }
+            uint32_t lo[5], hi[5];
+#pragma unroll
+            for (int f = 0; f < 5; ++f) {
+                lo[f] = __builtin_amdgcn_readlane(v, 2 * f);
+                hi[f] = __builtin_amdgcn_readlane(v, 2 * f + 1);
+            }
+            src = chunk_src(w0, lo, hi);
+        }
         walker_start(src, wave, kLoadWaves);
         uint32_t gcount = wave_groups(n_chunks(src), wave);
         auto advance_loader = [&]() {
@@ -270,6 +321,8 @@ __global__ __launch_bounds__(kThreads) void mlp_fused_kernel(MlpArgs a) {
             sl[u] = walker_load(src, lane);
             walker_advance(src);
         }
+        lds_barrier();                        // x staged, block ranges of the later layers in LDS
+        HT_PHASE(1);
         advance_loader();
         for (uint32_t l = 0; l < L; ++l) {
             const LayerDev &w = a.layer[l];
@@ -283,19 +336,22 @@ __global__ __launch_bounds__(kThreads) void mlp_fused_kernel(MlpArgs a) {
                     walker_advance(src);
                 }
                 advance_loader();
+                if (l == 0 && g == 0) HT_PHASE(2);
             }
-            __syncthreads();
+            HT_PHASE(3 + 4 * l);
+            lds_barrier();
+            HT_PHASE(4 + 4 * l);
             layer_tail(l);
+            HT_PHASE(5 + 4 * l);
             if (l + 1 < L) {
                 gather_hidden<M>(a.hw[l], a.layer[l].N, tagmask, xs, a.xcap, lane, wave, a.sync);
-                __syncthreads();
+                lds_barrier();
+                HT_PHASE(6 + 4 * l);
             }
         }
     }
-    if (threadIdx.x == 0 && arrived_before + 1u == gridDim.x) {
-        __hip_atomic_store(a.sync + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (t == 0 && threadIdx.x == 0)
         __hip_atomic_store(a.sync, (epoch % 15u + 1u) % 15u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
 }
 
 __global__ __launch_bounds__(256) void zero_fill_kernel(uint32_t *p, uint64_t n) {
@@ -382,6 +438,13 @@ ht_status mlp_plan(const ht_packed_weight *const *layers, int32_t L, int64_t M, 
         if (w->row_tile < 4) fusable = false;              // four rows per activation word
     }
     if (uint64_t(M) * rmax > 64) fusable = false;           // LDS row buffer
+    // every workgroup must own a row tile of some hidden layer: the call
+    // counter's advance by workgroup 0 is ordered after their reads of it
+    // only through the hidden layers' words
+    uint32_t thid = 0;
+    for (int32_t l = 0; l + 1 < L; ++l)
+        thid = uint32_t(layers[l]->n_tiles) > thid ? uint32_t(layers[l]->n_tiles) : thid;
+    if (L > 1 && tmax > thid) fusable = false;
     pl->xcap = kmax;
     pl->pcap = kbmax + 1;
     pl->rmax = rmax;
@@ -521,3 +584,16 @@ extern "C" ht_status ht_mlp_forward(const ht_packed_weight *const *layers, int32
     }
     return HT_OK;
 }
+
+#ifdef HT_MLP_PHASES
+// The phase table of the instrumented build (see HT_PHASE): n words of
+// [workgroup][event] timestamps in 10 ns ticks, copied to host memory after
+// the work queued so far has finished.
+extern "C" ht_status ht_mlp_phases(uint64_t *host_out, size_t n_words) {
+    if (!host_out || n_words > size_t(kPhaseGroups) * kPhaseEvents) return HT_EINVAL;
+    if (hipDeviceSynchronize() != hipSuccess) return HT_EHIP;
+    if (hipMemcpyFromSymbol(host_out, HIP_SYMBOL(ht_mlp_phase_ts), n_words * sizeof(uint64_t)) != hipSuccess)
+        return HT_EHIP;
+    return HT_OK;
+}
+#endif

@@ -324,7 +324,8 @@ ht_status ht_workspace_init(void *ws, size_t ws_bytes, ht_stream stream);
  *             packed back to back); the layers then read their input from it.
  *   path      HT_PATH_AUTO: one persistent launch for all layers when it fits
  *             (n_layers <= 8, M <= 4, row tile >= 4, x, partial sums and row
- *             buffer within the 160 KiB LDS of a compute unit, and every
+ *             buffer within the 160 KiB LDS of a compute unit, the last layer with
+ *             no more row tiles than the widest hidden layer, and every
  *             workgroup resident at once), else one launch per layer, each
  *             on the path HT_PATH_AUTO of ht_linear_forward takes for it;
  *             HT_PATH_GEMV: one register-path GEMV launch per layer;

@@ -505,17 +505,31 @@ def test_mlp_fused_call_counter_cycle(orc, preset):
         check_close(y.cpu().numpy(), np.maximum(orc.linear(Ws[-1], fmts[-1], h1), 0), f"call {call}")
         assert int(ws[8:12].view(torch.int32).item()) == 0
         assert 0 <= int(ws[0:4].view(torch.int32).item()) < 15      # the counter stays in its cycle
-        assert int(ws[4:8].view(torch.int32).item()) == 0           # arrivals reset by the last workgroup
 
 
 @pytest.mark.parametrize("M", [1, 2, 4])
-def test_mlp_fused_widening_stack(orc, M):
-    """A stack whose last layer has more row tiles than every hidden layer
-    (256 -> 256 -> 4096: 16 hidden tiles, 256 in the last layer), so most
-    workgroups own a tile only in the last layer: they read the call counter
-    before it advances (no wait expires, the flag word stays 0) and the
-    single launch equals one launch per layer bitwise, call after call."""
+def test_mlp_fused_uneven_stacks(orc, M):
+    """The single launch needs every workgroup to own a row tile of some
+    hidden layer (workgroup 0's advance of the call counter is ordered after
+    the others' reads only through the hidden layers' words).  256 -> 256 ->
+    4096 (16 hidden tiles, 256 in the last layer) is refused by
+    HT_PATH_FUSED and runs one launch per layer under HT_PATH_AUTO; 256 ->
+    4096 -> 256 -> 4096 runs as one launch although 240 of its workgroups
+    own tiles only in the first hidden layer and the last layer: bitwise the
+    per-layer result call after call, no wait expires."""
     Ws, fmts, pws = _small_stack(orc, [256, 256, 4096], 83)
+    ws = api.mlp_workspace(pws, M, dev())
+    x = wl.to_bf16_bits(np.random.default_rng(94).normal(size=(M, 256)).astype(np.float32))
+    with pytest.raises(B.HTError) as e:
+        api.mlp(pws, bf16_gpu(x), ws=ws, path=B.HT_PATH_FUSED)
+    assert e.value.code == 1
+    y, d = api.mlp(pws, bf16_gpu(x), dump=True, ws=ws, path=B.HT_PATH_AUTO)
+    if M < 4:   # AUTO's per-layer launches are the register path below 4 rows
+        assert torch.equal(y, api.mlp(pws, bf16_gpu(x), path=B.HT_PATH_GEMV))
+    h1 = d[-1].cpu().view(torch.int16).numpy().view(np.uint16)
+    check_close(y.cpu().numpy(), np.maximum(orc.linear(Ws[-1], fmts[-1], h1), 0), "refused stack, last layer")
+
+    Ws, fmts, pws = _small_stack(orc, [256, 4096, 256, 4096], 84)
     ws = api.mlp_workspace(pws, M, dev())
     for call in range(4):
         x = wl.to_bf16_bits(np.random.default_rng(95 + call).normal(size=(M, 256)).astype(np.float32))
@@ -524,8 +538,8 @@ def test_mlp_fused_widening_stack(orc, M):
         torch.cuda.synchronize()
         assert int(ws[8:12].view(torch.int32).item()) == 0, f"call {call}: a wait expired"
         assert torch.equal(y, ref), f"call {call}"
-    h1 = d[-1].cpu().view(torch.int16).numpy().view(np.uint16)
-    check_close(y.cpu().numpy(), np.maximum(orc.linear(Ws[-1], fmts[-1], h1), 0), "last layer")
+    h2 = d[-1].cpu().view(torch.int16).numpy().view(np.uint16)
+    check_close(y.cpu().numpy(), np.maximum(orc.linear(Ws[-1], fmts[-1], h2), 0), "last layer")
 
 
 def test_pack_full_mlp_layer_natural_plan(orc):
