@@ -71,6 +71,42 @@ def pack(W: torch.Tensor, fmt: torch.Tensor, row_tile: int = 16, stream=None, cn
     return PackedLinear(buf=buf, desc=desc, counts=cnt)
 
 
+@dataclass
+class RefreshState:
+    """Buffers of ht_refresh for one weight shape, allocated once: the packed
+    buffer at its upper bound, the format map, the device counts and the
+    initialised workspace."""
+    N: int
+    K: int
+    row_tile: int
+    buf: torch.Tensor
+    fmt: torch.Tensor
+    counts: torch.Tensor
+    ws: torch.Tensor
+
+
+def refresh_state(N: int, K: int, row_tile: int, device, stream=None) -> RefreshState:
+    buf_bytes, ws_bytes = B.ht_refresh_bytes(N, K, row_tile)
+    ws = _aligned_empty(ws_bytes, device)
+    B.ht_workspace_init(ws, stream=stream)
+    return RefreshState(N, K, row_tile, _aligned_empty(buf_bytes, device),
+                        torch.empty((N, K // 64), dtype=torch.uint8, device=device),
+                        torch.empty(5, dtype=torch.int64, device=device), ws)
+
+
+def refresh(W: torch.Tensor, st: RefreshState, stream=None, **params) -> PackedLinear:
+    """Re-plan and re-pack W into st.buf in one pass (ht_refresh), then
+    build the descriptor from the counts (one 40-byte copy to the host).
+    The previous packed weight of st is overwritten."""
+    B.ht_refresh(W, st.fmt, st.buf, st.counts, st.ws, plan_params(**params), row_tile=st.row_tile, stream=stream)
+    cnt = [int(v) for v in st.counts.cpu()]
+    if int(st.ws[8:12].view(torch.int32).item()) != 0:
+        raise RuntimeError("ht_refresh: a wait between workgroups expired (not all workgroups were resident); "
+                           "the refreshed buffer is invalid")
+    desc = B.ht_refresh_desc(st.N, st.K, st.row_tile, cnt, st.buf)
+    return PackedLinear(buf=st.buf[:int(desc.bytes)], desc=desc, counts=cnt)
+
+
 def workspace(nbytes: int, device) -> torch.Tensor | None:
     if nbytes == 0:
         return None

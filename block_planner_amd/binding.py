@@ -27,7 +27,8 @@ STATUS = {0: "HT_OK", 1: "HT_EINVAL", 2: "HT_ESHAPE", 3: "HT_EALIGN", 4: "HT_ESM
 
 # Every symbol include/ht.h declares.
 EXPORTS = ("ht_status_string", "ht_plan_params_default", "ht_plan", "ht_plan_counts",
-           "ht_pack_bytes", "ht_pack", "ht_check_packed", "ht_linear_workspace", "ht_linear_forward",
+           "ht_pack_bytes", "ht_pack", "ht_refresh_bytes", "ht_refresh", "ht_refresh_desc", "ht_check_packed",
+           "ht_linear_workspace", "ht_linear_forward",
            "ht_linear_forward_noalloc",
            "ht_linear_backward_workspace", "ht_linear_backward_data", "ht_linear_backward_weight",
            "ht_mlp_workspace", "ht_workspace_init", "ht_mlp_forward")
@@ -89,6 +90,14 @@ def load() -> ctypes.CDLL:
     lib.ht_pack.restype = St
     lib.ht_pack.argtypes = [P, I64, I64, I64, P, I64, ctypes.POINTER(ctypes.c_int64), P, ctypes.c_size_t,
                             ctypes.POINTER(PackedWeight), P]
+    lib.ht_refresh_bytes.restype = St
+    lib.ht_refresh_bytes.argtypes = [I64, I64, I64, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
+    lib.ht_refresh.restype = St
+    lib.ht_refresh.argtypes = [P, I64, I64, I64, ctypes.POINTER(PlanParams), I64, P, P, ctypes.c_size_t, P, P,
+                               ctypes.c_size_t, P]
+    lib.ht_refresh_desc.restype = St
+    lib.ht_refresh_desc.argtypes = [I64, I64, I64, ctypes.POINTER(ctypes.c_int64), P, ctypes.c_size_t,
+                                    ctypes.POINTER(PackedWeight)]
     lib.ht_check_packed.restype = St
     lib.ht_check_packed.argtypes = [ctypes.POINTER(PackedWeight), P, ctypes.c_size_t, P]
     lib.ht_linear_workspace.restype = St
@@ -180,6 +189,33 @@ def ht_pack(W, fmt_map, row_tile: int, counts, buf, stream=None, N=None, K=None,
     nbytes = buf.numel() * buf.element_size() if buf_bytes is None else buf_bytes
     _check("ht_pack", load().ht_pack(_ptr(W), N, K, ldw, _ptr(fmt_map), row_tile, c, _ptr(buf), nbytes,
                                      ctypes.byref(desc), _stream(stream)))
+    return desc
+
+
+def ht_refresh_bytes(N: int, K: int, row_tile: int) -> tuple:
+    """(buf_bytes, ws_bytes) for ht_refresh."""
+    b, w = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check("ht_refresh_bytes", load().ht_refresh_bytes(N, K, row_tile, ctypes.byref(b), ctypes.byref(w)))
+    return b.value, w.value
+
+
+def ht_refresh(W, fmt_map, buf, counts5, ws, params: PlanParams | None = None, row_tile: int = 16, stream=None,
+               N=None, K=None, ldw=None, buf_bytes=None, ws_bytes=None) -> None:
+    N = W.shape[0] if N is None else N
+    K = W.shape[1] if K is None else K
+    ldw = W.stride(0) if ldw is None else ldw
+    bb = buf.numel() * buf.element_size() if buf_bytes is None else buf_bytes
+    wb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    pp = ctypes.byref(params) if params is not None else None
+    _check("ht_refresh", load().ht_refresh(_ptr(W), N, K, ldw, pp, row_tile, _ptr(fmt_map), _ptr(buf), bb,
+                                           _ptr(counts5), _ptr(ws), wb, _stream(stream)))
+
+
+def ht_refresh_desc(N: int, K: int, row_tile: int, counts, buf, buf_bytes=None) -> PackedWeight:
+    c = (ctypes.c_int64 * 5)(*[int(v) for v in counts])
+    bb = buf.numel() * buf.element_size() if buf_bytes is None else buf_bytes
+    desc = PackedWeight()
+    _check("ht_refresh_desc", load().ht_refresh_desc(N, K, row_tile, c, _ptr(buf), bb, ctypes.byref(desc)))
     return desc
 
 

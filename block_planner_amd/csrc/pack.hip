@@ -211,69 +211,15 @@ __global__ __launch_bounds__(256) void pack_scatter_kernel(PackArgs a, PadArgs p
     const uint32_t pos = kbidx[uint64_t(f) * a.nk + col] + rank;
     if (pos >= a.counts[f]) return;                      // inconsistent counts: write nothing
 
-    if (part == 0) {
-        uint16_t id = uint16_t(kb * a.R + r);
-        *reinterpret_cast<uint16_t *>(a.buf + a.off_ids[f] + 2ull * pos) = id;
+    RegionOffsets o;
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+        o.ids[k] = a.off_ids[k];
+        o.pay[k] = a.off_pay[k];
     }
-    uint8_t *pay = a.buf + a.off_pay[f];
-    if (f <= 1u) {
-        const float Qf = f == 0u ? 7.0f : 127.0f;
-        const float amax = block_absmax(w);
-        float s = amax / Qf;
-        float q[kPerLane];
-        const uint32_t nf = block_nonfinite(w);
-        if (nf) {
-            s = (nf & 1u) ? __uint_as_float(0x7FC00000u) : __uint_as_float(0x7F800000u);
-#pragma unroll
-            for (int i = 0; i < kPerLane; ++i) q[i] = 0.0f;
-        } else {
-            lane_codes(w, s, Qf, q);
-        }
-        if (part == 0) *reinterpret_cast<float *>(a.buf + a.off_scale[f] + 4ull * pos) = s;
-        uint32_t wd[4];
-        if (f == 1u) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                wd[j] = (uint32_t(int(q[4 * j]) & 0xFF)) | (uint32_t(int(q[4 * j + 1]) & 0xFF) << 8) |
-                        (uint32_t(int(q[4 * j + 2]) & 0xFF) << 16) | (uint32_t(int(q[4 * j + 3]) & 0xFF) << 24);
-            *reinterpret_cast<uint4 *>(pay + 64ull * pos + 16 * part) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-        } else {
-            // byte i of the 16-byte half (p/2) takes entry i of this lane in
-            // its low nibble (even p) or high nibble (odd p)
-            const int sh = (part & 1) * 4;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                wd[j] = ((uint32_t(int(q[4 * j]) & 0xF)) << sh) | ((uint32_t(int(q[4 * j + 1]) & 0xF)) << (8 + sh)) |
-                        ((uint32_t(int(q[4 * j + 2]) & 0xF)) << (16 + sh)) |
-                        ((uint32_t(int(q[4 * j + 3]) & 0xF)) << (24 + sh));
-#pragma unroll
-            for (int j = 0; j < 4; ++j) wd[j] |= dpp_u32<kDppXor1>(wd[j]);
-            if ((part & 1) == 0)
-                *reinterpret_cast<uint4 *>(pay + 32ull * pos + 16 * (part >> 1)) =
-                    make_uint4(wd[0], wd[1], wd[2], wd[3]);
-        }
-    } else if (f == 2u || f == 3u) {
-        uint32_t hv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            uint32_t lo, hi;
-            if (f == 2u) {
-                lo = f32_to_bf16_rne(w[2 * j]);
-                hi = f32_to_bf16_rne(w[2 * j + 1]);
-            } else {
-                lo = __builtin_bit_cast(uint16_t, _Float16(w[2 * j]));
-                hi = __builtin_bit_cast(uint16_t, _Float16(w[2 * j + 1]));
-            }
-            hv[j] = lo | (hi << 16);
-        }
-        uint4 *dst = reinterpret_cast<uint4 *>(pay + 128ull * pos + 32 * part);
-        dst[0] = make_uint4(hv[0], hv[1], hv[2], hv[3]);
-        dst[1] = make_uint4(hv[4], hv[5], hv[6], hv[7]);
-    } else {
-        float4 *dst = reinterpret_cast<float4 *>(pay + 256ull * pos + 64 * part);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) dst[j] = make_float4(w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]);
-    }
+    o.scale[0] = a.off_scale[0];
+    o.scale[1] = a.off_scale[1];
+    store_block(a.buf, o, f, pos, uint16_t(kb * a.R + r), w, part);
 }
 
 }  // namespace ht

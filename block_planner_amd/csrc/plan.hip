@@ -29,9 +29,7 @@ struct PlanArgs {
     uint32_t KB;         // K / 64
     FastDiv div_kb;
     int64_t ldw;
-    double e2[4];        // eps^2 for INT4, INT8, BF16, FP16 (fl64(eps * eps))
-    int prefer_bf16;
-    int force;           // -1 or a format code
+    PlanRule rule;
 };
 
 template <bool EPS16_ZERO>
@@ -68,100 +66,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
         w[4 * k] = v.x; w[4 * k + 1] = v.y; w[4 * k + 2] = v.z; w[4 * k + 3] = v.w;
     }
 
-    // amax and the two scales
-    const float amax = block_absmax(w);
-    const float s4 = amax / 7.0f;     // correctly rounded fp32 division
-    const float s8 = amax / 127.0f;
-
-    // codes and exact residuals d = w - q*s (exactly representable in fp32,
-    // so the fused multiply-add returns it exactly)
-    float q[kPerLane], d4[kPerLane], d8[kPerLane];
-    lane_codes(w, s4, 7.0f, q);
-#pragma unroll
-    for (int i = 0; i < kPerLane; ++i) d4[i] = __builtin_fmaf(-q[i], s4, w[i]);
-    lane_codes(w, s8, 127.0f, q);
-#pragma unroll
-    for (int i = 0; i < kPerLane; ++i) d8[i] = __builtin_fmaf(-q[i], s8, w[i]);
-
-    // Screening in fp32: the sums of squares err4, err8, nrm2 to within
-    // 2^-17 relative plus 2^-120 absolute (66 roundings of non-negative
-    // partial sums, underflow included).  A decision that holds for every
-    // value in those intervals equals the decision on the fp64 pairwise
-    // trees; only the other blocks (near-ties, eps = 0, zero blocks,
-    // non-finite or huge entries) compute the fp64 trees, in waves that vote
-    // for them.
-    float e4f = 0.0f, e8f = 0.0f, nf = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kPerLane; ++i) {
-        e4f = __builtin_fmaf(d4[i], d4[i], e4f);
-        e8f = __builtin_fmaf(d8[i], d8[i], e8f);
-        nf = __builtin_fmaf(w[i], w[i], nf);
-    }
-    e4f = e4f + dpp_f32<kDppXor1>(e4f);
-    e8f = e8f + dpp_f32<kDppXor1>(e8f);
-    nf = nf + dpp_f32<kDppXor1>(nf);
-    e4f = e4f + dpp_f32<kDppXor2>(e4f);
-    e8f = e8f + dpp_f32<kDppXor2>(e8f);
-    nf = nf + dpp_f32<kDppXor2>(nf);
-    auto screen = [](double e2, float ef, float nfv) -> int {   // 0 no, 1 yes, 2 undecided
-        if (!(e2 > 0.0)) return 2;
-        const double E = ef, Nn = nfv, rel = 0x1p-17, ab = 0x1p-120;
-        if (E * (1.0 - rel) - ab > e2 * (Nn * (1.0 + rel) + ab)) return 0;
-        if (E * (1.0 + rel) + ab <= e2 * (Nn * (1.0 - rel) - ab)) return 1;
-        return 2;
-    };
-    const bool in_range = nf <= 0x1p126f;   // finite, and no square near overflow
-    const int dec4 = screen(a.e2[0], e4f, nf), dec8 = screen(a.e2[1], e8f, nf);
-    const bool need = !in_range || dec4 == 2 || dec8 == 2;
-    bool ok4 = dec4 == 1, ok8 = dec8 == 1, finite = true;
-    if (__any(need)) {
-        const double err4 = block_tree(tree16_sq(d4));
-        const double err8 = block_tree(tree16_sq(d8));
-        const double nrm2 = block_tree(tree16_sq(w));
-        if (need) {
-            ok4 = err4 <= a.e2[0] * nrm2;
-            ok8 = err8 <= a.e2[1] * nrm2;
-            finite = nrm2 <= DBL_MAX;   // false for Inf and NaN entries
-        }
-    }
-    float (&d)[kPerLane] = d4;   // scratch for the 16-bit tests below
-
-    // 16-bit formats
-    bool okb, okh;
-    if constexpr (EPS16_ZERO) {
-        uint32_t orb = 0;
-#pragma unroll
-        for (int i = 0; i < kPerLane; ++i) orb |= __float_as_uint(w[i]);
-        orb = block_or(orb);
-        okb = (orb & 0xFFFFu) == 0u;
-        // representable in binary16 => low 13 fraction bits are zero; only
-        // then test each entry exactly (rare: the whole quad agrees on orb)
-        uint32_t bad = 1u;
-        if ((orb & 0x1FFFu) == 0u) {
-            bad = 0u;
-#pragma unroll
-            for (int i = 0; i < kPerLane; ++i) bad |= (round_fp16(w[i]) != w[i]) ? 1u : 0u;
-            bad = block_or(bad);
-        }
-        okh = bad == 0u;
-    } else {
-#pragma unroll
-        for (int i = 0; i < kPerLane; ++i) d[i] = w[i] - round_bf16(w[i]);
-        const double errb = block_tree(tree16_sq(d));
-        // w - fp16(w) may not fit fp32 exactly only when fp16(w) overflows;
-        // that difference is infinite either way
-#pragma unroll
-        for (int i = 0; i < kPerLane; ++i) d[i] = w[i] - round_fp16(w[i]);
-        const double errh = block_tree(tree16_sq(d));
-        const double nrm2 = block_tree(tree16_sq(w));
-        okb = errb <= a.e2[2] * nrm2;
-        okh = errh <= a.e2[3] * nrm2;
-    }
-
-    const int f16a = a.prefer_bf16 ? (okb ? 2 : (okh ? 3 : 4)) : (okh ? 3 : (okb ? 2 : 4));
-    int f = ok4 ? 0 : (ok8 ? 1 : f16a);
-    f = finite ? f : 4;
-    f = a.force >= 0 ? a.force : f;
+    const int f = block_format<EPS16_ZERO>(w, a.rule);
     if (valid && part == 0) a.fmt[b] = uint8_t(f);
 }
 
@@ -245,9 +150,9 @@ extern "C" ht_status ht_plan(const float *W, int64_t N, int64_t K, int64_t ldw,
     a.KB = uint32_t(KB);
     a.div_kb = make_fastdiv(uint32_t(KB));
     a.ldw = ldw;
-    for (int i = 0; i < 4; ++i) a.e2[i] = eps[i] * eps[i];
-    a.prefer_bf16 = p->prefer_bf16 ? 1 : 0;
-    a.force = p->force_format;
+    for (int i = 0; i < 4; ++i) a.rule.e2[i] = eps[i] * eps[i];
+    a.rule.prefer_bf16 = p->prefer_bf16 ? 1 : 0;
+    a.rule.force = p->force_format;
     const uint32_t grid = uint32_t((nb + 63) / 64);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (p->eps_bf16 == 0.0 && p->eps_fp16 == 0.0)

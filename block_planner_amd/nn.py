@@ -24,7 +24,8 @@ Scope, as built:
   * The planner modes named on the page (LOWEST ... BEST) have no definition
     there; only the per-block rule is accepted (option None or "PER_BLOCK").
   * refresh_every > 0 with a master weight re-plans and re-packs every that
-    many forward calls (ht_plan + ht_pack; the page's refresh cadence).
+    many forward calls (the page's refresh cadence) with the fused single
+    pass ht_refresh, into buffers allocated once.
 """
 from __future__ import annotations
 
@@ -100,6 +101,7 @@ class HyperLinear(torch.nn.Module):
         self.weight = torch.nn.Parameter(w, requires_grad=not self.inference_only)
         self.packed: api.PackedLinear | None = None
         self.fmt: torch.Tensor | None = None
+        self._rs: api.RefreshState | None = None
         self._calls = 0
 
     # -- construction from existing layers / buffers --------------------------
@@ -114,7 +116,7 @@ class HyperLinear(torch.nn.Module):
         m.eps = _eps(**eps)
         m.weight = torch.nn.Parameter(lin.weight.detach().to(torch.float32).contiguous(),
                                       requires_grad=not m.inference_only)
-        m.packed, m.fmt, m._calls = None, None, 0
+        m.packed, m.fmt, m._rs, m._calls = None, None, None, 0
         m.pack(fmt)
         return m
 
@@ -126,15 +128,27 @@ class HyperLinear(torch.nn.Module):
         m.refresh_every, m.row_tile, m.inference_only = 0, int(packed.desc.row_tile), True
         m.eps = _eps()
         m.weight = None
-        m.packed, m.fmt, m._calls = packed, fmt, 0
+        m.packed, m.fmt, m._rs, m._calls = packed, fmt, None, 0
         return m
 
     # -- planning and packing ---------------------------------------------------
     def pack(self, fmt: torch.Tensor | None = None) -> None:
-        """Plan (unless a format map is given) and pack the master weight."""
+        """Plan (unless a format map is given) and pack the master weight.
+
+        A module that refreshes (refresh_every > 0, not inference-only)
+        re-plans and re-packs with the fused single pass (ht_refresh) into
+        buffers allocated on its first pack and reused afterwards; the
+        packed buffer is overwritten in place, so a backward pass must run
+        before the module's next refresh."""
         if self.weight is None:
             raise RuntimeError("no master weight to pack (inference-only module)")
         W = self.weight.detach()
+        if fmt is None and self.refresh_every > 0 and not self.inference_only:
+            if self._rs is None:
+                self._rs = api.refresh_state(self.out_features, self.in_features, self.row_tile, W.device)
+            self.packed = api.refresh(W.contiguous(), self._rs, **self.eps)
+            self.fmt = self._rs.fmt
+            return
         self.fmt = api.plan(W, **self.eps) if fmt is None else fmt.to(device=W.device, dtype=torch.uint8)
         self.packed = api.pack(W, self.fmt, row_tile=self.row_tile)
         if self.inference_only:
@@ -145,7 +159,8 @@ class HyperLinear(torch.nn.Module):
         the fp32 master weight."""
         packed = self.packed.nbytes if self.packed is not None else 0
         master = self.weight.numel() * 4 if self.weight is not None else 0
-        return {"packed": packed, "master_fp32": master, "total": packed + master}
+        held = int(self._rs.buf.numel()) if self._rs is not None else packed   # the refresh buffer's full size
+        return {"packed": packed, "master_fp32": master, "total": held + master}
 
     # -- forward -----------------------------------------------------------------
     def forward(self, x: torch.Tensor) -> torch.Tensor:

@@ -169,6 +169,50 @@ ht_status ht_pack(const float *W, int64_t N, int64_t K, int64_t ldw,
                   const uint8_t *fmt_map, int64_t row_tile, const int64_t counts5[5],
                   void *buf, size_t buf_bytes, ht_packed_weight *desc, ht_stream stream);
 
+/* ht_refresh_bytes -- buffer and workspace sizes for ht_refresh (host only).
+ *   buf_bytes   an upper bound of the packed size for any plan of W[N, K]
+ *               with this row tile (every split of the blocks into formats);
+ *   ws_bytes    the workspace (initialise it once with ht_workspace_init).
+ * HT_ESHAPE for the shapes ht_pack refuses. */
+ht_status ht_refresh_bytes(int64_t N, int64_t K, int64_t row_tile, size_t *buf_bytes, size_t *ws_bytes);
+
+/* ht_refresh -- re-plan and re-pack W into a buffer allocated in advance, in
+ * one pass over W and without a host round trip ("Usage Example":
+ * refresh_every, the packed weight following its trained master): the
+ * format map, the counts and the packed bytes are exactly those of ht_plan
+ * then ht_pack with the same thresholds and row tile.
+ *   W, N, K, ldw, p   as ht_plan;  row_tile as ht_pack.
+ *   fmt_map   uint8 [N, K/64] out (device): the new plan.
+ *   buf       device buffer of buf_bytes, 256-byte aligned; every byte of
+ *             the new layout is written (the block index, ids, scales,
+ *             payloads and the alignment padding).
+ *   counts5   int64 [5] out (device): blocks per format of the new plan.
+ *   ws        workspace of ws_bytes >= ht_refresh_bytes(...), initialised
+ *             once with ht_workspace_init; each call leaves it ready for the
+ *             next.  If a wait between workgroups ever expires (bounded,
+ *             about 50 ms), the 32-bit word at byte 8 of ws becomes nonzero
+ *             and that call's output is invalid.
+ * Then ht_refresh_desc gives the descriptor from the counts (the caller
+ * copies the 40 bytes of counts5 to the host).  When the new layout is
+ * larger than buf_bytes (a buffer smaller than ht_refresh_bytes's bound)
+ * the map and counts are written, the buffer is not, the word at byte 12
+ * of ws becomes nonzero and ht_refresh_desc returns HT_ESMALL.
+ * W is read once when the weight fits in the registers of the resident
+ * workgroups (up to 72 MB of fp32 W on 256 compute units); a larger weight
+ * is read twice (the planning pass, then the scatter).  All workgroups of
+ * the launch must be resident at once: the grid is sized from the current
+ * device's occupancy, and calls that run concurrently on other streams of
+ * the same device can delay it (a bounded wait, see ws). */
+ht_status ht_refresh(const float *W, int64_t N, int64_t K, int64_t ldw, const ht_plan_params *p,
+                     int64_t row_tile, uint8_t *fmt_map, void *buf, size_t buf_bytes, int64_t *counts5,
+                     void *ws, size_t ws_bytes, ht_stream stream);
+
+/* ht_refresh_desc -- the descriptor of a buffer ht_refresh filled, from its
+ * counts (host only): as ht_pack's descriptor for the same plan.
+ * HT_ESMALL when that layout needs more than buf_bytes. */
+ht_status ht_refresh_desc(int64_t N, int64_t K, int64_t row_tile, const int64_t counts5[5], void *buf,
+                          size_t buf_bytes, ht_packed_weight *desc);
+
 /* ht_check_packed -- validate a packed weight held in HOST memory (e.g. one
  * read from a file) before it is copied to the device and handed to the
  * kernels.  Host only: no GPU work, nothing enqueued.

@@ -418,3 +418,42 @@ def test_noalloc_argument_checks():
     need = B.ht_linear_workspace(d, 2048, B.HT_PATH_GEMM_I8)      # the encoded x of 2048 x 14336 and more
     assert need > 32 << 20
     assert f(ctypes.byref(d), x, 2048, 14336, y, 512, 0, B.HT_PATH_GEMM_I8, None) == 4
+
+
+def test_refresh_argument_checks(orc):
+    """ht_refresh_bytes bounds every plan's packed size; ht_refresh refuses
+    bad arguments and ht_refresh_desc a layout larger than the buffer, all on
+    the host before any launch."""
+    import itertools
+    for (N, K, R) in [(256, 256, 16), (37, 320, 4), (4096, 4096, 16), (5, 64, 1)]:
+        bb, wb = B.ht_refresh_bytes(N, K, R)
+        assert wb >= 256 + 16 * 2048
+        nb = N * (K // 64)
+        for f in range(5):   # every single-format plan and a few mixes fit the bound
+            c = [0] * 5
+            c[f] = nb
+            assert orc.pack_layout(N, K, R, c)[0] <= bb
+        for c in itertools.product(*[[0, nb // 3] for _ in range(4)]):
+            c = list(c) + [nb - sum(c)]
+            if c[4] >= 0:
+                assert orc.pack_layout(N, K, R, c)[0] <= bb
+    with pytest.raises(B.HTError):
+        B.ht_refresh_bytes(256, 100, 16)
+    lib = B.load()
+    f = lib.ht_refresh
+    W, fmt, buf, cnt, ws = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000
+    assert f(None, 256, 256, 256, None, 16, fmt, buf, 1 << 20, cnt, ws, 1 << 16, None) == 1
+    assert f(W, 256, 256, 128, None, 16, fmt, buf, 1 << 20, cnt, ws, 1 << 16, None) == 2   # ldw < K
+    assert f(W, 256, 256, 256, None, 3, fmt, buf, 1 << 20, cnt, ws, 1 << 16, None) == 2    # row tile
+    assert f(W, 256, 256, 256, None, 16, fmt, buf + 16, 1 << 20, cnt, ws, 1 << 16, None) == 3  # buf not 256-aligned
+    assert f(W, 256, 256, 256, None, 16, fmt, buf, 1 << 20, cnt, ws, 100, None) == 4       # workspace
+    p = B.ht_plan_params_default()
+    p.eps_int4 = -1.0
+    assert f(W, 256, 256, 256, ctypes.byref(p), 16, fmt, buf, 1 << 20, cnt, ws, 1 << 16, None) == 1
+    c = [0, 1024, 0, 0, 0]
+    size = orc.pack_layout(256, 256, 16, c)[0]
+    d = B.ht_refresh_desc(256, 256, 16, c, buf, buf_bytes=size)
+    assert int(d.bytes) == size and int(d.base) == buf
+    with pytest.raises(B.HTError) as e:
+        B.ht_refresh_desc(256, 256, 16, c, buf, buf_bytes=size - 1)
+    assert e.value.code == 4
