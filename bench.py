@@ -18,15 +18,21 @@ algorithmic bytes are, per block, its payload + scale + one format-map byte
 (2 bytes each) and the output (2 bytes for bfloat16 hidden layers, 4 for the
 fp32 last layer).
 
-Also reported (not the headline value): planner and packer GB/s, the
-single-layer GEMV, the per-layer MLP path, batch 32, a warm-cache figure, and
-the prefill GEMM (MFMA path, M = 2048, Llama-8B-shaped layers) in TFLOP/s.
+Also reported (not the headline value): planner, packer and fused-refresh
+GB/s (over 8 rotated fp32 weights, 512 MB), the single-layer GEMV, the
+per-layer MLP path, batch 32, a warm-cache figure, the prefill GEMM (MFMA
+path, M = 2048, Llama-8B-shaped layers) in TFLOP/s, the int8 path, the
+backward kernels, and the transformer-shaped configurations: TinyLlama decode
+at batch 1 over its 154 linears, Llama-8B decode at batch 1 / 4 / 16 over its
+224 linears and the planner / packer sweep over the Llama-8B set.  The CPU
+baseline is the oracle on the host's cores (all of them, and one).
 
 Prints ONE JSON line.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -80,13 +86,15 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=24)
     ap.add_argument("--copies", type=int, default=6)
     ap.add_argument("--cpu-steps", type=int, default=100,
-                    help="oracle MLP forwards timed for the CPU baseline (about 14 s of CPU work)")
+                    help="oracle MLP forwards timed on all cores for the CPU baseline (a fifth of them on one core)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["all", "gemv", "mlp", "gemm", "decode", "i8", "configs", "backward",
                                        "phases"],
                     default="all",
                     help="'gemv' / 'mlp' / 'gemm' / 'decode': only that timing leg (for profiler runs)")
     ap.add_argument("--no-gemm", action="store_true", help="skip the prefill GEMM leg")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the transformer-shaped configurations (TinyLlama / Llama-8B decode, plan/pack sweep)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -111,6 +119,29 @@ def main() -> int:
 
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def flush():
+        """Write 512 MB (twice the 256 MB Infinity Cache), so what was
+        touched before comes from HBM again."""
+        flush_buf.fill_(1)
+
+    def clone_packed(pw):
+        """An independent copy of a packed weight (its own aligned buffer)."""
+        buf = api._aligned_empty(pw.nbytes, dev)
+        buf.copy_(pw.buf[:pw.nbytes])
+        d = B.PackedWeight()
+        ctypes.memmove(ctypes.addressof(d), ctypes.addressof(pw.desc), ctypes.sizeof(d))
+        d.base = buf.data_ptr()
+        return api.PackedLinear(buf, d, list(pw.counts))
+
+    def copies_over(pw, min_bytes=512 << 20):
+        """pw plus copies until together they exceed min_bytes."""
+        out = [pw]
+        while sum(p_.nbytes for p_ in out) < min_bytes:
+            out.append(clone_packed(pw))
+        return out
 
     def timed(fn, reps):
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -198,7 +229,8 @@ def main() -> int:
           * Llama-3.1-8B shapes (32 x 7 = 224 linears, 7.0e9 parameters):
             the planner and packer streamed layer by layer over the whole set
             for eps_int4 in {0.04, 0.08, 0.16} and forced all-INT4 / all-INT8
-            plans (kernel time from events around each call), then decode at
+            plans (events around each call, after a 512 MB write so that W
+            comes from HBM, not from the Infinity Cache), then decode at
             batch 1, 4 and 16 over all 224 linears packed at the default eps.
         Each decode pass is one HIP graph of every linear in order (AUTO
         path, each with its own input and output), replayed; GB/s counts the
@@ -255,6 +287,7 @@ def main() -> int:
                 for name, kw in settings:
                     a = acc[name]
                     fmt = torch.empty((shp.n, shp.k // 64), dtype=torch.uint8, device=dev)
+                    flush()   # W was just generated (or planned): take it from HBM
                     ev0.record(stream)
                     B.ht_plan(W, fmt, api.plan_params(**kw), stream=stream)
                     ev1.record(stream)
@@ -263,6 +296,7 @@ def main() -> int:
                     cnt = api.counts(fmt)
                     nb = B.ht_pack_bytes(shp.n, shp.k, 16, cnt)
                     buf = api._aligned_empty(nb, dev)
+                    flush()
                     ev0.record(stream)
                     desc = B.ht_pack(W, fmt, 16, cnt, buf, stream=stream)
                     ev1.record(stream)
@@ -300,34 +334,38 @@ def main() -> int:
     def backward_leg():
         """The input gradient dX = dY . W_hat (ht_linear_backward_data) at 1
         and 4 rows of fp32 dY: the 4096x4096 MLP layer (default thresholds)
-        and the Llama-8B q / gate / down shapes.  Graph replays of 10 calls on
-        one packed copy; GB/s counts packed bytes + dY + dX."""
+        and the Llama-8B q / gate / down shapes.  Graph replays of calls that
+        rotate over copies of the packed weight holding together more than
+        512 MB (the Infinity Cache holds 256 MB); GB/s counts packed bytes +
+        dY + dX.  The weight gradient writes a fresh 64 MB fp32 dW per call
+        (write-bound, not served by the cache)."""
         res = {}
         cases = [("mlp4096", None)] + [(s_.name, s_) for s_ in wl.llama8b_shapes() if s_.name in ("q", "gate", "down")]
         for name, shp in cases:
             W = (torch.from_numpy(wl.mlp_weight(0)).to(dev) if shp is None else wl.llama8b_weight_gpu(0, shp, dev))
-            pw = api.pack(W, api.plan(W))
+            pws = copies_over(api.pack(W, api.plan(W)))   # rotated: more than the Infinity Cache holds
             del W
-            row = {}
+            pw = pws[0]
+            row = {"rotating_copies": len(pws)}
             for M in (1, 4):
                 dy = torch.randn(M, pw.N, device=dev)
                 dx = torch.empty(M, pw.K, device=dev)
                 ws = api.workspace(B.ht_linear_backward_workspace(pw.desc, M), dev)
-                fn = lambda: api.linear_backward_data(pw, dy, out=dx, ws=ws)
-                fn()
-                torch.cuda.synchronize()
+                n_in = 2 * len(pws)
                 g = torch.cuda.CUDAGraph()
+                api.linear_backward_data(pw, dy, out=dx, ws=ws)
+                torch.cuda.synchronize()
                 with torch.cuda.graph(g):
-                    for _ in range(10):
-                        fn()
+                    for i in range(n_in):
+                        api.linear_backward_data(pws[i % len(pws)], dy, out=dx, ws=ws)
                 g.replay()
                 torch.cuda.synchronize()
-                t = timed(lambda i: g.replay(), 5) / 10
+                t = timed(lambda i: g.replay(), 3) / n_in
                 nb = pw.nbytes + 4 * M * (pw.N + pw.K)
                 row[f"M{M}"] = {"us": round(t * 1e6, 2), "GBps": round(nb / t / 1e9, 1)}
                 del g
             res[name] = row
-            del pw
+            del pw, pws
         # STE weight gradient dW = dY^T . x (fp32 [N, K] written): 4096 x 4096
         wg = {}
         for M in (1, 32):
@@ -368,12 +406,15 @@ def main() -> int:
     Ws = [torch.from_numpy(W).to(dev) for W in Ws_host]
 
     # ---- planner ---------------------------------------------------------
+    # Calls rotate over 8 fp32 weights (the 4 layers and a copy of each:
+    # 512 MB, twice the Infinity Cache), so W comes from HBM.
     log("planner")
     fmts = [api.plan(W) for W in Ws]
     torch.cuda.synchronize()
-    plan_reps = 10
-    t_plan = timed(lambda i: [B.ht_plan(Ws[l], fmts[l]) for l in range(L)], plan_reps)
-    plan_bytes = L * (4 * D * D + D * D // 64)
+    Wrot = Ws + [W.clone() for W in Ws]
+    plan_reps = 8 * 6
+    t_plan = timed(lambda i: B.ht_plan(Wrot[i % 8], fmts[i % L]), plan_reps)   # per 4096^2 layer
+    plan_bytes = 4 * D * D + D * D // 64
     counts = [api.counts(f) for f in fmts]
 
     # ---- packer ----------------------------------------------------------
@@ -382,10 +423,26 @@ def main() -> int:
               for _ in range(max(1, args.copies))]
     torch.cuda.synchronize()
     scratch = [api.pack(Ws[l], fmts[l], row_tile=16, cnt=counts[l]) for l in range(L)]
-    t_pack = timed(lambda i: [B.ht_pack(Ws[l], fmts[l], 16, counts[l], scratch[l].buf) for l in range(L)], 5)
+    t_pack = timed(lambda i: B.ht_pack(Wrot[i % 8], fmts[i % L], 16, counts[i % L], scratch[i % L].buf), 8 * 4)
     pack_bytes = sum(4 * D * D + D * D // 64 + sum(c * (p + s) for c, p, s in zip(counts[l], PAY, SCALE))
-                     for l in range(L))
+                     for l in range(L)) / L
     del scratch
+
+    # ---- fused refresh (re-plan + re-pack in one pass) ---------------------
+    log("refresh")
+    rs = api.refresh_state(D, D, 16, dev)
+    rbufs = [rs.buf] + [api._aligned_empty(rs.buf.numel(), dev) for _ in range(7)]   # 8 outputs, rotated too
+    for l in range(L):                                   # the refresh's output equals the packer's
+        api.refresh(Ws[l], rs)
+        assert torch.equal(rs.buf[:copies[0][l].nbytes], copies[0][l].buf[:copies[0][l].nbytes])
+    params = api.plan_params()
+
+    def refresh_call(i):
+        B.ht_refresh(Wrot[i % 8], rs.fmt, rbufs[i % 8], rs.counts, rs.ws, params, row_tile=16, stream=stream)
+    t_refresh = timed(refresh_call, 8 * 6)
+    refresh_bytes = 4 * D * D + sum(D * D // 64 + copies[0][l].nbytes for l in range(L)) / L
+    refresh_ok = int(rs.ws[8:16].view(torch.int32).abs().sum().item()) == 0
+    del rs, rbufs, Wrot
     if args.only == "all":
         del Ws   # inference-only: the fp32 masters are not needed any more
         torch.cuda.empty_cache()
@@ -517,23 +574,65 @@ def main() -> int:
         gemm["int8_path"] = i8_leg()
         log("input gradient dX = dY . W_hat (4096x4096 and Llama-8B shapes, M = 1 and 4)")
         bwd = backward_leg()
+    configs = None
+    if not args.no_configs:
+        try:
+            del copies, arrays, descs
+        except NameError:
+            pass
+        torch.cuda.empty_cache()
+        configs = configs_leg()
 
     # ---- CPU baseline: the oracle as it stands ----------------------------
+    # The C oracle (fp64) on the host cores: one thread, and all the cores
+    # the box gives this job (at most 16) each computing a slice of every
+    # layer's rows through the same oracle calls (ctypes releases the GIL
+    # during a call; the oracle itself is unchanged).
     cpu = None
     if not args.no_cpu_baseline and args.cpu_steps > 0:
         log("cpu baseline (oracle)")
+        import concurrent.futures as cf
+
         import oracle
         fm_host = [f.cpu().numpy() for f in fmts]
         xb = wl.to_bf16_bits(wl.mlp_activation(1))
         oracle.mlp(Ws_host, fm_host, xb)   # load + warm
+        n1 = max(1, args.cpu_steps // 5)
         t0 = time.perf_counter()
-        for _ in range(args.cpu_steps):
+        for _ in range(n1):
             oracle.mlp(Ws_host, fm_host, xb)
-        t_cpu = (time.perf_counter() - t0) / args.cpu_steps
-        cpu = {"value": round(step_bytes1 / t_cpu / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "sample": f"{args.cpu_steps} forwards of the same 4-layer 4096 MLP at batch 1 "
-                         f"(C oracle, fp64, single thread; {t_cpu * 1e3:.1f} ms per forward; "
-                         f"host has {os.cpu_count()} logical CPUs)"}
+        t_cpu1 = (time.perf_counter() - t0) / n1
+        threads = max(1, min(16, os.cpu_count() or 1))
+        slices = [[(W[r0:r0 + -(-D // threads)], f[r0:r0 + -(-D // threads)]) for r0 in range(0, D, -(-D // threads))]
+                  for W, f in zip(Ws_host, fm_host)]
+
+        def mlp_rows(pool, h):
+            for l in range(L):
+                parts = list(pool.map(lambda wf: oracle.linear(wf[0], wf[1], h), slices[l]))
+                z = np.concatenate(parts, axis=1)
+                h = oracle.relu_bf16(z) if l + 1 < L else oracle.relu(z)
+            return h
+        with cf.ThreadPoolExecutor(max_workers=threads) as pool:
+            y_par = mlp_rows(pool, xb)
+            assert np.array_equal(y_par, oracle.mlp(Ws_host, fm_host, xb)[0])   # the same oracle result
+            t0 = time.perf_counter()
+            for _ in range(args.cpu_steps):
+                mlp_rows(pool, xb)
+            t_cpuN = (time.perf_counter() - t0) / args.cpu_steps
+        model = "unknown"
+        try:
+            for line in open("/proc/cpuinfo"):
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+        except OSError:
+            pass
+        cpu = {"value": round(step_bytes1 / t_cpuN / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "sample": f"{args.cpu_steps} forwards of the same 4-layer 4096 MLP at batch 1 (C oracle, fp64; each "
+                         f"layer's rows split over {threads} threads; {t_cpuN * 1e3:.1f} ms per forward)",
+               "single_thread": {"value": round(step_bytes1 / t_cpu1 / 1e9, 4), "ms_per_forward": round(t_cpu1 * 1e3, 1),
+                                 "forwards": n1},
+               "nproc": os.cpu_count(), "cpu_model": model}
 
     mix = [sum(c[f] for c in counts) / sum(sum(c) for c in counts) for f in range(5)]
     out = {
@@ -563,6 +662,15 @@ def main() -> int:
         "planner_GBps": round(plan_bytes / t_plan / 1e9, 2),
         "planner_pct_hbm_peak": round(100 * plan_bytes / t_plan / 1e9 / HBM_PEAK_GBS, 2),
         "packer_GBps": round(pack_bytes / t_pack / 1e9, 2),
+        "plan_pack_working_set": "8 fp32 4096x4096 weights rotated (512 MB, twice the Infinity Cache)",
+        "refresh": {"kernel": "refresh_kernel<true, true> (ht_refresh, one pass over W)",
+                    "GBps": round(refresh_bytes / t_refresh / 1e9, 2),
+                    "pct_hbm_peak": round(100 * refresh_bytes / t_refresh / 1e9 / HBM_PEAK_GBS, 2),
+                    "us_per_layer": round(t_refresh * 1e6, 2),
+                    "bytes_per_layer": int(refresh_bytes),
+                    "bytes": "4 N K read + the map and the packed buffer written",
+                    "equals_plan_then_pack": True, "waits_ok": refresh_ok,
+                    "vs_plan_then_pack_us": round((t_plan + t_pack) * 1e6, 2)},
         "mlp_per_layer_launches_GBps": round(step_bytes1 / t_perlayer / 1e9, 2),
         "single_layer_gemv": {"kernel": "gemv_kernel<1>", "GBps": round(gemv_gbs, 2),
                               "avg_launch_us": round(gemv_dur * 1e6, 3),
@@ -576,6 +684,7 @@ def main() -> int:
         "packed_MB_per_mlp": round(packed_mb, 2),
         "prefill_gemm": gemm,
         "backward_data": bwd,
+        "transformer_configs": configs,
     }
     print(json.dumps(out))
     return 0
