@@ -179,7 +179,7 @@ def main() -> int:
                          "TFLOPs": round(fl / t / 1e12, 1), "mfma_frac": round(fl / t / 2.5e15, 4)}
             del pw, xb, yg
             torch.cuda.empty_cache()
-        return {"kernel": "gemm_kernel<4>", "peak_TFLOPs": 2500.0, "shapes": out}
+        return {"kernel": "gemm_kernel<8>", "peak_TFLOPs": 2500.0, "shapes": out}
 
     def i8_leg():
         """The int8 matrix-core path (HT_PATH_GEMM_I8) against the MFMA path

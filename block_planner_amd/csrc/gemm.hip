@@ -4,8 +4,8 @@
 // float block sum_i w_i * x[m, 64kb+i] (HyperTensor 1.0.1 page, intro: fused
 // kernels execute the mixed-precision plan; "Key Features": HyperLinear).
 //
-// A workgroup owns a BM x 64 tile of y (BM = 256, 128 or 64 rows of x) and
-// walks K one 64-wide block at a time.  Per step the tile's 64 weight blocks
+// A workgroup owns a BM x 128 tile of y (BM = 256, 128 or 64 rows of x) and
+// walks K one 64-wide block at a time.  Per step the tile's 128 weight blocks
 // (one per output column) are dequantised into LDS as bfloat16:
 //   INT4 / INT8   the codes themselves (|q| <= 127 is exact in bfloat16);
 //                 the block's scale multiplies the 64-term partial afterwards;
@@ -20,10 +20,13 @@
 // that step, straight into the accumulators (float blocks have scale 1, and
 // integer columns hold zeros in the lo plane).
 //
-// Roles and pipeline: four waves run the MFMAs and copy x tiles straight
-// from memory into LDS (global_load_lds) two steps ahead; four waves load
-// the packed blocks two steps ahead into registers and dequantise the next
-// step's into the other LDS stage.  One barrier per step.
+// Roles and pipeline (512 threads): four waves run the MFMAs, each on a
+// (BM/2) x 64 quarter of the tile, and copy x tiles straight from memory into
+// LDS (global_load_lds) one step ahead; four waves load the packed blocks two
+// steps ahead into registers and dequantise the next step's into the other
+// LDS stage, two threads per block (32 entries each).  One barrier per step;
+// it waits only for LDS operations, so the producers' loads of later steps
+// stay in flight across it.
 #include "int8_tile.h"
 #include "linear_host.h"
 
@@ -32,7 +35,7 @@ namespace ht {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr uint32_t kGemmBN = 64;          // output columns (weight rows) per workgroup: 4 groups of 16
+constexpr uint32_t kGemmBN = 128;         // output columns (weight rows) per workgroup: 8 groups of 16
 constexpr uint32_t kGemmThreads = 512;    // 4 MFMA waves + 4 producer waves
 constexpr uint32_t kLdsRow = 72;          // bfloat16 per weight row in LDS: 64 + 8 of padding
 
@@ -56,39 +59,48 @@ struct WStage {
     uint16_t whi[kGemmBN][kLdsRow];    // bfloat16, row = output column
     uint16_t wlo[kGemmBN][kLdsRow];
     float scale[kGemmBN];
-    uint32_t need_lo[4];               // per 16-column group
+    uint32_t need_lo[kGemmBN / 16];    // per 16-column group
 };
 
-// What one producer thread loads for one K-step: quarter `part` of the packed
-// block of its column (16 of the 64 entries).
+// What one producer thread loads for one K-step: half `h` of the packed block
+// of its column slot (32 of the 64 entries).
 struct BlockLoad {
-    uint4 p[4];        // payload bytes of the quarter (8 / 16 / 32 / 32 / 64 bytes by format)
+    uint4 p[8];        // payload bytes of the half (16 / 32 / 64 / 64 / 128 bytes by format)
     float sc;
     uint32_t id2;      // the 4 bytes holding the block id (kb * R + r), as loaded
     uint32_t hi16;     // which half of id2 is the id
     int f;             // format, or 5 for "no block": the column is zero in this step
 };
 
-// Workgroup (mt, nt, split) owns rows [BM*mt, +BM) of x (BM = 64*MS) and
-// weight rows [64*nt, +64), over K-blocks [KBs*split, +KBs).  Consecutive
+// Workgroup barrier that waits for this wave's LDS operations only (not for
+// its outstanding global loads or copies into LDS, which are waited for
+// explicitly where their data is used).
+__device__ __forceinline__ void gemm_lds_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Workgroup (mt, nt, split) owns rows [BM*mt, +BM) of x (BM = 32*MI) and
+// weight rows [128*nt, +128), over K-blocks [KBs*split, +KBs).  Consecutive
 // workgroup indices go to different XCDs in turn, so the index is permuted
 // (when the grid is a multiple of 8) such that each XCD gets a contiguous run
 // of tiles, mostly one row tile of x, which its L2 then serves to all of them.
 //
-// Waves 0-3 run the MFMAs (wave c: rows [16*MS*c, +16*MS), all 64 columns)
-// and copy the next step's x tile straight from memory into LDS; waves 4-7
-// load the packed blocks two steps ahead into registers and dequantise the
-// next step's.  A workgroup's waves are spread over the four SIMDs in turn,
-// so each SIMD normally runs one wave of each kind and its matrix core and
-// vector ALU can work at the same time.  One workgroup barrier per step.
-template <int MS>
+// MFMA wave c owns rows [16*MI*(c>>1), +16*MI) and columns [64*(c&1), +64) of
+// the tile (MI row tiles of 16, four column groups of 16).  A workgroup's
+// waves are spread over the four SIMDs in turn, so each SIMD normally runs
+// one wave of each kind and its matrix core and vector ALU work at the same
+// time.
+template <int MI>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
-    constexpr uint32_t BM = 64 * MS;
+    constexpr uint32_t BM = 32 * MI;
     // x tiles: row r at 128 * r bytes, 16-byte slot s holds the row's entries
     // [8 * (s ^ ((r >> 1) & 7)), +8) (a swizzle that makes the MFMA operand
-    // reads conflict-free); three steps in flight, as separate objects so
-    // that the compiler sees the copies into one do not touch the others
-    __shared__ __align__(16) uint16_t xs0[BM * 64], xs1[BM * 64], xs2[BM * 64];
+    // reads conflict-free); two stages, as separate objects so that the
+    // compiler sees the copies into one do not touch the other
+    __shared__ __align__(16) uint16_t xs0[BM * 64], xs1[BM * 64];
     __shared__ __align__(16) WStage wt0, wt1;
 
     const LayerDev &w = a.w;
@@ -108,10 +120,22 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
 
     if (wave < 4) {
         // ================= MFMA waves =================
-        const uint32_t c = wave;
-        // x copy: 8-row group g = 2*MS*c + i of the tile per instruction i;
-        // lane l -> row 8g + l/8, slot l%8
+        const uint32_t c = wave, wr = c >> 1, wc = c & 1;
+        // x copy: wave c copies rows [BM/4 * c, +BM/4) (8 * MI rows), 8 rows per instruction;
+        // lane l -> row 8g + l/8, slot l%8 of 8-row group g.  Each instruction
+        // takes a uniform base (the group's first row, clamped to the last row
+        // of x, plus the K-step's offset) and a loop-invariant 32-bit byte
+        // offset per lane (rows past M read row M-1).
         const uint32_t xr = lane >> 3, xslot = lane & 7;
+        const uint16_t *xrow[MI];
+        uint32_t xoff[MI];
+#pragma unroll
+        for (uint32_t i = 0; i < MI; ++i) {
+            const uint32_t g = MI * c + i, r = 8 * g + xr;
+            const uint32_t rb = min(m0 + 8 * g, a.M - 1u), rr = min(m0 + r, a.M - 1u);
+            xrow[i] = a.x + int64_t(rb) * a.ldx;
+            xoff[i] = uint32_t((uint64_t(rr - rb) * uint64_t(a.ldx) + 8u * (xslot ^ ((r >> 1) & 7u))) * 2u);
+        }
         // Issued as inline assembly (M0 = LDS destination of the wave's 1 KiB),
         // so the compiler does not add waits for these copies before unrelated
         // LDS reads; this wave issues no other vector-memory loads, and waits
@@ -119,112 +143,113 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
         // publishes them.
         auto x_copy = [&](uint32_t kb, uint16_t *xs) {
 #pragma unroll
-            for (uint32_t i = 0; i < 2 * MS; ++i) {
-                const uint32_t g = 2 * MS * c + i, r = 8 * g + xr;
-                const uint32_t seg = xslot ^ ((r >> 1) & 7u);
-                const uint16_t *src = a.x + int64_t(min(m0 + r, a.M - 1u)) * a.ldx + kb * 64u + seg * 8u;
+            for (uint32_t i = 0; i < MI; ++i) {
+                const uint32_t g = MI * c + i;
+                const uint16_t *src = xrow[i] + kb * 64u;
                 const uint32_t dst = uint32_t(uintptr_t((__attribute__((address_space(3))) uint16_t *)(xs + 8 * g * 64)));
-                asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                              :
-                             : "v"(src), "s"(dst)
+                             : "v"(xoff[i]), "s"(src), "s"(dst)
                              : "memory", "m0");
             }
         };
         const uint32_t lr = lane & 15, lq = lane >> 4;      // MFMA operand row / k-quarter of this lane
-        f32x4 acc[MS][4];
+        f32x4 acc[MI][4];
 #pragma unroll
-        for (int i = 0; i < MS; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        // One K-step on LDS stages xs / st.  Hi planes: a fresh 64-term partial
-        // per 16x16 tile, added to acc times the column's scale (all operands
-        // read first, so the MFMAs and the scaling run as one straight-line
-        // sequence).  Lo planes (only in 16-column groups with an FP16 / FP32
-        // block; zero in integer columns, and float blocks have scale 1) go
-        // into acc directly through the MFMA accumulator.
+        // One K-step on LDS stages xs / st.  Per row tile: the hi plane's
+        // 64-term partials of the four column groups (fresh accumulators),
+        // added to acc times the column's scale; then the lo plane of the
+        // groups that hold an FP16 / FP32 block, straight into acc.
         auto mfma_step = [&](const uint16_t *xs, const WStage &st) {
-            bf16x8 A[MS][2], Bh[4][2];
+            bf16x8 Bh[4][2], Bl[4][2];
             float sc[4];
-            // read order = first use: row tile 0, all column groups, then the
-            // other row tiles (LDS reads complete in order, so the first MFMAs
-            // wait for four reads, not all of them)
-            auto readA = [&](int i) {
-                const uint32_t r = 16 * MS * c + 16 * i + lr;
+            const uint4 nlo4 = *reinterpret_cast<const uint4 *>(&st.need_lo[4 * wc]);
+            const uint32_t nl[4] = {uint32_t(__builtin_amdgcn_readfirstlane(nlo4.x)),
+                                    uint32_t(__builtin_amdgcn_readfirstlane(nlo4.y)),
+                                    uint32_t(__builtin_amdgcn_readfirstlane(nlo4.z)),
+                                    uint32_t(__builtin_amdgcn_readfirstlane(nlo4.w))};
+            auto readA = [&](int i, bf16x8 (&A)[2]) {
+                const uint32_t r = 16 * MI * wr + 16 * i + lr;
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
-                    A[i][h] = *reinterpret_cast<const bf16x8 *>(xs + r * 64 + 8 * ((lq + 4 * h) ^ ((r >> 1) & 7u)));
+                    A[h] = *reinterpret_cast<const bf16x8 *>(xs + r * 64 + 8 * ((lq + 4 * h) ^ ((r >> 1) & 7u)));
             };
-            readA(0);
+            bf16x8 A[2];
+            readA(0, A);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                Bh[j][0] = *reinterpret_cast<const bf16x8 *>(&st.whi[16 * j + lr][8 * lq]);
-                Bh[j][1] = *reinterpret_cast<const bf16x8 *>(&st.whi[16 * j + lr][32 + 8 * lq]);
-                sc[j] = st.scale[16 * j + lr];
+                const uint32_t col = 64 * wc + 16 * j + lr;
+                Bh[j][0] = *reinterpret_cast<const bf16x8 *>(&st.whi[col][8 * lq]);
+                Bh[j][1] = *reinterpret_cast<const bf16x8 *>(&st.whi[col][32 + 8 * lq]);
+                sc[j] = st.scale[col];
             }
 #pragma unroll
-            for (int i = 1; i < MS; ++i) readA(i);
-            const uint4 nlo = *reinterpret_cast<const uint4 *>(st.need_lo);
+            for (int j = 0; j < 4; ++j) {
+                if (nl[j] != 0u) {
+                    const uint32_t col = 64 * wc + 16 * j + lr;
+                    Bl[j][0] = *reinterpret_cast<const bf16x8 *>(&st.wlo[col][8 * lq]);
+                    Bl[j][1] = *reinterpret_cast<const bf16x8 *>(&st.wlo[col][32 + 8 * lq]);
+                }
+            }
 #pragma unroll
-            for (int i = 0; i < MS; ++i)
+            for (int i = 0; i < MI; ++i) {
+                bf16x8 An[2];
+                if (i + 1 < MI) readA(i + 1, An);
+                f32x4 cc[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    f32x4 cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][0], Bh[j][0], (f32x4{0.f, 0.f, 0.f, 0.f}), 0, 0, 0);
-                    cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][1], Bh[j][1], cc, 0, 0, 0);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(sc[j], cc[e], acc[i][j][e]);
+                    cc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0], Bh[j][0], (f32x4{0.f, 0.f, 0.f, 0.f}), 0, 0, 0);
+                    cc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[1], Bh[j][1], cc[j], 0, 0, 0);
                 }
-            const uint32_t lo[4] = {nlo.x, nlo.y, nlo.z, nlo.w};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (__builtin_amdgcn_readfirstlane(lo[j]) != 0u) {
-                    const bf16x8 Bl0 = *reinterpret_cast<const bf16x8 *>(&st.wlo[16 * j + lr][8 * lq]);
-                    const bf16x8 Bl1 = *reinterpret_cast<const bf16x8 *>(&st.wlo[16 * j + lr][32 + 8 * lq]);
+                for (int j = 0; j < 4; ++j)
 #pragma unroll
-                    for (int i = 0; i < MS; ++i) {
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][0], Bl0, acc[i][j], 0, 0, 0);
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][1], Bl1, acc[i][j], 0, 0, 0);
+                    for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(sc[j], cc[j][e], acc[i][j][e]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (nl[j] != 0u) {
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0], Bl[j][0], acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[1], Bl[j][1], acc[i][j], 0, 0, 0);
                     }
+                }
+                if (i + 1 < MI) {
+                    A[0] = An[0];
+                    A[1] = An[1];
                 }
             }
         };
 
-        // Workgroup barrier that leaves this wave's outstanding x copies in
-        // flight (the copy of a step is waited for, vmcnt(0), at the end of
-        // the step before the one that reads it).
-        auto cbar = [&]() {
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-            __builtin_amdgcn_s_barrier();
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        };
-        // x: three LDS stages; the copy for step t+2 is issued at the end of step t
+        // x: two LDS stages; the copy for step t+2 goes into step t's stage
+        // right after the barrier that ends step t
         x_copy(kb0, xs0);
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copy is in LDS
         if (nsteps > 1) x_copy(kb0 + 1, xs1);
-        cbar();
-        auto cstep = [&](uint32_t t, const uint16_t *xc, uint16_t *xn2) {
+        gemm_lds_barrier();
+        auto cstep = [&](uint32_t t, uint16_t *xc) {
             mfma_step(xc, (t & 1) ? wt1 : wt0);
             __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the copy for step t+1 is in LDS
-            if (t + 2 < nsteps) x_copy(kb0 + t + 2, xn2);
-            cbar();
+            gemm_lds_barrier();
+            if (t + 2 < nsteps) x_copy(kb0 + t + 2, xc);
         };
-        for (uint32_t t = 0; t < nsteps; t += 3) {
-            cstep(t, xs0, xs2);
-            if (t + 1 < nsteps) cstep(t + 1, xs1, xs0);
-            if (t + 2 < nsteps) cstep(t + 2, xs2, xs1);
+        for (uint32_t t = 0; t < nsteps; t += 2) {
+            cstep(t, xs0);
+            if (t + 1 < nsteps) cstep(t + 1, xs1);
         }
 
         // ---- output: lane holds column lr, rows 4*(lane/16) + e of each 16x16 tile ----
 #pragma unroll
-        for (int i = 0; i < MS; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const uint32_t n = n0 + 16 * j + lr;
+                const uint32_t n = n0 + 64 * wc + 16 * j + lr;
                 if (n >= w.N) continue;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const uint32_t m = m0 + 16 * MS * c + 16 * i + 4 * lq + e;
+                    const uint32_t m = m0 + 16 * MI * wr + 16 * i + 4 * lq + e;
                     if (m >= a.M) continue;
                     float v = acc[i][j][e];
                     if (a.partial) {
@@ -240,8 +265,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
     }
 
     // ================= producer waves =================
-    // thread pt -> quarter `part` of column gb
-    const uint32_t pt = tid - 256, pw = wave - 4, part = pt & 3, gb = pt >> 2;
+    // thread pt -> half h of column slot gb (the slot's block is the
+    // (gb % R)-th block of its row tile in this step, in format order)
+    const uint32_t pt = tid - 256, h = pt & 1, gb = pt >> 1;
     const uint8_t *base = w.base;                            // offsets below are 32-bit (buffer < 4 GiB)
     uint32_t opay[5], oids[5];
 #pragma unroll
@@ -254,7 +280,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
     const bool tok = tile < w.T;
     const uint32_t kbx = uint32_t(w.off_kbidx) + 4u * (tok ? tile * KB : 0u);
     // kbidx[f][tile*KB + kb]: block index where step kb starts in format f
-    // (loaded by every lane; a column past N reads tile 0 and takes zeros)
+    // (a column past N reads tile 0 and takes zeros)
     auto kload = [&](uint32_t kb, uint32_t (&v)[5]) {
         kb = min(kb, kb1);
 #pragma unroll
@@ -264,11 +290,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
         }
     };
 
-    // Loads of one column's block in the step that starts at ka and ends at
-    // kn (a step past the split's end has no blocks): up to four 16-byte loads
-    // at addresses chosen per format; a missing block reads the buffer's first
-    // bytes.  INT4's 8-byte quarter p comes with its neighbour in a 16-byte
-    // load at 16 * (p / 2).
+    // Loads of this thread's half block in the step that starts at ka and
+    // ends at kn (a step past the split's end has no blocks): up to eight
+    // 16-byte loads at addresses chosen per format; a missing block reads the
+    // buffer's first bytes.
     auto load_block = [&](const uint32_t (&ka)[5], const uint32_t (&kn)[5]) -> BlockLoad {
         BlockLoad q;
         q.f = 5;
@@ -284,47 +309,47 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
         }
         const bool has = q.f < 5;
         const int f = has ? q.f : 0;
-        uint32_t po = 0, io = 0, so = 0, qb = 0, nl = 1;
+        uint32_t po = 0, io = 0, so = 0, nl = 1;
 #pragma unroll
         for (int g = 0; g < 5; ++g) {
             if (f == g) {
-                po = opay[g] + blk * uint32_t(pay_bytes(g));
+                po = opay[g] + blk * uint32_t(pay_bytes(g)) + h * uint32_t(pay_bytes(g) / 2);
                 io = oids[g] + ((2u * blk) & ~3u);
                 so = g == 0 ? osc0 + 4u * blk : g == 1 ? osc1 + 4u * blk : 0u;
-                qb = g == 0 ? 16u * (part >> 1) : uint32_t(pay_bytes(g) / 4) * part;
-                nl = g < 2 ? 1u : g == 4 ? 4u : 2u;
+                nl = uint32_t(pay_bytes(g) / 32);
             }
         }
-        if (!has) po = io = so = qb = 0;
-        // the first 16 bytes always; the rest only for lanes whose quarter is
-        // longer (BF16 / FP16 / FP32), so an integer-only wave skips them
-        q.p[0] = *reinterpret_cast<const uint4 *>(base + (po + qb));
+        if (!has) po = io = so = 0;
+        // the first 16 bytes always; the rest only for lanes whose half is
+        // longer, so a wave without float blocks skips them
+        q.p[0] = *reinterpret_cast<const uint4 *>(base + po);
 #pragma unroll
-        for (uint32_t j = 1; j < 4; ++j)
-            q.p[j] = j < nl ? *reinterpret_cast<const uint4 *>(base + (po + qb + 16u * j)) : make_uint4(0, 0, 0, 0);
+        for (uint32_t j = 1; j < 8; ++j)
+            q.p[j] = j < nl ? *reinterpret_cast<const uint4 *>(base + (po + 16u * j)) : make_uint4(0, 0, 0, 0);
         q.id2 = *reinterpret_cast<const uint32_t *>(base + io);
         q.hi16 = blk & 1u;
         q.sc = *reinterpret_cast<const float *>(base + so);   // meaningful for INT4 / INT8 only
         return q;
     };
 
-    // Dequantise one column's quarter into st: entries [16*part, 16*part + 16)
-    // (INT4 quarters cover two runs of 8, see the nibble order of the layout),
-    // as packed bfloat16 pairs: integers via an exact fp32 conversion whose
-    // upper half is the bfloat16 (v_perm packs two), floats as hi = upper half
-    // (truncation) and lo = bf16_rne(w - hi) (v_cvt_pk_bf16_f32).  A
-    // non-finite FP16/FP32 entry makes lo NaN, so its output column is NaN.
+    // Dequantise one half block into st: entries [32h, 32h + 32) of the
+    // column, as packed bfloat16 pairs: integers via an exact fp32 conversion
+    // whose upper half is the bfloat16 (v_perm packs two), floats as hi =
+    // upper half (truncation) and lo = bf16_rne(w - hi).  A non-finite
+    // FP16/FP32 entry makes lo NaN, so its output column is NaN.
     auto store_block = [&](const BlockLoad &b, WStage &st) {
         const uint32_t id = b.hi16 ? b.id2 >> 16 : b.id2;
-        const uint32_t col = (gb / R) * R + (b.f < 5 ? (id & (R - 1u)) : bi);   // within the 64
+        const uint32_t col = (gb / R) * R + (b.f < 5 ? (id & (R - 1u)) : bi);   // within the 128
         const bool flt = b.f == 3 || b.f == 4;
-        const bool any_lo = __any(flt);                         // this wave's 16 columns need the lo plane
-        const uint32_t u[16] = {b.p[0].x, b.p[0].y, b.p[0].z, b.p[0].w, b.p[1].x, b.p[1].y, b.p[1].z, b.p[1].w,
-                                b.p[2].x, b.p[2].y, b.p[2].z, b.p[2].w, b.p[3].x, b.p[3].y, b.p[3].z, b.p[3].w};
-        uint32_t hp[8], lp[8];
+        const uint64_t bal = __ballot(flt);
+        const bool any_lo = ((bal >> (lane & 32u)) & 0xFFFFFFFFull) != 0;   // this column group needs the lo plane
+        const uint32_t u[32] = {b.p[0].x, b.p[0].y, b.p[0].z, b.p[0].w, b.p[1].x, b.p[1].y, b.p[1].z, b.p[1].w,
+                                b.p[2].x, b.p[2].y, b.p[2].z, b.p[2].w, b.p[3].x, b.p[3].y, b.p[3].z, b.p[3].w,
+                                b.p[4].x, b.p[4].y, b.p[4].z, b.p[4].w, b.p[5].x, b.p[5].y, b.p[5].z, b.p[5].w,
+                                b.p[6].x, b.p[6].y, b.p[6].z, b.p[6].w, b.p[7].x, b.p[7].y, b.p[7].z, b.p[7].w};
+        uint32_t hp[16], lp[16];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) lp[i] = 0u;
-        uint32_t k0 = 16 * part, k1 = k0 + 8;                  // where the two runs of 8 go
+        for (int i = 0; i < 16; ++i) lp[i] = 0u;
         auto nib = [](uint32_t v, uint32_t at) { return int32_t(v << (28u - at)) >> 28; };   // signed 4-bit field
         auto pair_hi = [](float f0, float f1) {                 // upper halves of two fp32 -> one word
             return __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
@@ -337,32 +362,33 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
         };
         switch (b.f) {
         case 0:
-            // bytes 8p .. 8p+7 (words 2*(p&1), +1 of the 16-byte load): low nibble
-            // -> entry 32*(p/2) + 8*(p%2) + i, high nibble -> that + 16
-            k0 = 32 * (part >> 1) + 8 * (part & 1);
-            k1 = k0 + 16;
+            // the half's 16 bytes: byte i of the first 8 holds entries 32h+i
+            // (low nibble) and 32h+16+i (high), byte 8+i entries 32h+8+i and
+            // 32h+24+i (the nibble order of the layout)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t wd = (part & 1) ? ((i >> 1) ? u[3] : u[2]) : ((i >> 1) ? u[1] : u[0]);
-                const uint32_t sh = 16 * (i & 1);
-                hp[i] = pair_hi(float(nib(wd, sh)), float(nib(wd, sh + 8)));
-                hp[4 + i] = pair_hi(float(nib(wd, sh + 4)), float(nib(wd, sh + 12)));
-            }
+            for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t wd = u[2 * q2 + (i >> 1)];
+                    const uint32_t sh = 16 * (i & 1);
+                    hp[4 * q2 + i] = pair_hi(float(nib(wd, sh)), float(nib(wd, sh + 8)));
+                    hp[8 + 4 * q2 + i] = pair_hi(float(nib(wd, sh + 4)), float(nib(wd, sh + 12)));
+                }
             break;
         case 1:
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < 16; ++i) {
                 const uint32_t wd = u[i >> 1], sh = 16 * (i & 1);
                 hp[i] = pair_hi(float(int8_t(wd >> sh)), float(int8_t(wd >> (sh + 8))));
             }
             break;
         case 2:
 #pragma unroll
-            for (int i = 0; i < 8; ++i) hp[i] = u[i];
+            for (int i = 0; i < 16; ++i) hp[i] = u[i];
             break;
         case 3:
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < 16; ++i) {
                 const float f0 = float(__builtin_bit_cast(_Float16, uint16_t(u[i])));
                 const float f1 = float(__builtin_bit_cast(_Float16, uint16_t(u[i] >> 16)));
                 hp[i] = pair_hi(f0, f1);
@@ -371,7 +397,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
             break;
         case 4:
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < 16; ++i) {
                 const float f0 = __uint_as_float(u[2 * i]), f1 = __uint_as_float(u[2 * i + 1]);
                 hp[i] = pair_hi(f0, f1);
                 lp[i] = pair_lo(f0, f1);
@@ -379,20 +405,23 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
             break;
         default:
 #pragma unroll
-            for (int i = 0; i < 8; ++i) hp[i] = 0u;
+            for (int i = 0; i < 16; ++i) hp[i] = 0u;
             break;
         }
-        *reinterpret_cast<uint4 *>(&st.whi[col][k0]) = make_uint4(hp[0], hp[1], hp[2], hp[3]);
-        *reinterpret_cast<uint4 *>(&st.whi[col][k1]) = make_uint4(hp[4], hp[5], hp[6], hp[7]);
+        const uint32_t k0 = 32 * h;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<uint4 *>(&st.whi[col][k0 + 8 * i]) = make_uint4(hp[4 * i], hp[4 * i + 1], hp[4 * i + 2], hp[4 * i + 3]);
         if (any_lo) {
-            *reinterpret_cast<uint4 *>(&st.wlo[col][k0]) = make_uint4(lp[0], lp[1], lp[2], lp[3]);
-            *reinterpret_cast<uint4 *>(&st.wlo[col][k1]) = make_uint4(lp[4], lp[5], lp[6], lp[7]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<uint4 *>(&st.wlo[col][k0 + 8 * i]) = make_uint4(lp[4 * i], lp[4 * i + 1], lp[4 * i + 2], lp[4 * i + 3]);
         }
-        if (part == 0) st.scale[col] = b.f < 2 ? b.sc : 1.0f;
-        if (lane == 0) st.need_lo[pw] = any_lo ? 1u : 0u;
+        if (h == 0) st.scale[col] = b.f < 2 ? b.sc : 1.0f;
+        if ((lane & 31u) == 0) st.need_lo[gb >> 4] = any_lo ? 1u : 0u;
     };
 
-    // kbidx entries run one step ahead of the block loads, which run two
+    // kbidx entries run two steps ahead of the block loads, which run two
     // steps ahead of the dequantisation
     uint32_t K2[5], K3[5], K4[5];
     BlockLoad QA, QB;
@@ -406,7 +435,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
         QA = load_block(K1, K2);
         store_block(QB, wt0);
     }
-    __syncthreads();
+    gemm_lds_barrier();
     // qc: the loads of step t+1; qn receives those of step t+2
     auto step = [&](uint32_t t, BlockLoad &qc, BlockLoad &qn, WStage &dst) {
         kload(kb0 + t + 4, K4);
@@ -417,7 +446,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
             K3[f] = K4[f];
         }
         if (t + 1 < nsteps) store_block(qc, dst);
-        __syncthreads();
+        gemm_lds_barrier();
     };
     for (uint32_t t = 0; t < nsteps; t += 2) {
         step(t, QA, QB, wt1);
@@ -430,28 +459,24 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
 // ---------------------------------------------------------------------------
 namespace {
 
-template <int MS>
+template <int MI>
 void launch_gemm(const GemmArgs &a, uint32_t S, hipStream_t s) {
     const uint32_t grid = a.MT * a.NT * S;
-    hipLaunchKernelGGL(gemm_kernel<MS>, dim3(grid), dim3(kGemmThreads), 0, s, a);
+    hipLaunchKernelGGL(gemm_kernel<MI>, dim3(grid), dim3(kGemmThreads), 0, s, a);
 }
 
-}  // namespace
-
-namespace {
-
 constexpr int64_t kGemmChunkRows = int64_t(1) << 20;   // rows per launch
-constexpr uint64_t kSplitTarget = 256;                   // compute units
+constexpr int64_t kGemmMaxLdx = int64_t(1) << 28;       // x row stride limit (elements)
+constexpr uint64_t kSplitTarget = 256;                   // compute units (one workgroup each)
 
 uint32_t gemm_bm(int64_t M) { return M >= 256 ? 256u : M >= 128 ? 128u : 64u; }
 
-// K-splits when there are fewer tiles than workgroup slots (one per compute
-// unit, two for 64-row tiles, whose LDS and registers allow two): at least 8
+// K-splits when there are fewer tiles than compute units: at least 8
 // K-blocks per split, every split non-empty.
 uint32_t gemm_splits(const ht_packed_weight *w, int64_t M) {
     const uint32_t KB = uint32_t(w->K / kBlockK);
     const uint64_t tiles = uint64_t((w->N + kGemmBN - 1) / kGemmBN) * uint64_t((M + gemm_bm(M) - 1) / gemm_bm(M));
-    const uint64_t target = gemm_bm(M) == 64 ? 2 * kSplitTarget : kSplitTarget;   // two 64-row workgroups fit a CU
+    const uint64_t target = kSplitTarget;
     if (tiles * 4 >= target * 3 || KB < 16) return 1;
     uint32_t S = uint32_t((target + tiles - 1) / tiles);
     if (S > KB / 8) S = KB / 8;
@@ -465,6 +490,7 @@ uint32_t gemm_split_count(const ht_packed_weight *w, int64_t Mt) { return gemm_s
 
 ht_status gemm_tiles(const ht_packed_weight *w, const uint16_t *x, int64_t Mt, int64_t ldx, float *y, uint16_t *ybf,
                      int64_t ldy, int act, float *partial, uint32_t S, bool skip_int8, hipStream_t s) {
+    if (ldx >= kGemmMaxLdx) return HT_ESHAPE;   // the x copies take 32-bit offsets of up to 7 rows
     GemmArgs a;
     a.w = layer_dev(w);
     a.x = x;
@@ -481,9 +507,9 @@ ht_status gemm_tiles(const ht_packed_weight *w, const uint16_t *x, int64_t Mt, i
     a.NT = uint32_t((a.w.N + kGemmBN - 1) / kGemmBN);
     a.skip_int8 = skip_int8 ? 1u : 0u;
     switch (BM) {
-    case 256: launch_gemm<4>(a, S, s); break;
-    case 128: launch_gemm<2>(a, S, s); break;
-    default: launch_gemm<1>(a, S, s); break;
+    case 256: launch_gemm<8>(a, S, s); break;
+    case 128: launch_gemm<4>(a, S, s); break;
+    default: launch_gemm<2>(a, S, s); break;
     }
     HT_LAUNCH_CHECK();
     return HT_OK;

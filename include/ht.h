@@ -240,7 +240,8 @@ ht_status ht_linear_workspace(const ht_packed_weight *w, int64_t M, int32_t path
 /* ht_linear_forward -- the fused mixed-format linear y = x . W_hat^T
  * ("Key Features": drop-in HyperLinear for nn.Linear, no bias).
  *   w      (host) descriptor from ht_pack.
- *   x      bfloat16 bit patterns [M, ldx], ldx >= K.
+ *   x      bfloat16 bit patterns [M, ldx], ldx >= K (on HT_PATH_GEMM and
+ *          HT_PATH_GEMM_I8 also ldx < 2^28, else HT_ESHAPE).
  *   y      fp32 [M, ldy] out, ldy >= N: y[m, n] = act(sum_k x[m,k] * w_hat[n,k]),
  *          accumulated in fp32; integer blocks apply their scale after the
  *          block's 64-term partial sum.  The result is bitwise reproducible
