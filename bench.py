@@ -333,12 +333,17 @@ def main() -> int:
 
     def backward_leg():
         """The input gradient dX = dY . W_hat (ht_linear_backward_data) at 1
-        and 4 rows of fp32 dY: the 4096x4096 MLP layer (default thresholds)
-        and the Llama-8B q / gate / down shapes.  Graph replays of calls that
+        and 4 rows of fp32 dY (register path) and at 2048 rows (matrix-core
+        path; TFLOP/s of 2*M*N*K and its fraction of the 2.5 PFLOP/s bf16
+        peak, the kernel issuing three bf16 products per product): the
+        4096x4096 MLP layer (default thresholds) and the Llama-8B q / gate /
+        down shapes.  Graph replays of calls that
         rotate over copies of the packed weight holding together more than
         512 MB (the Infinity Cache holds 256 MB); GB/s counts packed bytes +
         dY + dX.  The weight gradient writes a fresh 64 MB fp32 dW per call
-        (write-bound, not served by the cache)."""
+        (write-bound, not served by the cache); from 64 rows on the matrix cores,
+        at 2048 rows compute-bound (TFLOP/s of 2*M*N*K, two bf16 products per
+        product)."""
         res = {}
         cases = [("mlp4096", None)] + [(s_.name, s_) for s_ in wl.llama8b_shapes() if s_.name in ("q", "gate", "down")]
         for name, shp in cases:
@@ -364,11 +369,23 @@ def main() -> int:
                 nb = pw.nbytes + 4 * M * (pw.N + pw.K)
                 row[f"M{M}"] = {"us": round(t * 1e6, 2), "GBps": round(nb / t / 1e9, 1)}
                 del g
+            # training batch: 2048 rows of dY on the matrix-core path
+            M = 2048
+            dy = torch.randn(M, pw.N, device=dev)
+            dx = torch.empty(M, pw.K, device=dev)
+            ws = api.workspace(B.ht_linear_backward_workspace(pw.desc, M), dev)
+            api.linear_backward_data(pw, dy, out=dx, ws=ws)
+            torch.cuda.synchronize()
+            t = timed(lambda i: api.linear_backward_data(pws[i % len(pws)], dy, out=dx, ws=ws), 6)
+            fl = 2.0 * M * pw.N * pw.K
+            row["M2048"] = {"us": round(t * 1e6, 1), "TFLOPs": round(fl / t / 1e12, 1),
+                            "mfma_frac": round(fl / t / 2.5e15, 4)}
+            del dy, dx, ws
             res[name] = row
             del pw, pws
         # STE weight gradient dW = dY^T . x (fp32 [N, K] written): 4096 x 4096
         wg = {}
-        for M in (1, 32):
+        for M in (1, 32, 2048):
             dy = torch.randn(M, 4096, device=dev)
             xb = torch.randn(M, 4096, device=dev).to(torch.bfloat16)
             dw = torch.empty(4096, 4096, device=dev)
@@ -383,10 +400,12 @@ def main() -> int:
             torch.cuda.synchronize()
             t = timed(lambda i: g.replay(), 5) / 10
             nb = 4 * 4096 * 4096 + M * (2 * 4096 + 4 * 4096)
-            wg[f"M{M}"] = {"us": round(t * 1e6, 2), "GBps": round(nb / t / 1e9, 1)}
+            fl = 2.0 * M * 4096 * 4096
+            wg[f"M{M}"] = {"us": round(t * 1e6, 2), "GBps": round(nb / t / 1e9, 1),
+                           "TFLOPs": round(fl / t / 1e12, 1), "mfma_frac": round(fl / t / 2.5e15, 4)}
             del g, dw
-        return {"kernel": "linear_bwd_kernel<M>", "shapes": res,
-                "weight_grad_4096": {"kernel": "linear_dw_kernel", **wg}}
+        return {"kernel": "linear_bwd_kernel<M> (M < 16), bwd_gemm_kernel<4> (M = 2048)", "shapes": res,
+                "weight_grad_4096": {"kernel": "linear_dw_kernel (M < 64), dw_gemm_kernel (M >= 64)", **wg}}
 
     if args.only == "backward":
         print(json.dumps(backward_leg()))

@@ -315,7 +315,7 @@ extern "C" ht_status ht_linear_backward_workspace(const ht_packed_weight *w, int
     if (!bytes || !desc_ok(w)) return HT_EINVAL;
     if (M <= 0) return HT_ESHAPE;
     if (!bwd_ok(w)) return HT_EINVAL;
-    *bytes = bwd_ws(w, M);
+    *bytes = M >= kBwdGemmMinM ? bwd_gemm_ws(w, M) : bwd_ws(w, M);
     return HT_OK;
 }
 
@@ -325,8 +325,10 @@ extern "C" ht_status ht_linear_backward_data(const ht_packed_weight *w, const fl
     if (!bwd_ok(w)) return HT_EINVAL;
     if (M <= 0 || lddy < w->N || lddx < w->K) return HT_ESHAPE;
     if (!al16(dy) || !al16(dx) || !al16(w->base)) return HT_EALIGN;
-    const size_t need = bwd_ws(w, M);
+    const bool mfma = M >= kBwdGemmMinM;
+    const size_t need = mfma ? bwd_gemm_ws(w, M) : bwd_ws(w, M);
     if (need && (!ws || ws_bytes < need)) return HT_ESMALL;
     if (ws && !al16(ws)) return HT_EALIGN;
+    if (mfma) return run_bwd_gemm(w, dy, M, lddy, dx, lddx, ws, reinterpret_cast<hipStream_t>(stream));
     return run_bwd(w, dy, M, lddy, dx, lddx, ws, reinterpret_cast<hipStream_t>(stream));
 }

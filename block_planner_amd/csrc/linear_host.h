@@ -64,6 +64,19 @@ size_t bwd_ws(const ht_packed_weight *w, int64_t M);
 ht_status run_bwd(const ht_packed_weight *w, const float *dy, int64_t M, int64_t lddy, float *dx, int64_t lddx,
                   void *ws, hipStream_t s);
 
+// The input gradient on the matrix cores (row tile 16), for M >= 16 rows of
+// dY: its workspace bytes (per-split partial tiles) and one call.
+constexpr int64_t kBwdGemmMinM = 16;
+size_t bwd_gemm_ws(const ht_packed_weight *w, int64_t M);
+ht_status run_bwd_gemm(const ht_packed_weight *w, const float *dy, int64_t M, int64_t lddy, float *dx,
+                       int64_t lddx, void *ws, hipStream_t s);
+
+// The weight gradient on the matrix cores, for M >= 64 rows (arguments
+// assumed checked).
+constexpr int64_t kDwGemmMinM = 64;
+ht_status run_dw_gemm(const float *dy, int64_t M, int64_t lddy, const uint16_t *x, int64_t ldx, int64_t N,
+                      int64_t K, float *dw, int64_t lddw, int accumulate, hipStream_t s);
+
 // The path HT_PATH_AUTO resolves to for one linear over M rows: the MFMA
 // decode path for 4..32 rows (row tile 16), otherwise the LDS-staged MFMA path
 // from 16 rows and the register path below (1 to 3 rows stay on the register

@@ -317,10 +317,17 @@ ht_status ht_linear_backward_workspace(const ht_packed_weight *w, int64_t M, siz
  *   w      (host) descriptor from ht_pack; row tile 16 only, else HT_EINVAL.
  *   dy     fp32 [M, lddy], lddy >= N (the gradient of y).
  *   dx     fp32 [M, lddx] out, lddx >= K: dx[m, k] = sum_n dy[m, n] *
- *          w_hat[n, k], in fp32 (integer blocks as (dy * s) * q), summed in
- *          a fixed order (bitwise reproducible); columns k >= K untouched.
+ *          w_hat[n, k], summed in a fixed order (bitwise reproducible);
+ *          columns k >= K untouched.  Below 16 rows of dY: fp32 arithmetic
+ *          on the vector units (integer blocks as (dy * s) * q).  From 16
+ *          rows: bf16 MFMAs, dY and w_hat (s * q rounded to fp32 for
+ *          integer blocks) each as a hi + lo pair of bfloat16 planes, the
+ *          products hi.hi + hi.lo + lo.hi accumulated in fp32 (16
+ *          significant bits of each factor; fp32 subnormals kept down to
+ *          2^-133; an Inf or NaN weight entry gives NaN in its dx column).
  *   ws     workspace of ws_bytes >= ht_linear_backward_workspace(w, M):
- *          per-tile-group sums, added in group order by a second kernel.
+ *          per-split partial sums (over groups of row tiles of W), added
+ *          in split order by a second kernel.
  * Forward-only state is not needed: W may have been freed after packing. */
 ht_status ht_linear_backward_data(const ht_packed_weight *w, const float *dy, int64_t M, int64_t lddy,
                                   float *dx, int64_t lddx, void *ws, size_t ws_bytes, ht_stream stream);
@@ -333,9 +340,12 @@ ht_status ht_linear_backward_data(const ht_packed_weight *w, const float *dy, in
  *   x      bf16 bits [M, ldx], ldx >= K, ldx % 4 == 0: the activations the
  *          forward consumed.
  *   dw     fp32 [N, lddw] out, lddw >= K, lddw % 4 == 0, K % 4 == 0:
- *          dw[n, k] = sum_m dy[m, n] * x[m, k] in fp32, m in order (bitwise
+ *          dw[n, k] = sum_m dy[m, n] * x[m, k] in a fixed order (bitwise
  *          reproducible); with accumulate != 0 that sum is added to dw
  *          (gradient accumulation); M == 0 writes zeros (or leaves dw).
+ *          Below 64 rows: fp32 arithmetic, m in order.  From 64 rows: bf16
+ *          MFMAs, dY as a hi + lo pair of bfloat16 planes (16 significant
+ *          bits) against the exact bfloat16 x, fp32 accumulation.
  *   No workspace; dy, x and dw 16-byte aligned (HT_EALIGN), 4 * ceil(N / 16)
  *   at most 65535 (HT_ESHAPE).  Needs no packed weight: the plan and the packed
  *   buffers are rebuilt from the updated master by ht_plan / ht_pack. */
