@@ -80,6 +80,8 @@ def _load():
     lib.oracle_relu_bf16.argtypes = [P, I64, P]
     lib.oracle_x_planes.restype = None
     lib.oracle_x_planes.argtypes = [P, I64, I64, I64, P, P, P]
+    lib.oracle_x_w8a8.restype = None
+    lib.oracle_x_w8a8.argtypes = [P, I64, I64, I64, P, P]
     lib.oracle_pack_layout.restype = I64
     lib.oracle_pack_layout.argtypes = [I64, I64, I64, P, P]
     lib.oracle_pack.restype = None
@@ -295,6 +297,34 @@ def linear_xplanes(W: np.ndarray, fmt: np.ndarray, x_bf16: np.ndarray) -> np.nda
     """y [M, N] (double) = x_hat . W_hat^T with x_hat the two-plane encoding of
     x: what the int8 matrix-core path computes, before fp32 rounding."""
     return x_hat(*x_planes(x_bf16)) @ dequant(W, fmt).T
+
+
+def x_w8a8(x_bf16: np.ndarray):
+    """(q, bexp): x[m, k] ~ q[m, k] * 2^bexp[m, k // 64], one int8 code per
+    entry and one power-of-two scale per token and 64-wide K-block (the W8A8
+    encoding; its definition is in ht_oracle.c)."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    assert x.ndim == 2 and x.shape[1] % BLOCK_K == 0
+    M, K = x.shape
+    q = np.zeros((M, K), np.int8)
+    bexp = np.zeros((M, K // BLOCK_K), np.int32)
+    _load().oracle_x_w8a8(_ptr(x), M, K, K, _ptr(q), _ptr(bexp))
+    return q, bexp
+
+
+def x_hat_w8a8(q: np.ndarray, bexp: np.ndarray) -> np.ndarray:
+    """The W8A8-encoded x in double; blocks marked non-finite are NaN."""
+    ok = bexp != XEXP_NONFINITE
+    e = np.repeat(np.where(ok, bexp, 0), BLOCK_K, axis=1)
+    out = np.ldexp(q.astype(np.float64), e)
+    out[~np.repeat(ok, BLOCK_K, axis=1)] = np.nan
+    return out
+
+
+def linear_w8a8(W: np.ndarray, fmt: np.ndarray, x_bf16: np.ndarray) -> np.ndarray:
+    """y [M, N] (double) = x_hat . W_hat^T with x_hat the W8A8 encoding of x:
+    what the W8A8 mode computes on its integer tiles, before fp32 rounding."""
+    return x_hat_w8a8(*x_w8a8(x_bf16)) @ dequant(W, fmt).T
 
 
 def pack_layout(N: int, K: int, R: int, counts) -> tuple[int, list[int]]:

@@ -383,6 +383,52 @@ void oracle_x_planes(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
 }
 
 /* ------------------------------------------------------------------------ */
+/* W8A8 encoding of x (the opt-in mode with int8 activations).  Per token m   */
+/* and 64-wide K-block kb, one int8 code per entry and one power-of-two      */
+/* scale:                                                                    */
+/*   amax = max over the block of |x| = f * 2^E with f in [0.5, 1);          */
+/*   q = clamp(round_half_even(x * 2^(7-E)), -127, 127)  (|x * 2^(7-E)|      */
+/*       < 128; the clamp only takes the rounding of values in [127.5, 128)); */
+/*   x_hat = q * 2^(E-7), within 2^(E-8) <= amax * 2^-7 of x.                */
+/* An all-zero block has codes 0 and exponent 0 (x_hat = 0).  A block        */
+/* holding an Inf or NaN gets the exponent OR_XEXP_NONFINITE and zero codes  */
+/* (its contributions are NaN).  q: int8 [M][K]; bexp: int32 [M][K/64], the   */
+/* exponent E - 7 of the block's scale.                                      */
+/* ------------------------------------------------------------------------ */
+void oracle_x_w8a8(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                   int8_t *q, int32_t *bexp)
+{
+    int64_t KB = K / 64;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t kb = 0; kb < KB; ++kb) {
+            const uint16_t *xb = x + m * ldx + 64 * kb;
+            int8_t *qb = q + m * K + 64 * kb;
+            double amax = 0.0;
+            int finite = 1;
+            for (int i = 0; i < 64; ++i) {
+                double v = bf16_widen(xb[i]);
+                if (!isfinite(v)) finite = 0;
+                else if (fabs(v) > amax) amax = fabs(v);
+            }
+            if (!finite) {
+                bexp[m * KB + kb] = OR_XEXP_NONFINITE;
+                for (int i = 0; i < 64; ++i) qb[i] = 0;
+                continue;
+            }
+            int E = 0;
+            if (amax > 0.0) frexp(amax, &E);
+            bexp[m * KB + kb] = amax > 0.0 ? E - 7 : 0;
+            for (int i = 0; i < 64; ++i) {
+                double v = rint(ldexp(bf16_widen(xb[i]), 7 - E));
+                if (v > 127.0) v = 127.0;
+                if (v < -127.0) v = -127.0;
+                qb[i] = (int8_t)v;
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Execution buffers: the packed layout (version 1), written out directly    */
 /* from its specification.                                                   */
 /*                                                                           */

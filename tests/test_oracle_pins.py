@@ -667,6 +667,122 @@ def test_linear_xplanes_exact_and_bounded():
 
 
 # ---------------------------------------------------------------------------
+# W8A8 encoding of x (one int8 code per entry, one power-of-two scale per
+# token and 64-wide K-block)
+# ---------------------------------------------------------------------------
+def test_x_w8a8_golden_blocks():
+    """Hand-worked blocks (tests/golden/x_w8a8.json) laid out as two tokens of
+    four K-blocks: catches an exponent off by one at powers of two, a wrong
+    rounding mode (ties), a missing clamp (127.5 rounds to 128), a scale per
+    token instead of per block, and the zero / non-finite / subnormal cases."""
+    import json
+    import os
+    import oracle
+
+    data = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "x_w8a8.json")))
+    blocks = data["blocks"]
+    assert len(blocks) == 8
+    X = np.zeros((2, 4 * 64), np.uint16)
+    for b, blk in enumerate(blocks):
+        m, kb = b // 4, b % 4
+        for i, bits in blk["x"]:
+            X[m, 64 * kb + i] = int(bits, 16)
+    q, bexp = oracle.x_w8a8(X)
+    for b, blk in enumerate(blocks):
+        m, kb = b // 4, b % 4
+        want = np.zeros(64, np.int64)
+        for i, v in blk["q"]:
+            want[i] = v
+        assert q[m, 64 * kb:64 * kb + 64].astype(np.int64).tolist() == want.tolist(), blk["what"]
+        assert int(bexp[m, kb]) == blk["bexp"], blk["what"]
+
+
+def test_x_w8a8_properties_random():
+    """Random blocks over a wide range of magnitudes, each block of a token
+    with its own magnitude: the block exponent brackets the block maximum
+    (2^(bexp+6) <= amax < 2^(bexp+7)), every code is the nearest integer to
+    x * 2^-bexp with ties to even (exact rational arithmetic on a sample)
+    clamped to +-127, and |x - x_hat| <= 2^bexp (half a step, or the clamp)."""
+    import oracle
+
+    rng = np.random.default_rng(8)
+    scales = np.array([1e-38, 3e-20, 1e-3, 1.0, 7.0, 1e5, 1e30, 2.0 ** -130])
+    x = rng.standard_t(3, size=(4, 8 * 64)) * np.repeat(scales[None, :], 64, axis=1)
+    X = wl.to_bf16_bits(x.astype(np.float32))
+    q, bexp = oracle.x_w8a8(X)
+    xf = wl.bf16_bits_to_f32(X).astype(np.float64)
+    assert q.min() >= -127 and q.max() <= 127
+    xh = oracle.x_hat_w8a8(q, bexp)
+    for m in range(4):
+        for kb in range(8):
+            blk = xf[m, 64 * kb:64 * kb + 64]
+            amax, e = np.max(np.abs(blk)), int(bexp[m, kb])
+            assert 2.0 ** (e + 6) <= amax < 2.0 ** (e + 7), (m, kb)
+            assert np.all(np.abs(xh[m, 64 * kb:64 * kb + 64] - blk) <= np.ldexp(1.0, e))
+            for i in range(0, 64, 9):
+                t = Fraction(float(blk[i])) * Fraction(2) ** (-e)
+                fl = t.numerator // t.denominator
+                d = t - fl
+                want = fl + 1 if d > Fraction(1, 2) or (d == Fraction(1, 2) and fl % 2) else fl
+                want = max(-127, min(127, want))
+                assert int(q[m, 64 * kb + i]) == want, (m, kb, i)
+
+
+def test_x_w8a8_scale_sign_and_block_independence():
+    """x * 2^j keeps the codes and moves every block exponent by j; -x negates
+    the codes; changing one block leaves every other block's codes and
+    exponent unchanged (a per-token scale would not)."""
+    import oracle
+
+    rng = np.random.default_rng(9)
+    base = wl.bf16_bits_to_f32(wl.to_bf16_bits(rng.normal(size=(3, 256)).astype(np.float32)))
+    q, bexp = oracle.x_w8a8(wl.to_bf16_bits(base))
+    for j in (-20, -1, 3, 40):
+        q2, b2 = oracle.x_w8a8(wl.to_bf16_bits(base * np.float32(2.0 ** j)))
+        assert np.array_equal(q2, q) and np.array_equal(b2, bexp + j)
+    q3, b3 = oracle.x_w8a8(wl.to_bf16_bits(-base))
+    assert np.array_equal(q3, -q) and np.array_equal(b3, bexp)
+    big = base.copy()
+    big[1, 70] = 1000.0                         # token 1, K-block 1
+    q4, b4 = oracle.x_w8a8(wl.to_bf16_bits(big))
+    same = np.ones((3, 4), bool)
+    same[1, 1] = False
+    assert np.array_equal(b4[same], bexp[same]) and b4[1, 1] > bexp[1, 1]
+    for m in range(3):
+        for kb in range(4):
+            if same[m, kb]:
+                assert np.array_equal(q4[m, 64 * kb:64 * kb + 64], q[m, 64 * kb:64 * kb + 64])
+
+
+def test_linear_w8a8_exact_on_grid_and_bounded():
+    """x_hat . W_hat^T equals the exact linear when every x is on its block's
+    grid, and otherwise differs by at most sum_k 2^bexp[m, k/64] |w_hat[n, k]|;
+    a block holding Inf makes its token's outputs NaN."""
+    import oracle
+
+    rng = np.random.default_rng(10)
+    W = (rng.normal(size=(40, 256)) * 0.02).astype(np.float32)
+    fmt = oracle.plan(W)
+    # on the grid: every block's max is 4 (E = 3, step 2^-4) and entries are multiples of 1/16
+    xr = rng.integers(-64, 65, size=(5, 256)).astype(np.float32) / np.float32(16.0)
+    xr[:, ::64] = 4.0
+    Xr = wl.to_bf16_bits(xr)
+    assert np.allclose(oracle.linear_w8a8(W, fmt, Xr), oracle.linear(W, fmt, Xr), rtol=1e-13, atol=1e-13)
+    X = wl.to_bf16_bits(rng.normal(size=(6, 256)).astype(np.float32) * np.float32(3.0))
+    yw = oracle.linear_w8a8(W, fmt, X)
+    y = oracle.linear(W, fmt, X)
+    _, bexp = oracle.x_w8a8(X)
+    step = np.repeat(np.ldexp(1.0, bexp), 64, axis=1)
+    bound = step @ np.abs(oracle.dequant(W, fmt)).T
+    assert np.all(np.abs(yw - y) <= bound * (1 + 1e-12))
+    assert np.max(np.abs(yw - y)) > 0
+    Xn = X.copy()
+    Xn[4, 200] = 0x7F80
+    yn = oracle.linear_w8a8(W, fmt, Xn)
+    assert np.all(np.isnan(yn[4])) and np.all(np.isfinite(np.delete(yn, 4, axis=0)))
+
+
+# ---------------------------------------------------------------------------
 # Input gradient of the linear (training backward)
 # ---------------------------------------------------------------------------
 def test_backward_data_is_the_adjoint():
