@@ -182,13 +182,15 @@ def main() -> int:
         return {"kernel": "gemm_kernel<8>", "peak_TFLOPs": 2500.0, "shapes": out}
 
     def i8_leg():
-        """The int8 matrix-core path (HT_PATH_GEMM_I8) against the MFMA path
-        at M = 2048 on the same Llama-8B shapes: once on weights forced to
-        INT8 everywhere (every 256-column tile takes the int8 kernel) and
-        once on the planned weights (no tile is all INT8: the path adds the
-        encoding of x and an empty int8 launch).  TFLOP/s of 2*M*N*K; the
-        int8 kernel's fraction is of the 5.0 POP/s dense int8 MFMA peak (it
-        issues two int8 MFMAs per product, one per plane of x)."""
+        """The int8 matrix-core path (HT_PATH_GEMM_I8) and the opt-in W8A8
+        mode (HT_PATH_W8A8: x as one int8 plane per 64-wide K-block) against
+        the MFMA path at M = 2048 on the same Llama-8B shapes: once on
+        weights forced to INT8 everywhere (every 256-column tile takes the
+        int8 kernel) and once on the planned weights (no tile is all INT8:
+        the paths add the encoding of x and an empty int8 launch).  TFLOP/s
+        of 2*M*N*K; the int8 kernel's fraction is of the 5.0 POP/s dense
+        int8 MFMA peak (GEMM_I8 issues two int8 MFMAs per product, one per
+        plane of x; W8A8 one)."""
         out = {}
         M = 2048
         for name in ("q", "gate", "down"):
@@ -204,7 +206,8 @@ def main() -> int:
                        else api.plan(W))
                 pw = api.pack(W, fmt)
                 r = {}
-                for pname, path in (("GEMM", B.HT_PATH_GEMM), ("GEMM_I8", B.HT_PATH_GEMM_I8)):
+                paths = (("GEMM", B.HT_PATH_GEMM), ("GEMM_I8", B.HT_PATH_GEMM_I8), ("W8A8", B.HT_PATH_W8A8))
+                for pname, path in paths:
                     ws = api.workspace(B.ht_linear_workspace(pw.desc, M, path), dev)
                     for _ in range(2):
                         api.linear(pw, xg, out=yg, ws=ws, path=path)
@@ -213,13 +216,15 @@ def main() -> int:
                     r[pname + "_TFLOPs"] = round(fl / t / 1e12, 1)
                     del ws
                 r["speedup"] = round(r["GEMM_us"] / r["GEMM_I8_us"], 3)
+                r["W8A8_speedup"] = round(r["GEMM_us"] / r["W8A8_us"], 3)
                 row[kind] = r
                 del pw
             row["all_int8"]["int8_peak_frac"] = round(fl / (row["all_int8"]["GEMM_I8_us"] * 1e-6) / 5.0e15, 4)
+            row["all_int8"]["W8A8_int8_peak_frac"] = round(fl / (row["all_int8"]["W8A8_us"] * 1e-6) / 5.0e15, 4)
             out[name] = row
             del W, xg, yg
             torch.cuda.empty_cache()
-        return {"kernel": "gemm_i8_kernel + xq_kernel", "peak_int8_TOPs": 5000.0, "M": M, "shapes": out}
+        return {"kernel": "gemm_i8_kernel<false> + xq_kernel (GEMM_I8), gemm_i8_kernel<true> + xq8_kernel (W8A8)", "peak_int8_TOPs": 5000.0, "M": M, "shapes": out}
 
     def configs_leg():
         """The transformer-shaped configurations, on seeded device-drawn

@@ -21,7 +21,7 @@ PHASES_LIB_PATH = os.path.join(HERE, "libht_phases.so")
 
 HT_INT4, HT_INT8, HT_BF16, HT_FP16, HT_FP32 = range(5)
 HT_ACT_NONE, HT_ACT_RELU = 0, 1
-HT_PATH_AUTO, HT_PATH_GEMV, HT_PATH_FUSED, HT_PATH_GEMM, HT_PATH_GEMV_MFMA, HT_PATH_GEMM_I8 = 0, 1, 2, 3, 4, 5
+HT_PATH_AUTO, HT_PATH_GEMV, HT_PATH_FUSED, HT_PATH_GEMM, HT_PATH_GEMV_MFMA, HT_PATH_GEMM_I8, HT_PATH_W8A8 = 0, 1, 2, 3, 4, 5, 6
 HT_LAYOUT_VERSION = 1
 STATUS = {0: "HT_OK", 1: "HT_EINVAL", 2: "HT_ESHAPE", 3: "HT_EALIGN", 4: "HT_ESMALL", 5: "HT_EHIP"}
 

@@ -127,10 +127,66 @@ __global__ __launch_bounds__(256) void xq_kernel(XqArgs a) {
     }
 }
 
+// W8A8 encoding of x (HT_PATH_W8A8): per token m and 64-wide K-block kb, one
+// int8 code per entry and one power-of-two scale:
+//   amax = max over the block of |x| = f * 2^E, f in [0.5, 1);
+//   q = clamp(round_half_even(x * 2^(7-E)), -127, 127);
+//   scale 2^(E-7) (1 for an all-zero block, NaN for a block holding an Inf
+//   or NaN, whose codes are 0).
+// One workgroup per row of x; wavefront v encodes K-blocks v, v + 4, ...,
+// lane l entry l.  Codes go to the same operand order as the two-plane
+// encoding ([16-row group][kb][lane = row + 16 * (entry / 16)][16 bytes]),
+// one plane; the scales to [kb][16 * groups] (contiguous per K-block, as
+// the matrix-core kernel copies them).
+struct Xq8Args {
+    const uint16_t *x;
+    int64_t ldx;
+    uint32_t M, KB, Mp;   // Mp = 16 * groups
+    uint8_t *q;           // codes [G][KB][64][16]
+    float *sx;            // block scales [KB][Mp]
+};
+
+__global__ __launch_bounds__(256) void xq8_kernel(Xq8Args a) {
+    uint32_t m = blockIdx.x;
+    if ((gridDim.x & 7u) == 0) m = (blockIdx.x & 7u) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    const uint32_t t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const uint16_t *row = a.x + int64_t(m) * a.ldx;
+    const uint32_t g = m >> 4, r = m & 15;
+    for (uint32_t kb = wv; kb < a.KB; kb += 4u) {
+        const float f = __uint_as_float(uint32_t(row[64u * kb + lane]) << 16);
+        const float af = fabsf(f);
+        const bool bad = !(af <= 3.4028235e38f);   // Inf or NaN
+        float amax = bad ? 0.0f : af;
+        amax = fmaxf(amax, dpp_f32<kDppXor1>(amax));
+        amax = fmaxf(amax, dpp_f32<kDppXor2>(amax));
+        amax = fmaxf(amax, dpp_f32<kDppHalfMirror>(amax));
+        amax = fmaxf(amax, dpp_f32<kDppMirror>(amax));
+        amax = fmaxf(amax, __shfl_xor(amax, 16));
+        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        const bool anybad = __any(bad);
+        int E = 0;
+        if (amax > 0.0f) (void)frexpf(amax, &E);
+        const int sh = amax > 0.0f ? 7 - E : 0;
+        float v = anybad ? 0.0f : rintf(ldexpf(f, sh));
+        v = fminf(127.0f, fmaxf(-127.0f, v));
+        const uint32_t code = uint32_t(int32_t(v)) & 0xFFu;
+        const uint32_t word = code | (uint32_t(__shfl_down(int(code), 1)) << 8) |
+                              (uint32_t(__shfl_down(int(code), 2)) << 16) | (uint32_t(__shfl_down(int(code), 3)) << 24);
+        if ((lane & 3u) == 0u) {
+            uint8_t *dst = a.q + (uint64_t(g) * a.KB + kb) * 1024u + 16u * (r + 16u * (lane >> 4)) + 4u * ((lane & 15u) >> 2);
+            *reinterpret_cast<uint32_t *>(dst) = word;
+        }
+        if (lane == 0)
+            a.sx[uint64_t(kb) * a.Mp + m] = anybad ? __builtin_nanf("") : amax > 0.0f ? ldexpf(1.0f, E - 7) : 1.0f;
+    }
+}
+
 struct I8Args {
     LayerDev w;
     const uint8_t *q;         // x planes
-    const float *rs;          // x row scales
+    const float *rs;          // x row scales (two-plane encoding), or
+    const float *sx;          // x block scales [KB][Mp] (W8A8 encoding)
+    uint32_t Mp;
     float *y;                 // fp32 output, or
     uint16_t *ybf;            // bfloat16 output (round to nearest even), or
     float *partial;           // per-split partial sums [S][M][N] (no activation)
@@ -175,6 +231,11 @@ constexpr uint32_t kI8A = (kI8BM / 16) * 2048;               // x planes of one 
 constexpr uint32_t kI8B = (kI8TileRows / 16) * 1024;         // weight codes of one step
 constexpr uint32_t kI8Stage = kI8A + kI8B + kI8TileRows * 4; // + column scales
 
+// W8 (HT_PATH_W8A8): x is one plane of codes (row group w's at w * 1024 of the
+// stage) with a scale per row and K-block (the step's 128 row scales at
+// kI8A / 2, copied by wavefronts 4 and 5); per 16 x 16 tile and K-block one
+// int8 MFMA, then acc += s * (float(C) * x_scale[row]).
+template <bool W8>
 __global__ __launch_bounds__(kI8Threads) void gemm_i8_kernel(I8Args a) {
     __shared__ __align__(16) uint8_t lds[kI8Stages * kI8Stage];
     constexpr uint32_t NS = kI8Stages;
@@ -220,9 +281,16 @@ __global__ __launch_bounds__(kI8Threads) void gemm_i8_kernel(I8Args a) {
     auto issue = [&](uint32_t step, uint32_t st) {
         const uint32_t kb = kb0 + step;
         uint8_t *S = lds + st * kI8Stage;
-        const uint8_t *qa = a.q + ((uint64_t(ga) * KB + kb) * 2u) * 1024u + 16u * lane;
-        lds_copy16(qa, S + wave * 2048u);
-        lds_copy16(qa + 1024, S + wave * 2048u + 1024u);
+        if constexpr (W8) {
+            lds_copy16(a.q + (uint64_t(ga) * KB + kb) * 1024u + 16u * lane, S + wave * 1024u);
+            if (wave == 4 || wave == 5)
+                lds_copy4(a.sx + uint64_t(kb) * a.Mp + min(m0 + 64u * (wave - 4u) + lane, a.Mp - 1u),
+                          S + kI8A / 2 + (wave - 4u) * 256u);
+        } else {
+            const uint8_t *qa = a.q + ((uint64_t(ga) * KB + kb) * 2u) * 1024u + 16u * lane;
+            lds_copy16(qa, S + wave * 2048u);
+            lds_copy16(qa + 1024, S + wave * 2048u + 1024u);
+        }
         const uint32_t r = lane & 15u, hq = 16u * (lane >> 4);
         lds_copy16(pay8 + uint64_t(bb0 + step * nb0 + min(r, nb0 - 1u)) * 64u + hq, S + kI8A + (2u * wave) * 1024u);
         lds_copy16(pay8 + uint64_t(bb1 + step * nb1 + min(r, nb1 - 1u)) * 64u + hq,
@@ -230,14 +298,32 @@ __global__ __launch_bounds__(kI8Threads) void gemm_i8_kernel(I8Args a) {
         if (wave < 4)
             lds_copy4(sc8 + 4u * uint64_t(bs + step * ns + min(r, ns - 1u)), S + kI8A + kI8B + wave * 256u);
     };
-    // copies each wavefront issues per step: 4, plus the scales for 0-3
-    auto wait_copies = [&](bool keep) {
-        if (keep) {
-            if (wave < 4) __builtin_amdgcn_s_waitcnt(vm_wait(int(NS - 2) * 5));
-            else __builtin_amdgcn_s_waitcnt(vm_wait(int(NS - 2) * 4));
+    // copies each wavefront issues per step: two planes (W8: one) and two
+    // weight row tiles, plus the weight scales for 0-3 (W8: and the x
+    // scales for 4-5); wait until those of all but the last `steps` steps
+    // issued have landed
+    auto wait_steps = [&](int steps) __attribute__((always_inline)) {
+        if constexpr (W8) {
+            if (wave < 6) {
+                if (steps == int(NS - 1)) __builtin_amdgcn_s_waitcnt(vm_wait(int(NS - 1) * 4));
+                else __builtin_amdgcn_s_waitcnt(vm_wait(int(NS - 2) * 4));
+            } else {
+                if (steps == int(NS - 1)) __builtin_amdgcn_s_waitcnt(vm_wait(int(NS - 1) * 3));
+                else __builtin_amdgcn_s_waitcnt(vm_wait(int(NS - 2) * 3));
+            }
         } else {
-            __builtin_amdgcn_s_waitcnt(vm_wait(0));
+            if (wave < 4) {
+                if (steps == int(NS - 1)) __builtin_amdgcn_s_waitcnt(vm_wait(int(NS - 1) * 5));
+                else __builtin_amdgcn_s_waitcnt(vm_wait(int(NS - 2) * 5));
+            } else {
+                if (steps == int(NS - 1)) __builtin_amdgcn_s_waitcnt(vm_wait(int(NS - 1) * 4));
+                else __builtin_amdgcn_s_waitcnt(vm_wait(int(NS - 2) * 4));
+            }
         }
+    };
+    auto wait_copies = [&](bool keep) {
+        if (keep) wait_steps(int(NS - 2));
+        else __builtin_amdgcn_s_waitcnt(vm_wait(0));
     };
     // workgroup barrier that leaves outstanding copies in flight
     auto cbar = [&]() {
@@ -253,6 +339,43 @@ __global__ __launch_bounds__(kI8Threads) void gemm_i8_kernel(I8Args a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    auto compute8 = [&](uint32_t st) {
+        const uint8_t *S = lds + st * kI8Stage;
+        i32x4 B[4], A[4];
+        float sw[4];
+        f32x4 xs[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            B[j] = *reinterpret_cast<const i32x4 *>(S + kI8A + (4u * wc + j) * 1024u + 16u * lane);
+            sw[j] = *reinterpret_cast<const float *>(S + kI8A + kI8B + 4u * (64u * wc + 16u * j + (lane & 15u)));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            A[i] = *reinterpret_cast<const i32x4 *>(S + (4u * wr + i) * 1024u + 16u * lane);
+            xs[i] = *reinterpret_cast<const f32x4 *>(S + kI8A / 2 + 4u * (64u * wr + 16u * i + 4u * (lane >> 4)));
+        }
+        const i32x4 z = {0, 0, 0, 0};
+        i32x4 c[2];
+        c[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[0], B[0], z, 0, 0, 0);
+#pragma unroll
+        for (int k = 1; k <= 16; ++k) {
+            if (k < 16) c[k & 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[k >> 2], B[k & 3], z, 0, 0, 0);
+            const int p = k - 1, b = p & 1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                acc[p >> 2][p & 3][e] =
+                    __builtin_fmaf(sw[p & 3], float(c[b][e]) * xs[p >> 2][e], acc[p >> 2][p & 3][e]);
+        }
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);   // one tile's fp32 update
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(acc[i][j]));
+    };
     auto compute = [&](uint32_t st) {
         const uint8_t *S = lds + st * kI8Stage;
         i32x4 B[4], A[4][2];
@@ -303,15 +426,15 @@ __global__ __launch_bounds__(kI8Threads) void gemm_i8_kernel(I8Args a) {
     for (uint32_t t = 0; t < NS; ++t)
         if (t < nsteps) issue(t, t);
     if (nsteps >= NS) {
-        if (wave < 4) __builtin_amdgcn_s_waitcnt(vm_wait(int(NS - 1) * 5));
-        else __builtin_amdgcn_s_waitcnt(vm_wait(int(NS - 1) * 4));
+        wait_steps(int(NS - 1));
     } else {
         __builtin_amdgcn_s_waitcnt(vm_wait(0));
     }
     cbar();
     uint32_t st = 0;
     for (uint32_t t = 0; t < nsteps; ++t) {
-        compute(st);
+        if constexpr (W8) compute8(st);
+        else compute(st);
         if (t + 1 < nsteps) wait_copies(t + NS <= nsteps);
         cbar();
         if (t + NS < nsteps) issue(t + NS, st);
@@ -325,7 +448,7 @@ __global__ __launch_bounds__(kI8Threads) void gemm_i8_kernel(I8Args a) {
         for (int e = 0; e < 4; ++e) {
             const uint32_t m = m0 + 64u * wr + 16u * i + 4u * (lane >> 4) + uint32_t(e);
             if (m >= a.M) continue;
-            const float rsc = a.rs[m];
+            const float rsc = W8 ? 1.0f : a.rs[m];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const uint32_t n = n0 + 64u * wc + 16u * j + (lane & 15u);
@@ -351,12 +474,14 @@ struct I8Layout {
     size_t planes, scales, partial, total;   // byte offsets of the regions and total size
 };
 
-I8Layout i8_layout(const ht_packed_weight *w, int64_t Mt, uint32_t S, bool planes) {
+// planes: whether x is encoded at all; w8: the W8A8 encoding (one plane of
+// codes and a scale per row and K-block) instead of the two-plane one
+I8Layout i8_layout(const ht_packed_weight *w, int64_t Mt, uint32_t S, bool planes, bool w8) {
     const uint64_t G = uint64_t((Mt + 15) / 16), KB = uint64_t(w->K / kBlockK);
     I8Layout L;
     L.planes = 0;
-    L.scales = planes ? align256(G * KB * 2048u) : 0;
-    L.partial = L.scales + (planes ? align256(G * 16u * sizeof(float)) : 0);
+    L.scales = planes ? align256(G * KB * (w8 ? 1024u : 2048u)) : 0;
+    L.partial = L.scales + (planes ? align256((w8 ? KB : 1u) * G * 16u * sizeof(float)) : 0);
     L.total = L.partial + (S > 1 ? size_t(S) * size_t(Mt) * size_t(w->N) * sizeof(float) : 0);
     return L;
 }
@@ -403,39 +528,57 @@ I8Plan i8_plan(const ht_packed_weight *w, int64_t Mt) {
 
 bool i8_ok(const ht_packed_weight *w) { return w->row_tile == 16; }
 
-size_t i8_ws(const ht_packed_weight *w, int64_t M) {
+size_t i8_ws(const ht_packed_weight *w, int64_t M, bool w8) {
     const int64_t Mt = M < kI8ChunkRows ? M : kI8ChunkRows;
     const I8Plan P = i8_plan(w, Mt);
-    return i8_layout(w, Mt, P.S, P.mode != kNone).total;
+    return i8_layout(w, Mt, P.S, P.mode != kNone, w8).total;
 }
 
 ht_status run_gemm_i8(const ht_packed_weight *w, const uint16_t *x, int64_t M, int64_t ldx, float *y, uint16_t *ybf,
-                      int64_t ldy, int act, void *ws, hipStream_t s) {
+                      int64_t ldy, int act, void *ws, hipStream_t s, bool w8) {
     uint8_t *wsb = static_cast<uint8_t *>(ws);
     for (int64_t m0 = 0; m0 < M; m0 += kI8ChunkRows) {
         const int64_t Mt = M - m0 < kI8ChunkRows ? M - m0 : kI8ChunkRows;
         const I8Plan P = i8_plan(w, Mt);
         const uint32_t S = P.S;
-        const I8Layout Lw = i8_layout(w, Mt, S, P.mode != kNone);
+        const I8Layout Lw = i8_layout(w, Mt, S, P.mode != kNone, w8);
         float *yc = y ? y + m0 * ldy : nullptr;
         uint16_t *ybc = ybf ? ybf + m0 * ldy : nullptr;
         float *part = reinterpret_cast<float *>(wsb + Lw.partial);
         if (P.mode != kNone) {
             const uint32_t G = uint32_t((Mt + 15) / 16);
-            XqArgs q;
-            q.x = x + m0 * ldx;
-            q.ldx = ldx;
-            q.M = uint32_t(Mt);
-            q.KB = uint32_t(w->K / kBlockK);
-            q.q = wsb + Lw.planes;
-            q.rs = reinterpret_cast<float *>(wsb + Lw.scales);
-            hipLaunchKernelGGL(xq_kernel, dim3(uint32_t(Mt)), dim3(256), 0, s, q);
-            HT_LAUNCH_CHECK();
-
             I8Args a;
+            if (w8) {
+                Xq8Args q;
+                q.x = x + m0 * ldx;
+                q.ldx = ldx;
+                q.M = uint32_t(Mt);
+                q.KB = uint32_t(w->K / kBlockK);
+                q.Mp = 16u * G;
+                q.q = wsb + Lw.planes;
+                q.sx = reinterpret_cast<float *>(wsb + Lw.scales);
+                hipLaunchKernelGGL(xq8_kernel, dim3(uint32_t(Mt)), dim3(256), 0, s, q);
+                HT_LAUNCH_CHECK();
+                a.q = q.q;
+                a.rs = nullptr;
+                a.sx = q.sx;
+                a.Mp = q.Mp;
+            } else {
+                XqArgs q;
+                q.x = x + m0 * ldx;
+                q.ldx = ldx;
+                q.M = uint32_t(Mt);
+                q.KB = uint32_t(w->K / kBlockK);
+                q.q = wsb + Lw.planes;
+                q.rs = reinterpret_cast<float *>(wsb + Lw.scales);
+                hipLaunchKernelGGL(xq_kernel, dim3(uint32_t(Mt)), dim3(256), 0, s, q);
+                HT_LAUNCH_CHECK();
+                a.q = q.q;
+                a.rs = q.rs;
+                a.sx = nullptr;
+                a.Mp = 0;
+            }
             a.w = layer_dev(w);
-            a.q = q.q;
-            a.rs = q.rs;
             a.y = S > 1 ? nullptr : yc;
             a.ybf = S > 1 ? nullptr : ybc;
             a.partial = S > 1 ? part : nullptr;
@@ -446,7 +589,8 @@ ht_status run_gemm_i8(const ht_packed_weight *w, const uint16_t *x, int64_t M, i
             a.MT = uint32_t((Mt + kI8BM - 1) / kI8BM);
             a.NT = uint32_t((a.w.N + kI8TileRows - 1) / kI8TileRows);
             a.act = act;
-            hipLaunchKernelGGL(gemm_i8_kernel, dim3(a.MT * a.NT * S), dim3(kI8Threads), 0, s, a);
+            if (w8) hipLaunchKernelGGL(gemm_i8_kernel<true>, dim3(a.MT * a.NT * S), dim3(kI8Threads), 0, s, a);
+            else hipLaunchKernelGGL(gemm_i8_kernel<false>, dim3(a.MT * a.NT * S), dim3(kI8Threads), 0, s, a);
             HT_LAUNCH_CHECK();
         }
         if (P.mode != kAll8) {

@@ -269,13 +269,14 @@ static bool al16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) 
 
 static bool path_ok(int32_t path) {
     return path == HT_PATH_AUTO || path == HT_PATH_GEMV || path == HT_PATH_GEMM || path == HT_PATH_GEMV_MFMA ||
-           path == HT_PATH_GEMM_I8;
+           path == HT_PATH_GEMM_I8 || path == HT_PATH_W8A8;
 }
 
 static size_t path_ws(const ht_packed_weight *w, int64_t M, int32_t path) {
     return path == HT_PATH_GEMM        ? gemm_ws(w, M)
            : path == HT_PATH_GEMV_MFMA ? dec_ws(w, M)
            : path == HT_PATH_GEMM_I8   ? i8_ws(w, M)
+           : path == HT_PATH_W8A8      ? i8_ws(w, M, true)
                                        : linear_ws(w, M);
 }
 
@@ -285,7 +286,7 @@ extern "C" ht_status ht_linear_workspace(const ht_packed_weight *w, int64_t M, i
     if (!path_ok(path)) return HT_EINVAL;
     if (path == HT_PATH_AUTO) path = auto_linear_path(w, M);
     if (path == HT_PATH_GEMV_MFMA && !dec_ok(w)) return HT_EINVAL;
-    if (path == HT_PATH_GEMM_I8 && !i8_ok(w)) return HT_EINVAL;
+    if ((path == HT_PATH_GEMM_I8 || path == HT_PATH_W8A8) && !i8_ok(w)) return HT_EINVAL;
     *bytes = path_ws(w, M, path);
     return HT_OK;
 }
@@ -300,7 +301,7 @@ extern "C" ht_status ht_linear_forward(const ht_packed_weight *w, const uint16_t
     if (!al16(x) || !al16(y) || (ldx % 8) || !al16(w->base)) return HT_EALIGN;
     if (path == HT_PATH_AUTO) path = auto_linear_path(w, M);
     if (path == HT_PATH_GEMV_MFMA && !dec_ok(w)) return HT_EINVAL;
-    if (path == HT_PATH_GEMM_I8 && !i8_ok(w)) return HT_EINVAL;
+    if ((path == HT_PATH_GEMM_I8 || path == HT_PATH_W8A8) && !i8_ok(w)) return HT_EINVAL;
     const size_t need = path_ws(w, M, path);
     if (need && (!ws || ws_bytes < need)) return HT_ESMALL;
     if (ws && !al16(ws)) return HT_EALIGN;
@@ -308,6 +309,7 @@ extern "C" ht_status ht_linear_forward(const ht_packed_weight *w, const uint16_t
     if (path == HT_PATH_GEMM) return run_gemm(w, x, M, ldx, y, nullptr, ldy, act, ws, s);
     if (path == HT_PATH_GEMV_MFMA) return run_dec(w, x, M, ldx, y, nullptr, ldy, act, ws, s);
     if (path == HT_PATH_GEMM_I8) return run_gemm_i8(w, x, M, ldx, y, nullptr, ldy, act, ws, s);
+    if (path == HT_PATH_W8A8) return run_gemm_i8(w, x, M, ldx, y, nullptr, ldy, act, ws, s, true);
     return run_linear(w, x, M, ldx, y, nullptr, ldy, act, ws, s);
 }
 

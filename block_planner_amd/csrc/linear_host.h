@@ -39,10 +39,12 @@ ht_status gemm_tiles(const ht_packed_weight *w, const uint16_t *x, int64_t Mt, i
 // its workspace bytes for M rows (x's int8 planes and row scales, K-split
 // partials), and one linear on it (fp32 y or bfloat16 ybf; arguments assumed
 // checked).
+// With w8 the same path in its W8A8 form (x encoded as one int8 plane with
+// a power-of-two scale per row and K-block).
 bool i8_ok(const ht_packed_weight *w);
-size_t i8_ws(const ht_packed_weight *w, int64_t M);
+size_t i8_ws(const ht_packed_weight *w, int64_t M, bool w8 = false);
 ht_status run_gemm_i8(const ht_packed_weight *w, const uint16_t *x, int64_t M, int64_t ldx, float *y, uint16_t *ybf,
-                      int64_t ldy, int act, void *ws, hipStream_t s);
+                      int64_t ldy, int act, void *ws, hipStream_t s, bool w8 = false);
 
 // y[m, n] = act(sum over s in order of partial[s][m][n]), fp32 y or bfloat16 ybf.
 ht_status launch_split_reduce(const float *partial, uint32_t S, uint32_t M, uint32_t N, float *y, uint16_t *ybf,

@@ -118,7 +118,8 @@ enum {
     HT_PATH_FUSED = 2,  /* ht_mlp_forward only: all layers in one persistent launch */
     HT_PATH_GEMM = 3,   /* ht_linear_forward only: LDS dequantisation + bf16 MFMA   */
     HT_PATH_GEMV_MFMA = 4, /* ht_linear_forward only: register dequantisation + bf16 MFMA (row tile 16) */
-    HT_PATH_GEMM_I8 = 5    /* ht_linear_forward only: int8 MFMA for all-INT8 tiles, else as GEMM (row tile 16) */
+    HT_PATH_GEMM_I8 = 5,   /* ht_linear_forward only: int8 MFMA for all-INT8 tiles, else as GEMM (row tile 16) */
+    HT_PATH_W8A8 = 6       /* ht_linear_forward only: as GEMM_I8 with x as int8 per 64-wide K-block (opt-in W8A8) */
 };
 
 /* Human-readable name of a status code (static storage; never NULL). */
@@ -231,9 +232,9 @@ ht_status ht_refresh_desc(int64_t N, int64_t K, int64_t row_tile, const int64_t 
 ht_status ht_check_packed(const ht_packed_weight *w, const void *buf, size_t buf_bytes, uint8_t *fmt);
 
 /* ht_linear_workspace -- workspace bytes ht_linear_forward needs for M rows
- * on `path` (HT_PATH_AUTO, HT_PATH_GEMV, HT_PATH_GEMM, HT_PATH_GEMV_MFMA or
- * HT_PATH_GEMM_I8; HT_EINVAL for HT_PATH_GEMV_MFMA and HT_PATH_GEMM_I8 with a
- * row tile other than 16). */
+ * on `path` (HT_PATH_AUTO, HT_PATH_GEMV, HT_PATH_GEMM, HT_PATH_GEMV_MFMA,
+ * HT_PATH_GEMM_I8 or HT_PATH_W8A8; HT_EINVAL for HT_PATH_GEMV_MFMA,
+ * HT_PATH_GEMM_I8 and HT_PATH_W8A8 with a row tile other than 16). */
 ht_status ht_linear_workspace(const ht_packed_weight *w, int64_t M, int32_t path,
                               size_t *bytes);
 
@@ -279,6 +280,18 @@ ht_status ht_linear_workspace(const ht_packed_weight *w, int64_t M, int32_t path
  *          HT_PATH_GEMM would not.  The workspace holds the encoded x
  *          (unless the weight has too few INT8 blocks for any tile, when
  *          the call is HT_PATH_GEMM's); HT_PATH_AUTO never picks this path;
+ *          HT_PATH_W8A8: an opt-in mode with int8 activations (W8A8; row
+ *          tile 16 only, else HT_EINVAL), the same tiles as HT_PATH_GEMM_I8
+ *          but x encoded per token m and 64-wide K-block kb as one int8
+ *          code per entry and a power-of-two scale: 2^(E-1) <= max over
+ *          the block of |x| < 2^E, q = clamp(rne(x 2^(7-E)), -127, 127),
+ *          x_hat = q 2^(E-7), so |x_hat - x| <= 2^-7 of the block maximum
+ *          (an all-zero block has x_hat = 0; a block holding Inf or NaN
+ *          gives NaN).  Its tiles compute x_hat . W_hat^T with exact int32
+ *          block sums, one int8 MFMA per block and the two scales applied
+ *          in fp32 per block: a different output function, not within the
+ *          bf16 tolerance of the exact linear; other tiles as HT_PATH_GEMM.
+ *          HT_PATH_AUTO never picks it;
  *          HT_PATH_AUTO: GEMV_MFMA for 4 <= M <= 32 with row tile 16;
  *          otherwise GEMM when M >= 16, else GEMV.
  *   ws     workspace of ws_bytes >= ht_linear_workspace(w, M, path): K-split

@@ -179,12 +179,19 @@ def test_linear_argument_checks():
             KBs = -(-KB // S)
             S = -(-KB // KBs)
         assert B.ht_linear_workspace(dsc, M, B.HT_PATH_GEMM_I8) == extra + (S * Mt * dsc.N * 4 if S > 1 else 0)
+        # the W8A8 mode: the same tiles and splits, x as one int8 plane (1 byte
+        # per entry) and an fp32 scale per row and K-block ([kb][16 * groups])
+        extra8 = a256(G * KB * 1024) + a256(KB * G * 16 * 4)
+        assert B.ht_linear_workspace(dsc, M, B.HT_PATH_W8A8) == extra8 + (S * Mt * dsc.N * 4 if S > 1 else 0)
+        dsc = _with_counts(dsc, [0, dsc.N * KB - 1, 0, 0, 1])
+        assert B.ht_linear_workspace(dsc, M, B.HT_PATH_W8A8) == extra8 + B.ht_linear_workspace(dsc, Mt, B.HT_PATH_GEMM)
     for R in (1, 2, 4, 8):
-        with pytest.raises(B.HTError):
-            B.ht_linear_workspace(_desc(N=256, K=4096, R=R), 64, B.HT_PATH_GEMM_I8)
-        assert f(ctypes.byref(_desc(R=R)), x, 64, 256, y, 256, 0, B.HT_PATH_GEMM_I8, None, 0, None) == 1
+        for path in (B.HT_PATH_GEMM_I8, B.HT_PATH_W8A8):
+            with pytest.raises(B.HTError):
+                B.ht_linear_workspace(_desc(N=256, K=4096, R=R), 64, path)
+            assert f(ctypes.byref(_desc(R=R)), x, 64, 256, y, 256, 0, path, None, 0, None) == 1
     with pytest.raises(B.HTError):
-        B.ht_linear_workspace(big, 1, 6)                                        # no such path
+        B.ht_linear_workspace(big, 1, 7)                                        # no such path
     # AUTO on a row tile other than 16 keeps to the other two paths
     assert B.ht_linear_workspace(_desc(N=256, K=64 * 1024, R=8), 8, B.HT_PATH_AUTO) == \
         B.ht_linear_workspace(_desc(N=256, K=64 * 1024, R=8), 8, B.HT_PATH_GEMV)
