@@ -280,52 +280,56 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
     const bool tok = tile < w.T;
     const uint32_t kbx = uint32_t(w.off_kbidx) + 4u * (tok ? tile * KB : 0u);
     // kbidx[f][tile*KB + kb]: block index where step kb starts in format f
-    // (a column past N reads tile 0 and takes zeros)
+    // (a column past N reads tile 0's entries; load_block gives it no block)
     auto kload = [&](uint32_t kb, uint32_t (&v)[5]) {
         kb = min(kb, kb1);
 #pragma unroll
-        for (int f = 0; f < 5; ++f) {
-            const uint32_t x = *reinterpret_cast<const uint32_t *>(base + kbx + 4u * (uint32_t(f) * w.nk + kb));
-            v[f] = tok ? x : 0u;
-        }
+        for (int f = 0; f < 5; ++f)
+            v[f] = *reinterpret_cast<const uint32_t *>(base + kbx + 4u * (uint32_t(f) * w.nk + kb));
     };
 
     // Loads of this thread's half block in the step that starts at ka and
-    // ends at kn (a step past the split's end has no blocks): up to eight
-    // 16-byte loads at addresses chosen per format; a missing block reads the
+    // ends at kn (a step past the split's end has no blocks): eight 16-byte
+    // loads at addresses chosen per format; a missing block reads the
     // buffer's first bytes.
     auto load_block = [&](const uint32_t (&ka)[5], const uint32_t (&kn)[5]) -> BlockLoad {
         BlockLoad q;
-        q.f = 5;
-        uint32_t cum = 0, blk = 0;
+        // slot bi holds the (bi - c[f])-th block of format f, where c[] are
+        // the prefix sums of the step's block counts in format order and
+        // c[f] <= bi < c[f+1]; f is found by counting the boundaries c[1..5]
+        // not above bi (no branches: every lane takes the same path)
+        uint32_t c[6];
+        c[0] = 0;
 #pragma unroll
-        for (int f = 0; f < 5; ++f) {
-            const uint32_t cnt = kn[f] - ka[f];
-            if (q.f == 5 && bi < cum + cnt) {
-                q.f = f;
-                blk = ka[f] + (bi - cum);
-            }
-            cum += cnt;
+        for (int g = 0; g < 5; ++g) c[g + 1] = c[g] + (kn[g] - ka[g]);
+        uint32_t f = 0;
+#pragma unroll
+        for (int g = 1; g <= 5; ++g) f += bi >= c[g] ? 1u : 0u;
+        if (!tok) f = 5;
+        uint32_t kaf = ka[0], cf = 0, op = opay[0], oi = oids[0], sh = 5, osc = osc0;
+#pragma unroll
+        for (int g = 1; g < 5; ++g) {
+            const bool e = f == uint32_t(g);
+            kaf = e ? ka[g] : kaf;
+            cf = e ? c[g] : cf;
+            op = e ? opay[g] : op;
+            oi = e ? oids[g] : oi;
+            sh = e ? uint32_t(g == 1 ? 6 : g == 4 ? 8 : 7) : sh;   // log2 of the payload bytes
+            osc = e ? osc1 : osc;
         }
-        const bool has = q.f < 5;
-        const int f = has ? q.f : 0;
-        uint32_t po = 0, io = 0, so = 0, nl = 1;
+        const bool has = f < 5;
+        const uint32_t blk = kaf + bi - cf;
+        const uint32_t po = has ? op + (blk << sh) + (h << (sh - 1u)) : 0u;
+        const uint32_t io = has ? oi + ((2u * blk) & ~3u) : 0u;
+        const uint32_t so = has && f < 2 ? osc + 4u * blk : 0u;
+        const uint32_t nl = 1u << (sh - 5u);                     // 16-byte pieces in the half
+        q.f = int(f);
+        // eight 16-byte loads for every lane, with no branch, so that the
+        // compiler counts them exactly and waits only for the loads it uses;
+        // past the half's length a lane re-reads its last 16 bytes (in cache)
 #pragma unroll
-        for (int g = 0; g < 5; ++g) {
-            if (f == g) {
-                po = opay[g] + blk * uint32_t(pay_bytes(g)) + h * uint32_t(pay_bytes(g) / 2);
-                io = oids[g] + ((2u * blk) & ~3u);
-                so = g == 0 ? osc0 + 4u * blk : g == 1 ? osc1 + 4u * blk : 0u;
-                nl = uint32_t(pay_bytes(g) / 32);
-            }
-        }
-        if (!has) po = io = so = 0;
-        // the first 16 bytes always; the rest only for lanes whose half is
-        // longer, so a wave without float blocks skips them
-        q.p[0] = *reinterpret_cast<const uint4 *>(base + po);
-#pragma unroll
-        for (uint32_t j = 1; j < 8; ++j)
-            q.p[j] = j < nl ? *reinterpret_cast<const uint4 *>(base + (po + 16u * j)) : make_uint4(0, 0, 0, 0);
+        for (uint32_t j = 0; j < 8; ++j)
+            q.p[j] = *reinterpret_cast<const uint4 *>(base + (po + 16u * min(j, nl - 1u)));
         q.id2 = *reinterpret_cast<const uint32_t *>(base + io);
         q.hi16 = blk & 1u;
         q.sc = *reinterpret_cast<const float *>(base + so);   // meaningful for INT4 / INT8 only
@@ -340,16 +344,15 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
     auto store_block = [&](const BlockLoad &b, WStage &st) {
         const uint32_t id = b.hi16 ? b.id2 >> 16 : b.id2;
         const uint32_t col = (gb / R) * R + (b.f < 5 ? (id & (R - 1u)) : bi);   // within the 128
-        const bool flt = b.f == 3 || b.f == 4;
-        const uint64_t bal = __ballot(flt);
-        const bool any_lo = ((bal >> (lane & 32u)) & 0xFFFFFFFFull) != 0;   // this column group needs the lo plane
+        st.scale[col] = b.f < 2 ? b.sc : 1.0f;   // both halves write the same value
+        const uint64_t bal = __ballot(b.f == 3 || b.f == 4);
+        if ((lane & 31u) == 0) st.need_lo[gb >> 4] = ((bal >> (lane & 32u)) & 0xFFFFFFFFull) != 0 ? 1u : 0u;
+        uint4 *hd = reinterpret_cast<uint4 *>(&st.whi[col][32 * h]);
+        uint4 *ld = reinterpret_cast<uint4 *>(&st.wlo[col][32 * h]);
         const uint32_t u[32] = {b.p[0].x, b.p[0].y, b.p[0].z, b.p[0].w, b.p[1].x, b.p[1].y, b.p[1].z, b.p[1].w,
                                 b.p[2].x, b.p[2].y, b.p[2].z, b.p[2].w, b.p[3].x, b.p[3].y, b.p[3].z, b.p[3].w,
                                 b.p[4].x, b.p[4].y, b.p[4].z, b.p[4].w, b.p[5].x, b.p[5].y, b.p[5].z, b.p[5].w,
                                 b.p[6].x, b.p[6].y, b.p[6].z, b.p[6].w, b.p[7].x, b.p[7].y, b.p[7].z, b.p[7].w};
-        uint32_t hp[16], lp[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) lp[i] = 0u;
         auto nib = [](uint32_t v, uint32_t at) { return int32_t(v << (28u - at)) >> 28; };   // signed 4-bit field
         auto pair_hi = [](float f0, float f1) {                 // upper halves of two fp32 -> one word
             return __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
@@ -360,11 +363,20 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
             const bf16x2 v = {(__bf16)r0, (__bf16)r1};
             return __builtin_bit_cast(uint32_t, v);
         };
+        auto put = [](uint4 *d, const uint32_t (&v)[16]) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) d[i] = make_uint4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+        };
+        const uint4 z = make_uint4(0, 0, 0, 0);
+        // Each format writes both planes itself (the integer formats and a
+        // missing block write a zero lo plane), so that no value crosses the
+        // end of the switch.
         switch (b.f) {
-        case 0:
+        case 0: {
             // the half's 16 bytes: byte i of the first 8 holds entries 32h+i
             // (low nibble) and 32h+16+i (high), byte 8+i entries 32h+8+i and
             // 32h+24+i (the nibble order of the layout)
+            uint32_t hp[16];
 #pragma unroll
             for (int q2 = 0; q2 < 2; ++q2)
 #pragma unroll
@@ -374,19 +386,27 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
                     hp[4 * q2 + i] = pair_hi(float(nib(wd, sh)), float(nib(wd, sh + 8)));
                     hp[8 + 4 * q2 + i] = pair_hi(float(nib(wd, sh + 4)), float(nib(wd, sh + 12)));
                 }
+            put(hd, hp);
+            ld[0] = z; ld[1] = z; ld[2] = z; ld[3] = z;
             break;
-        case 1:
+        }
+        case 1: {
+            uint32_t hp[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const uint32_t wd = u[i >> 1], sh = 16 * (i & 1);
                 hp[i] = pair_hi(float(int8_t(wd >> sh)), float(int8_t(wd >> (sh + 8))));
             }
+            put(hd, hp);
+            ld[0] = z; ld[1] = z; ld[2] = z; ld[3] = z;
             break;
+        }
         case 2:
-#pragma unroll
-            for (int i = 0; i < 16; ++i) hp[i] = u[i];
+            hd[0] = b.p[0]; hd[1] = b.p[1]; hd[2] = b.p[2]; hd[3] = b.p[3];
+            ld[0] = z; ld[1] = z; ld[2] = z; ld[3] = z;
             break;
-        case 3:
+        case 3: {
+            uint32_t hp[16], lp[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const float f0 = float(__builtin_bit_cast(_Float16, uint16_t(u[i])));
@@ -394,63 +414,61 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs a) {
                 hp[i] = pair_hi(f0, f1);
                 lp[i] = pair_lo(f0, f1);
             }
+            put(hd, hp);
+            put(ld, lp);
             break;
-        case 4:
+        }
+        case 4: {
+            uint32_t hp[16], lp[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const float f0 = __uint_as_float(u[2 * i]), f1 = __uint_as_float(u[2 * i + 1]);
                 hp[i] = pair_hi(f0, f1);
                 lp[i] = pair_lo(f0, f1);
             }
+            put(hd, hp);
+            put(ld, lp);
             break;
+        }
         default:
-#pragma unroll
-            for (int i = 0; i < 16; ++i) hp[i] = 0u;
+            hd[0] = z; hd[1] = z; hd[2] = z; hd[3] = z;
+            ld[0] = z; ld[1] = z; ld[2] = z; ld[3] = z;
             break;
         }
-        const uint32_t k0 = 32 * h;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<uint4 *>(&st.whi[col][k0 + 8 * i]) = make_uint4(hp[4 * i], hp[4 * i + 1], hp[4 * i + 2], hp[4 * i + 3]);
-        if (any_lo) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                *reinterpret_cast<uint4 *>(&st.wlo[col][k0 + 8 * i]) = make_uint4(lp[4 * i], lp[4 * i + 1], lp[4 * i + 2], lp[4 * i + 3]);
-        }
-        if (h == 0) st.scale[col] = b.f < 2 ? b.sc : 1.0f;
-        if ((lane & 31u) == 0) st.need_lo[gb >> 4] = any_lo ? 1u : 0u;
     };
 
-    // kbidx entries run two steps ahead of the block loads, which run two
-    // steps ahead of the dequantisation
-    uint32_t K2[5], K3[5], K4[5];
+    // The kbidx entries of step k live in Ks[k % 4]: those of step t+5 are
+    // loaded in step t, two steps before their first use (by the loads of
+    // step t+4, issued in step t+2); the block loads of step t+2 are issued
+    // in step t and dequantised in step t+1.  The loop is unrolled four
+    // times, so that a register just loaded is never copied (a copy would
+    // wait for the load).
+    uint32_t Ks[4][5];
     BlockLoad QA, QB;
-    {
-        uint32_t K0[5], K1[5];
-        kload(kb0, K0);
-        kload(kb0 + 1, K1);
-        kload(kb0 + 2, K2);
-        kload(kb0 + 3, K3);
-        QB = load_block(K0, K1);
-        QA = load_block(K1, K2);
-        store_block(QB, wt0);
-    }
+    kload(kb0, Ks[0]);
+    kload(kb0 + 1, Ks[1]);
+    kload(kb0 + 2, Ks[2]);
+    kload(kb0 + 3, Ks[3]);
+    QB = load_block(Ks[0], Ks[1]);
+    QA = load_block(Ks[1], Ks[2]);
+    kload(kb0 + 4, Ks[0]);
+    store_block(QB, wt0);
     gemm_lds_barrier();
-    // qc: the loads of step t+1; qn receives those of step t+2
-    auto step = [&](uint32_t t, BlockLoad &qc, BlockLoad &qn, WStage &dst) {
-        kload(kb0 + t + 4, K4);
-        qn = load_block(K2, K3);
-#pragma unroll
-        for (int f = 0; f < 5; ++f) {
-            K2[f] = K3[f];
-            K3[f] = K4[f];
-        }
+    // step t (t % 4 == S): qc holds the loads of step t+1, qn receives those
+    // of step t+2; the entries of step t+5 replace those of step t+1 (last
+    // used in step t-1)
+    auto step = [&](uint32_t t, auto S, BlockLoad &qc, BlockLoad &qn, WStage &dst) {
+        constexpr int s = decltype(S)::value;
+        qn = load_block(Ks[(s + 2) & 3], Ks[(s + 3) & 3]);
+        kload(kb0 + t + 5, Ks[(s + 1) & 3]);
         if (t + 1 < nsteps) store_block(qc, dst);
         gemm_lds_barrier();
     };
-    for (uint32_t t = 0; t < nsteps; t += 2) {
-        step(t, QA, QB, wt1);
-        if (t + 1 < nsteps) step(t + 1, QB, QA, wt0);
+    for (uint32_t t = 0; t < nsteps; t += 4) {
+        step(t, std::integral_constant<int, 0>{}, QA, QB, wt1);
+        if (t + 1 < nsteps) step(t + 1, std::integral_constant<int, 1>{}, QB, QA, wt0);
+        if (t + 2 < nsteps) step(t + 2, std::integral_constant<int, 2>{}, QA, QB, wt1);
+        if (t + 3 < nsteps) step(t + 3, std::integral_constant<int, 3>{}, QB, QA, wt0);
     }
 }
 
