@@ -20,7 +20,7 @@ OUT_PHASES = os.path.join(HERE, "libht_phases.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.cpp", "plan.hip", "pack.hip", "linear.hip", "gemm.hip", "gemm_i8.hip", "gemv_mfma.hip", "mlp.hip", "backward.hip", "bwd_gemm.hip", "noalloc.hip", "refresh.hip"]
+SOURCES = ["api.cpp", "plan.hip", "pack.hip", "linear.hip", "gemm.hip", "gemm_xw.hip", "gemm_i8.hip", "gemv_mfma.hip", "mlp.hip", "backward.hip", "bwd_gemm.hip", "noalloc.hip", "refresh.hip"]
 
 # -packed-fp32-ops off: no v_pk_{add,mul,fma}_f32 are generated.
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -280,6 +280,10 @@ static size_t path_ws(const ht_packed_weight *w, int64_t M, int32_t path) {
                                        : linear_ws(w, M);
 }
 
+size_t ht::linear_path_ws_min(const ht_packed_weight *w, int64_t M, int32_t path) {
+    return path == HT_PATH_GEMM ? gemm_ws_min(w, M) : path_ws(w, M, path);
+}
+
 extern "C" ht_status ht_linear_workspace(const ht_packed_weight *w, int64_t M, int32_t path, size_t *bytes) {
     if (!bytes || !desc_ok(w)) return HT_EINVAL;
     if (M <= 0) return HT_ESHAPE;
@@ -302,11 +306,11 @@ extern "C" ht_status ht_linear_forward(const ht_packed_weight *w, const uint16_t
     if (path == HT_PATH_AUTO) path = auto_linear_path(w, M);
     if (path == HT_PATH_GEMV_MFMA && !dec_ok(w)) return HT_EINVAL;
     if ((path == HT_PATH_GEMM_I8 || path == HT_PATH_W8A8) && !i8_ok(w)) return HT_EINVAL;
-    const size_t need = path_ws(w, M, path);
+    const size_t need = linear_path_ws_min(w, M, path);
     if (need && (!ws || ws_bytes < need)) return HT_ESMALL;
     if (ws && !al16(ws)) return HT_EALIGN;
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (path == HT_PATH_GEMM) return run_gemm(w, x, M, ldx, y, nullptr, ldy, act, ws, s);
+    if (path == HT_PATH_GEMM) return run_gemm(w, x, M, ldx, y, nullptr, ldy, act, ws, ws ? ws_bytes : 0, s);
     if (path == HT_PATH_GEMV_MFMA) return run_dec(w, x, M, ldx, y, nullptr, ldy, act, ws, s);
     if (path == HT_PATH_GEMM_I8) return run_gemm_i8(w, x, M, ldx, y, nullptr, ldy, act, ws, s);
     if (path == HT_PATH_W8A8) return run_gemm_i8(w, x, M, ldx, y, nullptr, ldy, act, ws, s, true);

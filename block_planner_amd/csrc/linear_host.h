@@ -19,13 +19,33 @@ size_t linear_ws(const ht_packed_weight *w, int64_t M);
 ht_status run_linear(const ht_packed_weight *w, const uint16_t *x, int64_t M, int64_t ldx, float *y,
                      uint16_t *ybf, int64_t ldy, int act, void *ws, hipStream_t s);
 
-// Workspace bytes of one linear over M rows on the MFMA path (K-split partials).
+// Workspace bytes of one linear over M rows on the MFMA path: gemm_ws the
+// bytes it prefers (the two-pass kernel's records where it takes M rows),
+// gemm_ws_min the least it runs with (the single-pass kernel's K-split
+// partials).
 size_t gemm_ws(const ht_packed_weight *w, int64_t M);
+size_t gemm_ws_min(const ht_packed_weight *w, int64_t M);
 
 // Enqueue one linear on the MFMA path: fp32 y or bfloat16 ybf (one of them
-// non-null).  Arguments are assumed checked.
+// non-null); the two-pass kernel when it takes M rows and ws_bytes holds its
+// records, else the single-pass kernel.  Arguments are assumed checked
+// (ws_bytes >= gemm_ws_min).
 ht_status run_gemm(const ht_packed_weight *w, const uint16_t *x, int64_t M, int64_t ldx, float *y, uint16_t *ybf,
-                   int64_t ldy, int act, void *ws, hipStream_t s);
+                   int64_t ldy, int act, void *ws, size_t ws_bytes, hipStream_t s);
+
+// The least workspace ht_linear_forward runs with on `path` (a resolved
+// path, not HT_PATH_AUTO); ht_linear_workspace reports the preferred bytes.
+size_t linear_path_ws_min(const ht_packed_weight *w, int64_t M, int32_t path);
+
+// The two-pass prefill GEMM (weight tiles expanded once into bfloat16
+// planes, then a matrix-core kernel on them): whether the MFMA path takes it
+// for M rows (from kXwMinM rows, with enough tiles to fill the chip), its
+// workspace bytes (the expanded records), and one linear on it.
+constexpr int64_t kXwMinM = 1024;
+bool xw_takes(const ht_packed_weight *w, int64_t M);
+size_t xw_ws(const ht_packed_weight *w);
+ht_status run_gemm_xw(const ht_packed_weight *w, const uint16_t *x, int64_t M, int64_t ldx, float *y, uint16_t *ybf,
+                      int64_t ldy, int act, void *ws, hipStream_t s);
 
 // The MFMA path's K-splits for Mt rows (one launch), and its main kernel
 // alone over Mt rows: with S > 1 it writes partial[S][Mt][N] (for

@@ -575,7 +575,7 @@ extern "C" ht_status ht_mlp_forward(const ht_packed_weight *const *layers, int32
             yo = y;
         }
         const int32_t lp = path == HT_PATH_GEMV ? HT_PATH_GEMV : auto_linear_path(w, M);
-        st = lp == HT_PATH_GEMM        ? run_gemm(w, in, M, ld_in, yo, out, ldo, HT_ACT_RELU, part, s)
+        st = lp == HT_PATH_GEMM        ? run_gemm(w, in, M, ld_in, yo, out, ldo, HT_ACT_RELU, part, pl.part, s)
              : lp == HT_PATH_GEMV_MFMA ? run_dec(w, in, M, ld_in, yo, out, ldo, HT_ACT_RELU, part, s)
                                        : run_linear(w, in, M, ld_in, yo, out, ldo, HT_ACT_RELU, part, s);
         if (st != HT_OK) return st;

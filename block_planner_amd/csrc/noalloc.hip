@@ -47,11 +47,14 @@ ht_status scratch_for_current_device(void **out) {
 extern "C" ht_status ht_linear_forward_noalloc(const ht_packed_weight *w, const uint16_t *x, int64_t M,
                                                int64_t ldx, float *y, int64_t ldy, int32_t act, int32_t path,
                                                ht_stream stream) {
-    // descriptor, M and path checks, and the workspace this call needs
+    // descriptor, M and path checks, and the least workspace this call runs
+    // with (on HT_PATH_GEMM the two-pass kernel is used when its records fit
+    // the array, as ht_linear_forward does given a workspace of this size)
     size_t need = 0;
     ht_status st = ht_linear_workspace(w, M, path, &need);
     if (st != HT_OK) return st;
-    if (need > kScratchBytes) return HT_ESMALL;
+    if (path == HT_PATH_AUTO) path = ht::auto_linear_path(w, M);
+    if (ht::linear_path_ws_min(w, M, path) > kScratchBytes) return HT_ESMALL;
     void *ws = nullptr;
     st = scratch_for_current_device(&ws);
     if (st != HT_OK) return st;

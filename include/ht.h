@@ -231,10 +231,12 @@ ht_status ht_refresh_desc(int64_t N, int64_t K, int64_t row_tile, const int64_t 
  * non-finite values the kernels handle). */
 ht_status ht_check_packed(const ht_packed_weight *w, const void *buf, size_t buf_bytes, uint8_t *fmt);
 
-/* ht_linear_workspace -- workspace bytes ht_linear_forward needs for M rows
+/* ht_linear_workspace -- workspace bytes ht_linear_forward wants for M rows
  * on `path` (HT_PATH_AUTO, HT_PATH_GEMV, HT_PATH_GEMM, HT_PATH_GEMV_MFMA,
  * HT_PATH_GEMM_I8 or HT_PATH_W8A8; HT_EINVAL for HT_PATH_GEMV_MFMA,
- * HT_PATH_GEMM_I8 and HT_PATH_W8A8 with a row tile other than 16). */
+ * HT_PATH_GEMM_I8 and HT_PATH_W8A8 with a row tile other than 16).  On
+ * HT_PATH_GEMM from 1024 rows this is the two-pass kernel's expanded weight
+ * (see ht_linear_forward); less still runs, on the single-pass kernel. */
 ht_status ht_linear_workspace(const ht_packed_weight *w, int64_t M, int32_t path,
                               size_t *bytes);
 
@@ -255,7 +257,14 @@ ht_status ht_linear_workspace(const ht_packed_weight *w, int64_t M, int32_t path
  *          FP16 and to 16 significant bits for normal FP32 entries, to
  *          2^-133 absolute for fp32 subnormals; an Inf or NaN entry gives
  *          NaN in its output column) and multiplied with bf16 MFMA, fp32
- *          accumulation (for prefill, many rows);
+ *          accumulation (for prefill, many rows).  From 1024 rows, when the
+ *          256-row x 128-column output tiles number at least 192 and ws holds
+ *          ht_linear_workspace's bytes (33 KiB per 128-column x 64-K weight
+ *          tile), it runs in two passes: the weight tiles are first expanded
+ *          once into those bfloat16 planes in ws, which every row tile then
+ *          reads; the lo plane's products are added once at the end instead
+ *          of per K-block, so the result differs from the single-pass
+ *          kernel's (which runs with a smaller workspace) by fp32 rounding;
  *          HT_PATH_GEMV_MFMA: for decode at a few to a few tens of rows
  *          (row tile 16 only, else HT_EINVAL): each block is dequantised
  *          in registers straight into the operands of bf16 MFMAs (the same
@@ -295,7 +304,10 @@ ht_status ht_linear_workspace(const ht_packed_weight *w, int64_t M, int32_t path
  *          HT_PATH_AUTO: GEMV_MFMA for 4 <= M <= 32 with row tile 16;
  *          otherwise GEMM when M >= 16, else GEMV.
  *   ws     workspace of ws_bytes >= ht_linear_workspace(w, M, path): K-split
- *          partial sums, added in split order by a second kernel. */
+ *          partial sums, added in split order by a second kernel (and on
+ *          HT_PATH_GEMM from 1024 rows the expanded weight tiles; there a
+ *          workspace that holds only the partials, if any, runs the
+ *          single-pass kernel instead). */
 ht_status ht_linear_forward(const ht_packed_weight *w, const uint16_t *x, int64_t M,
                             int64_t ldx, float *y, int64_t ldy, int32_t act, int32_t path,
                             void *ws, size_t ws_bytes, ht_stream stream);
@@ -307,7 +319,10 @@ ht_status ht_linear_forward(const ht_packed_weight *w, const uint16_t *x, int64_
  * of HT_NOALLOC_SCRATCH_BYTES on each GPU it runs on, held until the process
  * ends; the call allocates and frees nothing.
  *   Arguments, paths and results as ht_linear_forward (the same kernels:
- *   the result is bitwise that of ht_linear_forward on the same path).
+ *   the result is bitwise that of ht_linear_forward on the same path with a
+ *   workspace of HT_NOALLOC_SCRATCH_BYTES; on HT_PATH_GEMM the two-pass
+ *   kernel runs when its expanded tiles fit the array, else the single-pass
+ *   one).
  *   The current device must be the device of x, y, the packed buffer and
  *   `stream`.
  * HT_ESMALL when the call needs more workspace than the array holds

@@ -156,21 +156,36 @@ def test_linear_argument_checks():
     wide = _desc(N=16384, K=4096, R=16)
     # the int8 matrix-core path, 8192 rows per launch (sized for 8192 at most),
     # decided by the weight's INT8 count: none (too few for any 256-row tile)
-    # -> exactly the MFMA path's workspace; mixed -> x's two int8 planes
+    # -> exactly the single-pass MFMA kernel's partials (the MFMA path's
+    # workspace below 1024 rows); mixed -> x's two int8 planes
     # (2 bytes per entry, rows in groups of 16) and 16 fp32 row scales per
     # group, each region 256-byte aligned, then the MFMA path's partials; all
     # INT8 -> planes, scales and partials for the int8 kernel's own K-splits
     # (128 x 256 tiles, split when fewer than 192, at least 8 K-blocks each)
     def a256(v):
         return (v + 255) // 256 * 256
+
+    def single_pass_ws(dsc, Mt):
+        """K-split partials of the single-pass MFMA kernel (256 x 128 tiles
+        from 256 rows), which the int8 path runs beside the int8 kernel."""
+        KB = dsc.K // 64
+        BM = 256 if Mt >= 256 else 128 if Mt >= 128 else 64
+        tiles = (dsc.N + 127) // 128 * ((Mt + BM - 1) // BM)
+        if tiles * 4 >= 3 * 256 or KB < 16:
+            return 0
+        S = min(-(-256 // tiles), KB // 8)
+        KBs = -(-KB // S)
+        return -(-KB // KBs) * Mt * dsc.N * 4
     for dsc, M in ((wide, 2048), (wide, 20000), (big, 1), (big, 33)):
         Mt = min(M, 8192)
         G, KB = (Mt + 15) // 16, dsc.K // 64
         extra = a256(G * KB * 2048) + a256(G * 16 * 4)
         dsc = _with_counts(dsc, [0, 0, 0, 0, dsc.N * KB])
-        assert B.ht_linear_workspace(dsc, M, B.HT_PATH_GEMM_I8) == B.ht_linear_workspace(dsc, Mt, B.HT_PATH_GEMM)
+        assert B.ht_linear_workspace(dsc, M, B.HT_PATH_GEMM_I8) == single_pass_ws(dsc, Mt)
+        if M < 1024:
+            assert single_pass_ws(dsc, Mt) == B.ht_linear_workspace(dsc, Mt, B.HT_PATH_GEMM)
         dsc = _with_counts(dsc, [0, dsc.N * KB - 1, 0, 0, 1])
-        assert B.ht_linear_workspace(dsc, M, B.HT_PATH_GEMM_I8) == extra + B.ht_linear_workspace(dsc, Mt, B.HT_PATH_GEMM)
+        assert B.ht_linear_workspace(dsc, M, B.HT_PATH_GEMM_I8) == extra + single_pass_ws(dsc, Mt)
         dsc = _with_counts(dsc, [0, dsc.N * KB, 0, 0, 0])
         tiles = (Mt + 127) // 128 * ((dsc.N + 255) // 256)
         S = 1
@@ -184,7 +199,7 @@ def test_linear_argument_checks():
         extra8 = a256(G * KB * 1024) + a256(KB * G * 16 * 4)
         assert B.ht_linear_workspace(dsc, M, B.HT_PATH_W8A8) == extra8 + (S * Mt * dsc.N * 4 if S > 1 else 0)
         dsc = _with_counts(dsc, [0, dsc.N * KB - 1, 0, 0, 1])
-        assert B.ht_linear_workspace(dsc, M, B.HT_PATH_W8A8) == extra8 + B.ht_linear_workspace(dsc, Mt, B.HT_PATH_GEMM)
+        assert B.ht_linear_workspace(dsc, M, B.HT_PATH_W8A8) == extra8 + single_pass_ws(dsc, Mt)
     for R in (1, 2, 4, 8):
         for path in (B.HT_PATH_GEMM_I8, B.HT_PATH_W8A8):
             with pytest.raises(B.HTError):
@@ -195,7 +210,14 @@ def test_linear_argument_checks():
     # AUTO on a row tile other than 16 keeps to the other two paths
     assert B.ht_linear_workspace(_desc(N=256, K=64 * 1024, R=8), 8, B.HT_PATH_AUTO) == \
         B.ht_linear_workspace(_desc(N=256, K=64 * 1024, R=8), 8, B.HT_PATH_GEMV)
-    assert B.ht_linear_workspace(wide, 2048, B.HT_PATH_GEMM) == 0                 # 4096 tiles: no split
+    # the MFMA path: no K-split with 128 output tiles at 1000 rows; from 1024
+    # rows (at least 192 tiles of 256 x 128) it prefers the two-pass kernel,
+    # whose workspace holds a 33 KiB record per 128-column x 64-K weight tile
+    assert B.ht_linear_workspace(wide, 1000, B.HT_PATH_GEMM) == 0
+    assert B.ht_linear_workspace(wide, 2048, B.HT_PATH_GEMM) == (16384 // 128) * (4096 // 64) * 33 * 1024
+    assert B.ht_linear_workspace(_desc(N=6144, K=4096, R=16), 1024, B.HT_PATH_GEMM) == 48 * 64 * 33 * 1024
+    # 188 tiles: the single-pass kernel, which splits K in two below 192
+    assert B.ht_linear_workspace(_desc(N=6016, K=4096, R=16), 1024, B.HT_PATH_GEMM) == 2 * 1024 * 6016 * 4
     with pytest.raises(B.HTError):
         B.ht_linear_workspace(big, 1, B.HT_PATH_FUSED)                        # MLP-only path
     assert f(ctypes.byref(d), x, 1, 256, y, 256, 0, B.HT_PATH_FUSED, None, 0, None) == 1
