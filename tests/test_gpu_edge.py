@@ -8,8 +8,9 @@ overflow tie, NaN and +-Inf) is laid out in classes of similar magnitude, so
 that the bar max|y_gpu - y_oracle| <= 1e-3 * max|y_oracle| of one call is
 not decided by a single huge row.  Each class runs under the natural plan
 and with every block forced to each format, through HT_PATH_GEMV,
-HT_PATH_GEMV_MFMA, HT_PATH_GEMM and HT_PATH_GEMM_I8, through the input
-gradient, and through the MLP (single launch and per layer).
+HT_PATH_GEMV_MFMA, HT_PATH_GEMM (single pass, and the two-pass form it
+takes from 1024 rows) and HT_PATH_GEMM_I8, through the input gradient, and
+through the MLP (single launch and per layer).
 
 Non-finite results.  Positions where the oracle's fp64 result is not finite
 must be exactly the GPU's non-finite positions, and NaN where the oracle has
@@ -185,6 +186,34 @@ def test_edge_linear(orc, cls, path, M):
             keep = i8_in_range(orc, W, fmt, x)
             y, y_or = np.where(keep, y, 0.0), np.where(keep, y_or, 0.0)
         fails += check_edge(y, y_or, path in MFMA_PATHS, what)
+    assert not fails, "\n".join(fails)
+
+
+@pytest.mark.parametrize("cls", list(CLASSES))
+def test_edge_linear_two_pass(orc, cls):
+    """The MFMA path's two-pass form (weight tiles expanded once, taken from
+    1024 rows with at least 192 output tiles): 6144 x 128 weights of one
+    edge class at 1024 rows, under the natural plan and every forced format,
+    with the MFMA paths' rules."""
+    N, K, M = 6144, 128, 1024
+    W = class_weight(cls, N, K, seed=7)
+    x = class_x(cls, M, K, seed=11)
+    Wg = gpu(W)
+    fails = []
+    for plan in PLANS:
+        fmt = plan_for(orc, W, plan)
+        pw = api.pack(Wg, gpu(fmt))
+        assert B.ht_linear_workspace(pw.desc, M, B.HT_PATH_GEMM) == 48 * 2 * 33 * 1024   # the records
+        what = f"{cls} plan={plan} two-pass M={M}"
+        print(what, flush=True)
+        y = run(pw, x, B.HT_PATH_GEMM)
+        y_or = orc.linear(W, fmt, x)
+        if cls == "subnormal" and plan in (BF16, FP32):
+            bound = TOL * np.max(np.abs(y_or)) + float_subnormal_bound(orc, W, fmt, x)
+            if not np.all(np.abs(y - y_or) <= bound):
+                fails.append(f"{what}: beyond the subnormal bound")
+            continue
+        fails += check_edge(y, y_or, True, what)
     assert not fails, "\n".join(fails)
 
 
