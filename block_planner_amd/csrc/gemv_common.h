@@ -281,11 +281,12 @@ __device__ __forceinline__ void consume(const Slot &sl, uint32_t lane, const flo
 
 // Row sums of P in a fixed order: for (m, r), lane l adds P[m][r][l], then
 // P[m][r][l+64], ...; then a fixed butterfly over the 64 lanes.  Calls
-// out(m, r, value) on lane 0 for every (m, r) of this wave.
-template <int M, typename Out>
+// out(m, r, value) on lane 0 for every (m, r) of this wave (rows dealt to the
+// workgroup's NW wavefronts in turn).
+template <int M, int NW = kWaves, typename Out>
 __device__ __forceinline__ void reduce_rows(const float *P, uint32_t pstride, uint32_t R, uint32_t nkb,
                                             uint32_t wave, uint32_t lane, Out out) {
-    for (uint32_t pr = wave; pr < M * R; pr += kWaves) {
+    for (uint32_t pr = wave; pr < M * R; pr += NW) {
         const uint32_t m = pr / R, r = pr - m * R;
         float v = 0.0f;
         for (uint32_t k = lane; k < nkb; k += 64) v += P[(m * R + r) * pstride + k];

@@ -6,8 +6,10 @@
 //   INT4 / INT8:  blk = s * (sum_i q_i * x[m, 64kb+i])   (scale after the partial)
 //   BF16 / FP16 / FP32:  blk = sum_i w_i * x[m, 64kb+i]
 // all in fp32.  Workgroup (row tile t, K-split s) owns rows [tR, tR+R) and
-// K-blocks [kb0, kb1).  Its 16 wavefronts first issue x's loads, then one
-// batch of 8 chunks each (a 16-row x 4096 tile is a single batch), stage x in
+// K-blocks [kb0, kb1).  Its NW wavefronts (16, or 8 when there are more
+// workgroups than compute units: then two fit on a compute unit and all of
+// them run at once) first issue x's loads, then one batch of 8 chunks each
+// (a 16-row x 4096 tile is a single batch at 16 wavefronts), stage x in
 // LDS as fp32 while the weights are in flight, and consume each chunk as soon
 // as its own data has arrived.  Block partials go to an LDS table P[m][r][kb];
 // each (m, r) sums its row of P in a fixed order, so the result is bitwise
@@ -31,8 +33,10 @@ struct LinArgs {
     int act;
 };
 
-template <int M>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(LinArgs a) {
+template <int M, int NW>
+__global__ __launch_bounds__(64 * NW) void gemv_kernel(LinArgs a) {
+    constexpr uint32_t NT = 64 * NW;         // threads
+    constexpr int XL = 2 * kWaves / NW;      // 16-byte x loads per thread
     extern __shared__ float lds[];
     const LayerDev &w = a.w;
     const uint32_t t = blockIdx.x, sidx = blockIdx.y;
@@ -49,13 +53,13 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(LinArgs a) {
     // pointers derived from it then stay in scalar registers
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-    // x for these K-blocks: at most two 16-byte loads per thread (the host
+    // x for these K-blocks: at most XL 16-byte loads per thread (the host
     // keeps the M * nkb * 64 * 4 bytes of fp32 x within 64 KiB), issued first
     const uint32_t per_row = nkb * 8;   // 8 bf16 per 16-byte load
-    uint4 xr[2];
+    uint4 xr[XL];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const uint32_t i = threadIdx.x + j * kThreads;
+    for (int j = 0; j < XL; ++j) {
+        const uint32_t i = threadIdx.x + j * NT;
         if (i < M * per_row) {
             const uint32_t m = i / per_row, jj = i - m * per_row;
             xr[j] = *reinterpret_cast<const uint4 *>(a.x + int64_t(m) * a.ldx + kb0 * 64 + jj * 8);
@@ -72,7 +76,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(LinArgs a) {
         lo[f] = kbidx[uint64_t(f) * w.nk + col0];
     }
     ChunkWalker src = chunk_src(w, lo, hi);
-    walker_start(src, wave, kWaves);
+    walker_start(src, wave, NW);
 
     // first batch in flight while x goes into LDS
     Slot sl[kUnroll];
@@ -83,8 +87,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(LinArgs a) {
     }
 
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const uint32_t i = threadIdx.x + j * kThreads;
+    for (int j = 0; j < XL; ++j) {
+        const uint32_t i = threadIdx.x + j * NT;
         if (i < M * per_row) {
             const uint32_t m = i / per_row, jj = i - m * per_row;
             const uint4 v = xr[j];
@@ -109,7 +113,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(LinArgs a) {
     }
     __syncthreads();
 
-    reduce_rows<M>(P, pstride, w.R, nkb, wave, lane, [&](uint32_t m, uint32_t r, float v) {
+    reduce_rows<M, NW>(P, pstride, w.R, nkb, wave, lane, [&](uint32_t m, uint32_t r, float v) {
         const uint32_t n = t * w.R + r;
         if (n >= w.N) return;
         if (a.S == 1) {
@@ -188,16 +192,28 @@ uint32_t choose_splits(const ht_packed_weight *w, uint32_t Mt) {
 
 int m_tile(int64_t M) { return int(M < kMaxM ? M : kMaxM); }
 
-template <int M>
-ht_status launch_gemv(const LinArgs &a, uint32_t T, uint32_t lds, hipStream_t s) {
+// Workgroups of 8 wavefronts when there are more of them than compute units
+// and two fit on one (LDS), so that all run at once; else 16.  Both give the
+// same bits (each chunk's partial lands in its own slot of P).
+constexpr uint64_t kComputeUnits = 256;
+constexpr uint32_t kHalfLds = 80 * 1024;
+
+template <int M, int NW>
+ht_status launch_gemv_nw(const LinArgs &a, uint32_t T, uint32_t lds, hipStream_t s) {
     // more than 64 KiB of dynamic LDS is requested explicitly
     if (lds > 64u * 1024u &&
-        hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_kernel<M>), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            int(kMaxLds)) != hipSuccess)
+        hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_kernel<M, NW>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxLds)) != hipSuccess)
         return HT_EHIP;
-    hipLaunchKernelGGL(gemv_kernel<M>, dim3(T, a.S), dim3(kThreads), lds, s, a);
+    hipLaunchKernelGGL((gemv_kernel<M, NW>), dim3(T, a.S), dim3(64 * NW), lds, s, a);
     HT_LAUNCH_CHECK();
     return HT_OK;
+}
+
+template <int M>
+ht_status launch_gemv(const LinArgs &a, uint32_t T, uint32_t lds, hipStream_t s) {
+    if (uint64_t(T) * a.S > kComputeUnits && lds <= kHalfLds) return launch_gemv_nw<M, kWaves / 2>(a, T, lds, s);
+    return launch_gemv_nw<M, kWaves>(a, T, lds, s);
 }
 
 }  // namespace
