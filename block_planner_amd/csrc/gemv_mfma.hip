@@ -51,6 +51,7 @@ struct DecArgs {
     uint32_t M;
     uint32_t KBs;             // K-blocks per split
     uint32_t TPW;             // row tiles per workgroup (tiles blockIdx.x + i * gridDim.x, i < TPW)
+    uint32_t nbytes;          // packed buffer size (below 4 GiB)
     int act;
 };
 
@@ -72,8 +73,12 @@ template <int MG> constexpr uint32_t dec_row() { return (kDecChunk / MG) * 64u +
 
 // ROLL: the workgroup has more than one (round, tile) step, so columns are
 // refilled as they are consumed; without it each wavefront loads its columns
-// once.
-template <int MG, bool ROLL>
+// once.  BUF: the layer has many blocks wider than 16 bytes per lane (BF16,
+// FP16, FP32), so every column issues the same six loads with the unneeded
+// pieces masked per lane (buffer loads past the buffer's end read zeros
+// without a memory access); without it the pieces past the column's widest
+// format are skipped and lanes that need fewer re-read their first piece.
+template <int MG, bool ROLL, bool BUF>
 __global__ __launch_bounds__(kDecThreads) void gemv_mfma_kernel(DecArgs a) {
     constexpr uint32_t CK = kDecChunk / MG;           // K-blocks per round
     constexpr uint32_t CW = CK / kDecWaves;           // K-blocks per wavefront per round (4 or 2)
@@ -88,6 +93,8 @@ __global__ __launch_bounds__(kDecThreads) void gemv_mfma_kernel(DecArgs a) {
     const uint32_t kbs0 = blockIdx.y * a.KBs;
     const uint32_t kbs1 = min(w.KB, kbs0 + a.KBs);
     const uint8_t *base = w.base;                          // offsets below are 32-bit (buffer < 4 GiB)
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, int(a.nbytes), 0x00020000);
+    constexpr uint32_t kOut = 0xFFFFFFF0u;                 // an offset past the buffer (nbytes < kOut)
     const uint32_t *kbx = reinterpret_cast<const uint32_t *>(base + w.off_kbidx);
 
     uint32_t opay[5], oids[5];
@@ -114,7 +121,8 @@ __global__ __launch_bounds__(kDecThreads) void gemv_mfma_kernel(DecArgs a) {
 
     // Loads of column c of the window: the lane's block is slot j of the
     // column in the packed order; a missing block (slot past the tile's rows,
-    // or a column past the range) reads the buffer's first bytes.
+    // or a column past the range) reads the buffer's first bytes, or with
+    // BUF nothing.
     auto load_col = [&](uint32_t kv, uint32_t kv4, uint32_t c) -> DecLoad {
         DecLoad d;
         uint32_t ka[5], kn[5];
@@ -146,6 +154,19 @@ __global__ __launch_bounds__(kDecThreads) void gemv_mfma_kernel(DecArgs a) {
         }
         d.f = f;
         d.hi16 = blk & 1u;
+        if (BUF) {
+            // a fixed count of loads per column, so that the wait before a
+            // column's arithmetic counts exactly the later columns' loads
+            const bool has = f < 5;
+#pragma unroll
+            for (uint32_t i = 0; i < 4; ++i) {
+                const u32x4 pv = __builtin_amdgcn_raw_buffer_load_b128(rs, has && i < nl ? po + 16u * i : kOut, 0, 0);
+                d.p[i] = make_uint4(pv.x, pv.y, pv.z, pv.w);
+            }
+            d.id2 = __builtin_amdgcn_raw_buffer_load_b32(rs, has ? io : kOut, 0, 0);
+            d.sc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, f < 2 ? so : kOut, 0, 0));
+            return d;
+        }
         const u32x4 p0 = ld_stream_u4(base + po);
         d.p[0] = make_uint4(p0.x, p0.y, p0.z, p0.w);
         // further pieces only when some lane of the column needs them; a lane
@@ -329,14 +350,16 @@ __global__ __launch_bounds__(kDecThreads) void gemv_mfma_kernel(DecArgs a) {
 #pragma unroll
         for (uint32_t i = 0; i < NT; ++i) {
             if (!tile_ok(i)) continue;                    // workgroup-uniform
-            if (!ROLL) {                                  // one tile: load its columns now
-#pragma unroll
-                for (uint32_t c = 0; c < CW; ++c) d[c] = load_col(kv, kv4, c);
-                kbidx_window(blockIdx.x, kc + CK, kv, kv4);   // the next round's window (clamped past the end)
-            }
             if (i == 0) {
                 __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): this wavefront's x pieces are in LDS
                 __syncthreads();
+            }
+            if (!ROLL) {
+                // one tile: load its columns now, after the barrier, so that
+                // each column's arithmetic waits only for its own loads
+#pragma unroll
+                for (uint32_t c = 0; c < CW; ++c) d[c] = load_col(kv, kv4, c);
+                if (kc + CK < kbs1) kbidx_window(blockIdx.x, kc + CK, kv, kv4);   // the next round's window
             }
             // after the workgroup's last tile of its last round there is
             // nothing to refill; at MG = 2 the loads are skipped then, at
@@ -428,15 +451,30 @@ uint32_t dec_tpw(uint32_t T) {
     return tpw < kDecMaxTPW ? tpw : kDecMaxTPW;
 }
 
+template <int MG, bool ROLL>
+void launch_dec(const DecArgs &a, uint32_t G, uint32_t S, bool buf, hipStream_t s) {
+    if (buf) hipLaunchKernelGGL((gemv_mfma_kernel<MG, ROLL, true>), dim3(G, S), dim3(kDecThreads), 0, s, a);
+    else hipLaunchKernelGGL((gemv_mfma_kernel<MG, ROLL, false>), dim3(G, S), dim3(kDecThreads), 0, s, a);
+}
+
 template <int MG>
-void launch_dec(const DecArgs &a, uint32_t G, uint32_t S, bool roll, hipStream_t s) {
-    if (roll) hipLaunchKernelGGL((gemv_mfma_kernel<MG, true>), dim3(G, S), dim3(kDecThreads), 0, s, a);
-    else hipLaunchKernelGGL((gemv_mfma_kernel<MG, false>), dim3(G, S), dim3(kDecThreads), 0, s, a);
+void launch_dec(const DecArgs &a, uint32_t G, uint32_t S, bool roll, bool buf, hipStream_t s) {
+    if (roll) launch_dec<MG, true>(a, G, S, buf, s);
+    else launch_dec<MG, false>(a, G, S, buf, s);
+}
+
+// Masked fixed-count loads pay when most columns hold a block wider than 16
+// bytes per lane: with a share p of such blocks a 16-block column has one
+// with probability 1 - (1 - p)^16, one half at p = 4.2%.
+bool dec_buf(const ht_packed_weight *w) {
+    const int64_t wide = w->counts[2] + w->counts[3] + w->counts[4];
+    const int64_t all = wide + w->counts[0] + w->counts[1];
+    return wide * 24 >= all;
 }
 
 }  // namespace
 
-bool dec_ok(const ht_packed_weight *w) { return w->row_tile == 16; }
+bool dec_ok(const ht_packed_weight *w) { return w->row_tile == 16 && w->bytes < 0xFFFFFF00ull; }
 
 size_t dec_ws(const ht_packed_weight *w, int64_t M) {
     const int64_t Mt = M < kDecMaxM ? M : kDecMaxM;
@@ -455,6 +493,8 @@ ht_status run_dec(const ht_packed_weight *w, const uint16_t *x, int64_t M, int64
     a.KBs = d.KBs;
     const uint32_t T = uint32_t(w->n_tiles);
     a.TPW = dec_tpw(T);
+    a.nbytes = uint32_t(w->bytes);
+    const bool buf = dec_buf(w);
     const uint32_t G = (T + a.TPW - 1) / a.TPW;
     for (int64_t m0 = 0; m0 < M; m0 += kDecMaxM) {
         const int64_t Mt = M - m0 < kDecMaxM ? M - m0 : kDecMaxM;
@@ -475,8 +515,8 @@ ht_status run_dec(const ht_packed_weight *w, const uint16_t *x, int64_t M, int64
         // a K range longer than one round (64 K-blocks at MG = 1, 32 at 2)
         const uint32_t ck = Mt <= 16 ? kDecChunk : kDecChunk / 2;
         const bool roll = a.TPW > 1 || d.KBs > ck;
-        if (Mt <= 16) launch_dec<1>(a, G, d.S, roll, s);
-        else launch_dec<2>(a, G, d.S, roll, s);
+        if (Mt <= 16) launch_dec<1>(a, G, d.S, roll, buf, s);
+        else launch_dec<2>(a, G, d.S, roll, buf, s);
         HT_LAUNCH_CHECK();
         if (d.S > 1) {
             const ht_status st = launch_split_reduce(static_cast<const float *>(ws), d.S, uint32_t(Mt), a.w.N, yo,

@@ -70,7 +70,8 @@ ht_status run_gemm_i8(const ht_packed_weight *w, const uint16_t *x, int64_t M, i
 ht_status launch_split_reduce(const float *partial, uint32_t S, uint32_t M, uint32_t N, float *y, uint16_t *ybf,
                               int64_t ldy, int act, hipStream_t s);
 
-// The register-dequantising MFMA path (row tile 16 only): whether it takes
+// The register-dequantising MFMA path (row tile 16, packed buffer below 4 GiB,
+// its offsets being 32-bit): whether it takes
 // this weight, its workspace bytes for M rows (K-split partials), and one
 // linear on it (fp32 y or bfloat16 ybf; arguments assumed checked).
 bool dec_ok(const ht_packed_weight *w);
@@ -100,11 +101,11 @@ ht_status run_dw_gemm(const float *dy, int64_t M, int64_t lddy, const uint16_t *
                       int64_t K, float *dw, int64_t lddw, int accumulate, hipStream_t s);
 
 // The path HT_PATH_AUTO resolves to for one linear over M rows: the MFMA
-// decode path for 4..32 rows (row tile 16), otherwise the LDS-staged MFMA path
+// decode path for 4..32 rows (row tile 16, buffer below 4 GiB), otherwise the LDS-staged MFMA path
 // from 16 rows and the register path below (1 to 3 rows stay on the register
 // path, fastest there; from 4 rows its fp32 copy of x needs a K-split).
 inline int32_t auto_linear_path(const ht_packed_weight *w, int64_t M) {
-    if (M >= 4 && M <= 32 && w->row_tile == 16) return HT_PATH_GEMV_MFMA;
+    if (M >= 4 && M <= 32 && dec_ok(w)) return HT_PATH_GEMV_MFMA;
     return M >= 16 ? HT_PATH_GEMM : HT_PATH_GEMV;
 }
 
