@@ -82,8 +82,11 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(LinArgs a) {
     Slot sl[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-        sl[u] = walker_load(src, lane);
-        walker_advance(src);
+        sl[u].f = 5;
+        if (src.f < 5) {   // wave-uniform: no loads for slots past the wave's last chunk
+            sl[u] = walker_load(src, lane);
+            walker_advance(src);
+        }
     }
 
 #pragma unroll
@@ -105,8 +108,11 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(LinArgs a) {
     while (src.f < 5) {   // wave-uniform: chunks left for this wave
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            sl[u] = walker_load(src, lane);
-            walker_advance(src);
+            sl[u].f = 5;
+            if (src.f < 5) {
+                sl[u] = walker_load(src, lane);
+                walker_advance(src);
+            }
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) consume<M>(sl[u], lane, xs, xstride, P, pstride, kb0, nkb, w.R, w.lgR);
