@@ -233,13 +233,15 @@ def main() -> int:
         """The transformer-shaped configurations, on seeded device-drawn
         weights (workloads.*_weight_gpu):
           * TinyLlama-1.1B shapes (22 layers x 7 linears = 154): decode at
-            batch 1 over all of them, back to back;
+            batch 1 over all of them, back to back; then the same with q|k|v
+            and gate|up packed as one weight each (4 launches per layer);
           * Llama-3.1-8B shapes (32 x 7 = 224 linears, 7.0e9 parameters):
             the planner and packer streamed layer by layer over the whole set
             for eps_int4 in {0.04, 0.08, 0.16} and forced all-INT4 / all-INT8
             plans (events around each call, after a 512 MB write so that W
             comes from HBM, not from the Infinity Cache), then decode at
-            batch 1, 4 and 16 over all 224 linears packed at the default eps.
+            batch 1, 4 and 16 over all 224 linears packed at the default eps,
+            and over the 128 fused-projection weights.
         Each decode pass is one HIP graph of every linear in order (AUTO
         path, each with its own input and output), replayed; GB/s counts the
         packed bytes plus activations and outputs."""
@@ -269,7 +271,22 @@ def main() -> int:
                     "GBps": round(nbytes / t / 1e9, 1), "pct_hbm_peak": round(100 * nbytes / t / 1e9 / HBM_PEAK_GBS, 2),
                     "bytes_per_pass": int(nbytes)}
 
-        # TinyLlama: decode at batch 1 over the 154 linears
+        def fused_stack(gen, shapes, layers):
+            """Per layer four linears: q|k|v and gate|up as one weight each
+            (rows concatenated before planning, as serving engines fuse these
+            projections; the plan is per block, so every row gets the blocks
+            it gets alone), then o and down."""
+            sh = {s_.name: s_ for s_ in shapes}
+            out = []
+            for layer in range(layers):
+                for group in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",)):
+                    W = torch.cat([gen(layer, sh[n], dev) for n in group])
+                    out.append(api.pack(W, api.plan(W)))
+                    del W
+            return out
+
+        # TinyLlama: decode at batch 1 over the 154 linears, then over the 88
+        # launches of the fused q|k|v and gate|up weights
         log("configs: TinyLlama stack")
         pws = []
         for layer in range(wl.TINYLLAMA_LAYERS):
@@ -278,6 +295,9 @@ def main() -> int:
                 pws.append(api.pack(W, api.plan(W)))
                 del W
         res["tinyllama_decode_b1"] = decode_pass(pws, 1, 20)
+        del pws
+        pws = fused_stack(wl.tinyllama_weight_gpu, wl.tinyllama_shapes(), wl.TINYLLAMA_LAYERS)
+        res["tinyllama_decode_b1_fused_qkv_gateup"] = decode_pass(pws, 1, 20)
         del pws
         torch.cuda.empty_cache()
 
@@ -336,6 +356,11 @@ def main() -> int:
         for M in (1, 4, 16):
             res[f"llama8b_decode_b{M}"] = decode_pass(keep, M, 5)
         del keep
+        torch.cuda.empty_cache()
+        pws = fused_stack(wl.llama8b_weight_gpu, wl.llama8b_shapes(), wl.LLAMA8B_LAYERS)
+        for M in (1, 4, 16):
+            res[f"llama8b_decode_b{M}_fused_qkv_gateup"] = decode_pass(pws, M, 5)
+        del pws
         torch.cuda.empty_cache()
         return res
 

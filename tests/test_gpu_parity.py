@@ -281,6 +281,30 @@ def test_linear_long_k_split(orc):
         check_close(run_linear(W, fmt, x), orc.linear(W, fmt, x), f"K=14336 M={M}")
 
 
+@pytest.mark.parametrize("M", [1, 16, 64])
+def test_linear_fused_projections(orc, M):
+    """q|k|v rows concatenated into one weight (the fused projection of the
+    transformer decode stacks): its plan is the per-part plans stacked (the
+    plan is per block), every output matches the oracle, and each part's rows
+    equal the separate linear's within fp32 summation order (K-splits and
+    paths may differ with the row count): 1e-5 * max|y|."""
+    rng = np.random.default_rng(900 + M)
+    parts = [(rng.normal(0.0, 0.02, size=(n, 512)) * np.where(rng.random((n, 512)) < 0.001, 30.0, 1.0))
+             .astype(np.float32) for n in (256, 64, 64)]
+    W = np.concatenate(parts)
+    fmt = gpu_plan(W)
+    np.testing.assert_array_equal(fmt, np.concatenate([orc.plan(Wp) for Wp in parts]))
+    x = wl.to_bf16_bits(rng.normal(size=(M, 512)).astype(np.float32))
+    y = run_linear(W, fmt, x)
+    check_close(y, orc.linear(W, fmt, x), f"fused M={M}")
+    r0 = 0
+    for Wp in parts:
+        yp = run_linear(Wp, gpu_plan(Wp), x)
+        ys = y[:, r0:r0 + Wp.shape[0]]
+        assert np.max(np.abs(ys - yp)) <= 1e-5 * max(np.max(np.abs(yp)), 1e-30)
+        r0 += Wp.shape[0]
+
+
 def test_linear_deterministic():
     W = wl.mlp_weight(1, dim=4096)[:2048]
     Wg = gpu(W)
