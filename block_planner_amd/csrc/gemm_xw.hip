@@ -276,7 +276,7 @@ __global__ __launch_bounds__(kXwThreads) void gemm_xw_kernel(XwGemmArgs a) {
     // record's group flag; other groups' lo planes are not even written).
     // A operands are read two row tiles ahead; one scheduling region per row
     // tile keeps that order.
-    auto mfma_step = [&](const uint8_t *st) {
+    auto mfma_step = [&](const uint8_t *st, auto &&mid) {
         const uint16_t *xs = reinterpret_cast<const uint16_t *>(st);
         const uint8_t *rec = st + kXwX;
         bf16x8 Bh[2][2], Bl[2][2];
@@ -330,6 +330,7 @@ __global__ __launch_bounds__(kXwThreads) void gemm_xw_kernel(XwGemmArgs a) {
                 }
             }
             if (i > 1) scale_add(i - 2, cp[i % 2]);
+            if (i == 1) mid();   // the next copies, once this step's first operands are in registers
             cp[i % 2][0] = cc[0];
             cp[i % 2][1] = cc[1];
             __builtin_amdgcn_sched_barrier(0);
@@ -338,21 +339,23 @@ __global__ __launch_bounds__(kXwThreads) void gemm_xw_kernel(XwGemmArgs a) {
         scale_add(7, cp[1]);
     };
 
-    // two LDS stages; the copy for step t+2 goes into step t's stage right
-    // after the barrier that ends step t
+    // two LDS stages; the copy for step t+2 goes into step t's stage during
+    // step t+1 (after the barrier that ends step t), issued once step t+1's
+    // first operands have been read, so that they do not queue behind it
     copy(0, lds0);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies are in LDS
     if (KB > 1) copy(1, lds1);
     xw_lds_barrier();
-    auto step = [&](uint32_t t, uint8_t *st) {
-        mfma_step(st);
+    auto step = [&](uint32_t t, const uint8_t *st, uint8_t *prev) {
+        mfma_step(st, [&]() {
+            if (t >= 1 && t + 1 < KB) copy(t + 1, prev);
+        });
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the copies for step t+1 are in LDS
         xw_lds_barrier();
-        if (t + 2 < KB) copy(t + 2, st);
     };
     for (uint32_t t = 0; t < KB; t += 2) {
-        step(t, lds0);
-        if (t + 1 < KB) step(t + 1, lds1);
+        step(t, lds0, lds1);
+        if (t + 1 < KB) step(t + 1, lds1, lds0);
     }
 
     // ---- output: lane holds column lr, rows 4*(lane/16) + e of each 16x16 tile ----
