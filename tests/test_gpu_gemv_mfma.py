@@ -191,3 +191,19 @@ def test_dec_several_tiles_per_workgroup(orc, N, K, M):
     fmt = rng.integers(0, 5, size=(N, K // 64)).astype(np.uint8)
     x = wl.to_bf16_bits(rng.normal(size=(M, K)).astype(np.float32))
     check_close(run_dec(W, fmt, x), orc.linear(W, fmt, x), f"N={N} K={K} M={M}")
+
+
+@pytest.mark.parametrize("share", [0.03, 0.06])
+@pytest.mark.parametrize("N,K,M", [(4096, 4096, 16), (5632, 2048, 16), (4096, 4096, 32)])
+def test_dec_load_schemes(orc, share, N, K, M):
+    """Both load schemes: a layer whose FP32 blocks are 3% of its blocks
+    (under the 4.2% at which a 16-block column holds one with probability
+    1/2: the columns skip the pieces no lane needs) and one with 6% (every
+    column issues its fixed six loads with the unneeded ones masked), each
+    with one step per workgroup (4096 x 4096 at 16 rows), several row tiles
+    per workgroup (352 tiles) and two rounds of K (32 rows)."""
+    rng = np.random.default_rng(int(share * 1000) + N + M)
+    W = (rng.standard_t(4, size=(N, K)) * 0.02).astype(np.float32)
+    fmt = np.where(rng.random((N, K // 64)) < share, FP32, INT8).astype(np.uint8)
+    x = wl.to_bf16_bits(rng.normal(size=(M, K)).astype(np.float32))
+    check_close(run_dec(W, fmt, x), orc.linear(W, fmt, x), f"share={share} N={N} K={K} M={M}")
