@@ -541,12 +541,12 @@ size_t gemm_ws_min(const ht_packed_weight *w, int64_t M) {
 
 size_t gemm_ws(const ht_packed_weight *w, int64_t M) {
     const size_t m = gemm_ws_min(w, M);
-    return xw_takes(w, M) && xw_ws(w) > m ? xw_ws(w) : m;
+    return xw_takes(w, M) && xw_ws(w, M) > m ? xw_ws(w, M) : m;
 }
 
 ht_status run_gemm(const ht_packed_weight *w, const uint16_t *x, int64_t M, int64_t ldx, float *y, uint16_t *ybf,
                    int64_t ldy, int act, void *ws, size_t ws_bytes, hipStream_t s) {
-    if (xw_takes(w, M) && ws && ws_bytes >= xw_ws(w)) return run_gemm_xw(w, x, M, ldx, y, ybf, ldy, act, ws, s);
+    if (xw_takes(w, M) && ws && ws_bytes >= xw_ws(w, M)) return run_gemm_xw(w, x, M, ldx, y, ybf, ldy, act, ws, s);
     for (int64_t m0 = 0; m0 < M; m0 += kGemmChunkRows) {
         const int64_t Mt = M - m0 < kGemmChunkRows ? M - m0 : kGemmChunkRows;
         const uint32_t S = gemm_splits(w, Mt);

@@ -186,6 +186,11 @@ struct XwGemmArgs {
     int64_t ldy;
     uint32_t M, N, KB, MT, NT;
     int act;
+    // tiles [full, MT*NT) run as two workgroups each, K-blocks [0, KBh) and
+    // [KBh, KB), dispatched after the others; they write fp32 partial sums
+    // part[half][tile - full][256][128] that xw_tail_kernel adds
+    uint32_t full, KBh;
+    float *part;
 };
 
 // Workgroup barrier that waits for this wave's LDS operations only.
@@ -208,11 +213,25 @@ __global__ __launch_bounds__(kXwThreads) void gemm_xw_kernel(XwGemmArgs a) {
 
     const uint32_t tid = threadIdx.x, lane = tid & 63;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    uint32_t L = blockIdx.x;
-    if ((gridDim.x & 7u) == 0) L = (blockIdx.x & 7u) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    // Workgroup -> tile: the whole-K tiles first, then the split tiles' halves
+    // (so that those short workgroups fill the last round); each range
+    // spread over the XCDs in contiguous runs.
+    uint32_t L, kb0 = 0, kb1 = a.KB, half = 2u;
+    if (blockIdx.x < a.full) {
+        L = blockIdx.x;
+        if ((a.full & 7u) == 0) L = (L & 7u) * (a.full >> 3) + (L >> 3);
+    } else {
+        const uint32_t n = gridDim.x - a.full;
+        uint32_t j = blockIdx.x - a.full;
+        if ((n & 7u) == 0) j = (j & 7u) * (n >> 3) + (j >> 3);
+        L = a.full + (j >> 1);
+        half = j & 1u;
+        kb0 = half ? a.KBh : 0u;
+        kb1 = half ? a.KB : a.KBh;
+    }
     const uint32_t nt = L / a.MT, mt = L - nt * a.MT;
     const uint32_t n0 = nt * kXwBN, m0 = mt * kXwBM;
-    const uint32_t KB = a.KB;
+    const uint32_t KB = kb1 - kb0;
     const uint32_t wr = wave >> 2, wc = wave & 3;
 
     // x copy: instruction g (of 32) moves rows [8g, +8): lane l -> row
@@ -229,7 +248,7 @@ __global__ __launch_bounds__(kXwThreads) void gemm_xw_kernel(XwGemmArgs a) {
         xrow[i] = a.x + int64_t(rb) * a.ldx;
         xoff[i] = uint32_t((uint64_t(rr - rb) * uint64_t(a.ldx) + 8u * (xslot ^ ((r >> 1) & 7u))) * 2u);
     }
-    const uint8_t *recs = a.rec + uint64_t(nt) * KB * kXwRec;
+    const uint8_t *recs = a.rec + (uint64_t(nt) * a.KB + kb0) * kXwRec;
     // Issued as inline assembly (M0 = LDS destination of the instruction's
     // 1 KiB), so the compiler adds no waits for them before unrelated LDS
     // reads; each wave waits for its own copies (vmcnt(0)) before the barrier
@@ -238,7 +257,7 @@ __global__ __launch_bounds__(kXwThreads) void gemm_xw_kernel(XwGemmArgs a) {
         const uint32_t base = uint32_t(uintptr_t((__attribute__((address_space(3))) uint8_t *)st));
 #pragma unroll
         for (uint32_t i = 0; i < 4; ++i) {
-            const uint16_t *src = xrow[i] + kb * 64u;
+            const uint16_t *src = xrow[i] + (kb0 + kb) * 64u;
             const uint32_t dst = base + 1024u * (4 * wave + i);
             asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                          :
@@ -359,6 +378,17 @@ __global__ __launch_bounds__(kXwThreads) void gemm_xw_kernel(XwGemmArgs a) {
     }
 
     // ---- output: lane holds column lr, rows 4*(lane/16) + e of each 16x16 tile ----
+    if (half < 2u) {   // a split tile: this half's partial sums, whole tile, no activation
+        float *p = a.part + (uint64_t(half) * (a.MT * a.NT - a.full) + (L - a.full)) * (kXwBM * kXwBN);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    p[(128 * wr + 16 * i + 4 * lq + e) * kXwBN + 32 * wc + 16 * j + lr] = acc[i][j][e] + alo[i][j][e];
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -377,6 +407,32 @@ __global__ __launch_bounds__(kXwThreads) void gemm_xw_kernel(XwGemmArgs a) {
         }
 }
 
+// The split tiles: y = act(part[0] + part[1]) (the first K half's sum plus
+// the second's, always in that order), four outputs per thread.
+__global__ __launch_bounds__(256) void xw_tail_kernel(XwGemmArgs a) {
+    const uint32_t i = blockIdx.x * 256u + threadIdx.x;     // [tile][row][column / 4]
+    const uint32_t tail = a.MT * a.NT - a.full;
+    if (i >= tail * (kXwBM * kXwBN / 4)) return;
+    const uint32_t tl = i / (kXwBM * kXwBN / 4), rem = i - tl * (kXwBM * kXwBN / 4);
+    const uint32_t r = rem / (kXwBN / 4), c4 = rem - r * (kXwBN / 4);
+    const uint32_t L = a.full + tl, nt = L / a.MT, mt = L - nt * a.MT;
+    const uint32_t m = mt * kXwBM + r;
+    if (m >= a.M) return;
+    const uint64_t off = uint64_t(tl) * (kXwBM * kXwBN) + r * kXwBN + 4 * c4;
+    const float4 p0 = *reinterpret_cast<const float4 *>(a.part + off);
+    const float4 p1 = *reinterpret_cast<const float4 *>(a.part + uint64_t(tail) * (kXwBM * kXwBN) + off);
+    const float v[4] = {p0.x + p1.x, p0.y + p1.y, p0.z + p1.z, p0.w + p1.w};
+#pragma unroll
+    for (uint32_t e = 0; e < 4; ++e) {
+        const uint32_t n = nt * kXwBN + 4 * c4 + e;
+        if (n >= a.N) continue;
+        float o = v[e];
+        if (a.act == HT_ACT_RELU) o = o > 0.0f ? o : 0.0f;
+        if (a.ybf) a.ybf[int64_t(m) * a.ldy + n] = f32_to_bf16_rne(o);
+        else a.y[int64_t(m) * a.ldy + n] = o;
+    }
+}
+
 constexpr int64_t kXwChunkRows = int64_t(1) << 20;   // rows per GEMM launch
 constexpr int64_t kXwMaxLdx = int64_t(1) << 28;      // x row stride limit (elements)
 
@@ -389,9 +445,34 @@ bool xw_takes(const ht_packed_weight *w, int64_t M) {
     return M >= kXwMinM && NT * ((Mt + kXwBM - 1) / kXwBM) >= 192;
 }
 
-size_t xw_ws(const ht_packed_weight *w) {
+// Compute units (one GEMM workgroup each: its LDS allows one).
+uint32_t xw_units() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    return uint32_t(cus);
+}
+
+// Tiles of one launch run with K split in two: the last round's, when it
+// would fill at most half of the compute units (then its halves fill it, in
+// about half the time), and only when K has two K-blocks or more.
+uint32_t xw_split_tiles(uint32_t tiles, uint32_t KB, uint32_t units) {
+    const uint32_t tail = tiles % units;
+    return tiles > units && tail > 0 && 2 * tail <= units && KB >= 2 ? tail : 0u;
+}
+
+size_t xw_records(const ht_packed_weight *w) {
     const uint64_t NT = uint64_t((w->N + kXwBN - 1) / kXwBN), KB = uint64_t(w->K / kBlockK);
     return size_t(NT * KB * kXwRec);
+}
+
+size_t xw_ws(const ht_packed_weight *w, int64_t M) {
+    const uint64_t NT = uint64_t((w->N + kXwBN - 1) / kXwBN);
+    const int64_t Mt = M < kXwChunkRows ? M : kXwChunkRows;
+    const uint64_t tiles = NT * uint64_t((Mt + kXwBM - 1) / kXwBM);
+    const uint32_t split = xw_split_tiles(uint32_t(tiles), uint32_t(w->K / kBlockK), xw_units());
+    return xw_records(w) + size_t(split) * 2u * kXwBM * kXwBN * sizeof(float);
 }
 
 ht_status run_gemm_xw(const ht_packed_weight *w, const uint16_t *x, int64_t M, int64_t ldx, float *y, uint16_t *ybf,
@@ -419,8 +500,16 @@ ht_status run_gemm_xw(const ht_packed_weight *w, const uint16_t *x, int64_t M, i
         a.MT = uint32_t((Mt + kXwBM - 1) / kXwBM);
         a.NT = e.NT;
         a.act = act;
-        hipLaunchKernelGGL(gemm_xw_kernel, dim3(a.MT * a.NT), dim3(kXwThreads), 0, s, a);
+        const uint32_t tiles = a.MT * a.NT, split = xw_split_tiles(tiles, a.KB, xw_units());
+        a.full = tiles - split;
+        a.KBh = a.KB / 2;
+        a.part = reinterpret_cast<float *>(e.rec + xw_records(w));
+        hipLaunchKernelGGL(gemm_xw_kernel, dim3(a.full + 2 * split), dim3(kXwThreads), 0, s, a);
         HT_LAUNCH_CHECK();
+        if (split) {
+            hipLaunchKernelGGL(xw_tail_kernel, dim3(split * (kXwBM * kXwBN / 4) / 256), dim3(256), 0, s, a);
+            HT_LAUNCH_CHECK();
+        }
     }
     return HT_OK;
 }

@@ -43,7 +43,7 @@ size_t linear_path_ws_min(const ht_packed_weight *w, int64_t M, int32_t path);
 // workspace bytes (the expanded records), and one linear on it.
 constexpr int64_t kXwMinM = 1024;
 bool xw_takes(const ht_packed_weight *w, int64_t M);
-size_t xw_ws(const ht_packed_weight *w);
+size_t xw_ws(const ht_packed_weight *w, int64_t M);
 ht_status run_gemm_xw(const ht_packed_weight *w, const uint16_t *x, int64_t M, int64_t ldx, float *y, uint16_t *ybf,
                       int64_t ldy, int act, void *ws, hipStream_t s);
 

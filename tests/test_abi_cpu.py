@@ -216,6 +216,11 @@ def test_linear_argument_checks():
     assert B.ht_linear_workspace(wide, 1000, B.HT_PATH_GEMM) == 0
     assert B.ht_linear_workspace(wide, 2048, B.HT_PATH_GEMM) == (16384 // 128) * (4096 // 64) * 33 * 1024
     assert B.ht_linear_workspace(_desc(N=6144, K=4096, R=16), 1024, B.HT_PATH_GEMM) == 48 * 64 * 33 * 1024
+    # 112 x 8 = 896 output tiles: the last round's 128 tiles (half of 256
+    # compute units) run as two K halves, whose fp32 partial sums follow the
+    # records
+    assert B.ht_linear_workspace(_desc(N=14336, K=4096, R=16), 2048, B.HT_PATH_GEMM) == \
+        112 * 64 * 33 * 1024 + 128 * 2 * 256 * 128 * 4
     # 188 tiles: the single-pass kernel, which splits K in two below 192
     assert B.ht_linear_workspace(_desc(N=6016, K=4096, R=16), 1024, B.HT_PATH_GEMM) == 2 * 1024 * 6016 * 4
     with pytest.raises(B.HTError):

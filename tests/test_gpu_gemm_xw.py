@@ -132,3 +132,29 @@ def test_xw_smaller_workspace_runs_single_pass():
     y_xw = linear(pw, x)
     assert torch.equal(y_small[:1000], y_1000)
     assert (y_small - y_xw).abs().max().item() <= 1e-5 * y_xw.abs().max().item()
+
+
+@pytest.mark.parametrize("act", [B.HT_ACT_NONE, B.HT_ACT_RELU])
+def test_xw_split_last_round(orc, act):
+    """36 x 8 = 288 output tiles: the last round's 32 tiles run as two
+    workgroups each over the K halves and a second kernel adds the halves
+    (first, then second) and applies the activation.  N = 4600 (ragged last
+    column tile), M = 2040 (ragged last row tile), K = 256: every output
+    against fp64, and the first 1000 rows against the single-pass kernel
+    within 1e-5 * max|y|."""
+    rng = np.random.default_rng(530 + act)
+    W, fmt = mixed_weight(rng, 4600, 256)
+    pw = api.pack(gpu(W), gpu(fmt))
+    x = wl.to_bf16_bits(rng.normal(size=(2040, 256)).astype(np.float32))
+    y = api.linear(pw, bf16_gpu(x), act=act, path=GEMM)
+    torch.cuda.synchronize()
+    ref = orc.linear(W, fmt, x)
+    if act == B.HT_ACT_RELU:
+        ref = np.maximum(ref, 0.0)
+    yc = y.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(yc))
+    assert np.max(np.abs(yc - ref)) <= TOL * np.max(np.abs(ref))
+    y1 = api.linear(pw, bf16_gpu(x[:1000]), act=act, path=GEMM)
+    torch.cuda.synchronize()
+    assert (y[:1000] - y1).abs().max().item() <= 1e-5 * y1.abs().max().item()
+    assert torch.equal(api.linear(pw, bf16_gpu(x), act=act, path=GEMM), y)
