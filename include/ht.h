@@ -260,7 +260,10 @@ ht_status ht_linear_workspace(const ht_packed_weight *w, int64_t M, int32_t path
  *          accumulation (for prefill, many rows).  From 1024 rows, when the
  *          256-row x 128-column output tiles number at least 192 and ws holds
  *          ht_linear_workspace's bytes (33 KiB per 128-column x 64-K weight
- *          tile), it runs in two passes: the weight tiles are first expanded
+ *          tile, plus 256 KiB per output tile of a last round that fills at
+ *          most half of the compute units: those tiles run as two K halves
+ *          whose fp32 sums a second kernel adds, first half then second),
+ *          it runs in two passes: the weight tiles are first expanded
  *          once into those bfloat16 planes in ws, which every row tile then
  *          reads; the lo plane's products are added once at the end instead
  *          of per K-block, so the result differs from the single-pass
