@@ -20,11 +20,13 @@ fp32 last layer).
 
 Also reported (not the headline value): planner, packer and fused-refresh
 GB/s (over 8 rotated fp32 weights, 512 MB), the single-layer GEMV, the
-per-layer MLP path, batch 32, a warm-cache figure, the prefill GEMM (MFMA
+per-layer MLP path, batch 16 (µs per 4096^2 layer on the MFMA decode path)
+and 32, a warm-cache figure, the prefill GEMM (MFMA
 path, M = 2048, Llama-8B-shaped layers) in TFLOP/s, the int8 path, the
 backward kernels, and the transformer-shaped configurations: TinyLlama decode
-at batch 1 over its 154 linears, Llama-8B decode at batch 1 / 4 / 16 over its
-224 linears and the planner / packer sweep over the Llama-8B set.  The CPU
+at batch 1 over its 154 linears (and over its 88 fused-projection weights),
+Llama-8B decode at batch 1 / 4 / 16 over its 224 linears (and 128 fused) and
+the planner / packer sweep over the Llama-8B set.  The CPU
 baseline is the oracle on the host's cores (all of them, and one).
 
 Prints ONE JSON line.
@@ -607,14 +609,18 @@ def main() -> int:
         return 0
 
     packed_mb = sum(p.nbytes for p in copies[0]) / 1e6
-    log("mlp per-layer path, batch 32, warm cache")
+    log("mlp per-layer path, batch 16 and 32, warm cache")
     gp = graph_of(mlp_fn(x1, y1, path=B.HT_PATH_GEMV), G)
     t_perlayer = replay_timed(gp, reps, 1) / G
+    x16, y16 = xbf(16), torch.empty((16, D), dtype=torch.float32, device=dev)
+    g16 = graph_of(mlp_fn(x16, y16), C)   # the MFMA decode path, one launch per 4096^2 layer
+    t16 = replay_timed(g16, 10, 2) / C
+    step_bytes16 = sum(layer_bytes(counts[l], 16, D, D, 2 if l + 1 < L else 4) for l in range(L))
     g32 = graph_of(mlp_fn(x32, y32), C)
     t32 = replay_timed(g32, 10, 2) / C
     gw = graph_of(mlp_fn(x1, y1, rotate=False), G)
     t_warm = replay_timed(gw, reps, 1) / G
-    del gp, g32, gw
+    del gp, g16, g32, gw
 
     gemm = bwd = None
     if not args.no_gemm:
@@ -727,6 +733,8 @@ def main() -> int:
         "single_layer_gemv": {"kernel": "gemv_kernel<1>", "GBps": round(gemv_gbs, 2),
                               "avg_launch_us": round(gemv_dur * 1e6, 3),
                               "algorithmic_bytes_per_launch": int(avg_lin_bytes)},
+        "mlp_batch16_us_per_layer": round(t16 / L * 1e6, 2),
+        "mlp_batch16_GBps": round(step_bytes16 / t16 / 1e9, 2),
         "mlp_batch32_GBps": round(step_bytes32 / t32 / 1e9, 2),
         "mlp_batch32_ms_per_step": round(t32 * 1e3, 4),
         "mlp_batch1_warm_cache_GBps": round(step_bytes1 / t_warm / 1e9, 2),
