@@ -52,6 +52,7 @@ struct XwExpandArgs {
     LayerDev w;
     uint8_t *rec;    // [NT][KB] records
     uint32_t NT;
+    uint32_t nbytes; // packed buffer size (below 4 GiB: 32-bit offsets)
 };
 
 // One workgroup per (column tile nt, run of kXwExpandKb K-blocks); thread
@@ -76,39 +77,68 @@ __global__ __launch_bounds__(256) void xw_expand_kernel(XwExpandArgs a) {
         const bf16x2 v = {(__bf16)r0, (__bf16)r1};
         return __builtin_bit_cast(uint32_t, v);
     };
+    // per-format offsets as scalars (selected below by compares, not by
+    // indexing the argument block); buffer loads past the buffer read zeros
+    uint32_t opay[5], oids[5];
+#pragma unroll
+    for (int g = 0; g < 5; ++g) {
+        opay[g] = uint32_t(w.off_pay[g]);
+        oids[g] = uint32_t(w.off_ids[g]);
+    }
+    const uint32_t osc0 = uint32_t(w.off_scale[0]), osc1 = uint32_t(w.off_scale[1]);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)w.base, 0, int(a.nbytes), 0x00020000);
+    constexpr uint32_t kOut = 0xFFFFFFF0u;
     for (uint32_t kb = kb0; kb < kb1; ++kb) {
         // the slot's format f and block index: c[f] <= bi < c[f+1] over the
-        // prefix sums of the step's block counts in format order
-        int f = 5;
-        uint32_t blk = 0;
-        if (tok) {
-            uint32_t cum = 0;
-            for (int g = 0; g < 5; ++g) {
-                const uint32_t *e = kbidx + uint32_t(g) * w.nk + tile * w.KB + kb;
-                const uint32_t ka = e[0], cnt = e[1] - ka;
-                if (f == 5 && bi < cum + cnt) {
-                    f = g;
-                    blk = ka + (bi - cum);
-                }
-                cum += cnt;
+        // prefix sums of the step's block counts in format order (all ten
+        // kbidx words loaded at once, then compares: one round trip)
+        uint32_t ka[5], kn[5];
+#pragma unroll
+        for (int g = 0; g < 5; ++g) {
+            const uint32_t e = uint32_t(g) * w.nk + (tok ? tile : 0u) * w.KB + kb;
+            ka[g] = __builtin_amdgcn_raw_buffer_load_b32(rs, uint32_t(w.off_kbidx) + 4u * e, 0, 0);
+            kn[g] = __builtin_amdgcn_raw_buffer_load_b32(rs, uint32_t(w.off_kbidx) + 4u * (e + 1u), 0, 0);
+        }
+        uint32_t c = 0, f = 0, cf = 0, kaf = 0;
+#pragma unroll
+        for (int g = 0; g < 5; ++g) {
+            const uint32_t cnt = kn[g] - ka[g];
+            const bool past = bi >= c + cnt;          // the slot lies beyond format g
+            f += past ? 1u : 0u;
+            cf = (f == uint32_t(g)) ? c : cf;         // set while f == g: the start of the slot's format
+            kaf = (f == uint32_t(g)) ? ka[g] : kaf;
+            c += cnt;
+        }
+        if (!tok) f = 5;
+        const uint32_t blk = kaf + (bi - cf);
+        uint32_t po = kOut, io = kOut, so = kOut, np = 0, pb = 0;
+#pragma unroll
+        for (int g = 0; g < 5; ++g) {
+            if (f == uint32_t(g)) {
+                pb = uint32_t(pay_bytes(g));
+                po = opay[g] + blk * pb + h * (pb / 2);
+                io = oids[g] + 2u * blk;
+                so = g == 0 ? osc0 + 4u * blk : g == 1 ? osc1 + 4u * blk : kOut;
+                np = pb / 32;   // 16-byte pieces of this half
             }
         }
-        uint32_t hp[16], lp[16], id = gb, u[32];
-        float sc = 1.0f;
+        // eight 16-byte pieces, those past this half's bytes masked
+        uint32_t u[32];
+#pragma unroll
+        for (uint32_t j = 0; j < 8; ++j) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, j < np ? po + 16u * j : kOut, 0, 0);
+            u[4 * j] = v.x;
+            u[4 * j + 1] = v.y;
+            u[4 * j + 2] = v.z;
+            u[4 * j + 3] = v.w;
+        }
+        const uint32_t idv = __builtin_amdgcn_raw_buffer_load_b32(rs, io & ~3u, 0, 0);
+        const float scv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, so, 0, 0));
+        uint32_t hp[16], lp[16];
+        const uint32_t id = f < 5 ? ((io & 2u) ? idv >> 16 : idv & 0xFFFFu) : gb;
+        const float sc = f < 2 ? scv : 1.0f;
+#pragma unroll
         for (int i = 0; i < 16; ++i) hp[i] = lp[i] = 0u;
-        if (f < 5) {
-            const uint32_t pb = uint32_t(pay_bytes(f));
-            const uint8_t *src = w.base + w.off_pay[f] + uint64_t(blk) * pb + h * (pb / 2);
-            for (uint32_t j = 0; j < pb / 32; ++j) {
-                const uint4 v = reinterpret_cast<const uint4 *>(src)[j];
-                u[4 * j] = v.x;
-                u[4 * j + 1] = v.y;
-                u[4 * j + 2] = v.z;
-                u[4 * j + 3] = v.w;
-            }
-            id = reinterpret_cast<const uint16_t *>(w.base + w.off_ids[f])[blk];
-            if (f < 2) sc = reinterpret_cast<const float *>(w.base + w.off_scale[f])[blk];
-        }
         switch (f) {
         case 0:
             // byte i of the half's first 8 holds entries 32h+i (low nibble)
@@ -441,8 +471,9 @@ constexpr int64_t kXwMaxLdx = int64_t(1) << 28;      // x row stride limit (elem
 bool xw_takes(const ht_packed_weight *w, int64_t M) {
     const int64_t NT = (w->N + kXwBN - 1) / kXwBN;
     const int64_t Mt = M < kXwChunkRows ? M : kXwChunkRows;
-    // several row tiles share each expansion, and the tiles fill the chip
-    return M >= kXwMinM && NT * ((Mt + kXwBM - 1) / kXwBM) >= 192;
+    // several row tiles share each expansion, and the tiles fill the chip;
+    // the expansion reads the packed buffer with 32-bit offsets
+    return M >= kXwMinM && NT * ((Mt + kXwBM - 1) / kXwBM) >= 192 && w->bytes < 0xFFFFFF00ull;
 }
 
 // Compute units (one GEMM workgroup each: its LDS allows one).
@@ -482,6 +513,7 @@ ht_status run_gemm_xw(const ht_packed_weight *w, const uint16_t *x, int64_t M, i
     e.w = layer_dev(w);
     e.rec = static_cast<uint8_t *>(ws);
     e.NT = uint32_t((w->N + kXwBN - 1) / kXwBN);
+    e.nbytes = uint32_t(w->bytes);
     const uint32_t kbr = (e.w.KB + kXwExpandKb - 1) / kXwExpandKb;
     hipLaunchKernelGGL(xw_expand_kernel, dim3(e.NT * kbr), dim3(256), 0, s, e);
     HT_LAUNCH_CHECK();
