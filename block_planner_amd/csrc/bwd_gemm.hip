@@ -46,6 +46,7 @@ struct BgArgs {
     uint32_t M, MT, KT;   // rows of dY, row tiles of dX, column tiles of dX
     uint32_t TPS;         // row tiles of W per split (a multiple of 4)
     uint32_t vec;         // lddy % 4 == 0: dY rows read as float4
+    uint32_t nbytes;      // packed buffer size (below 4 GiB: 32-bit offsets)
 };
 
 template <int MI>
@@ -230,45 +231,55 @@ __global__ __launch_bounds__(kBgThreads) void bwd_gemm_kernel(BgArgs a) {
         oids[f] = uint32_t(w.off_ids[f]);
     }
     const uint32_t osc0 = uint32_t(w.off_scale[0]), osc1 = uint32_t(w.off_scale[1]);
-    const uint32_t *kbx = reinterpret_cast<const uint32_t *>(base + w.off_kbidx);
+    const uint32_t okx = uint32_t(w.off_kbidx);
 
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, int(a.nbytes), 0x00020000);
+    constexpr uint32_t kOut = 0xFFFFFFF0u;   // a buffer offset past the end: reads zeros
     auto load_block = [&](uint32_t t) -> BgLoad {
         BgLoad q;
-        q.f = 5;
         const uint32_t tile = t0 + kBgTilesPerStep * t + tl;
         const bool ok = kok && tile < t1 && t < nsteps;
         const uint32_t ix = ok ? tile * w.KB + kb : 0u;
-        uint32_t cum = 0, blk = 0;
-#pragma unroll
-        for (int f = 0; f < 5; ++f) {
-            const uint32_t ka = kbx[uint32_t(f) * w.nk + ix], kn = kbx[uint32_t(f) * w.nk + ix + 1];
-            const uint32_t cnt = ok ? kn - ka : 0u;
-            if (q.f == 5 && bi < cum + cnt) {
-                q.f = f;
-                blk = ka + (bi - cum);
-            }
-            cum += cnt;
-        }
-        const bool has = q.f < 5;
-        const int f = has ? q.f : 0;
-        uint32_t po = 0, io = 0, so = 0, nl = 1;
+        // the slot's format and block: c[f] <= bi < c[f+1] over the prefix
+        // sums of the block counts in format order (the ten kbidx words
+        // loaded at once, then compares: one round trip)
+        uint32_t ka[5], kn[5];
 #pragma unroll
         for (int g = 0; g < 5; ++g) {
-            if (f == g) {
+            const uint32_t e = uint32_t(g) * w.nk + ix;
+            ka[g] = __builtin_amdgcn_raw_buffer_load_b32(rs, okx + 4u * e, 0, 0);
+            kn[g] = __builtin_amdgcn_raw_buffer_load_b32(rs, okx + 4u * (e + 1u), 0, 0);
+        }
+        uint32_t c = 0, f = 0, cf = 0, kaf = 0;
+#pragma unroll
+        for (int g = 0; g < 5; ++g) {
+            const uint32_t cnt = kn[g] - ka[g];
+            f += (bi >= c + cnt) ? 1u : 0u;           // the slot lies beyond format g
+            cf = (f == uint32_t(g)) ? c : cf;
+            kaf = (f == uint32_t(g)) ? ka[g] : kaf;
+            c += cnt;
+        }
+        if (!ok) f = 5;
+        const uint32_t blk = kaf + (bi - cf);
+        uint32_t po = kOut, io = kOut, so = kOut, nl = 0;
+#pragma unroll
+        for (int g = 0; g < 5; ++g) {
+            if (f == uint32_t(g)) {
                 po = opay[g] + blk * uint32_t(pay_bytes(g)) + h * uint32_t(pay_bytes(g) / 2);
                 io = oids[g] + ((2u * blk) & ~3u);
-                so = g == 0 ? osc0 + 4u * blk : g == 1 ? osc1 + 4u * blk : 0u;
-                nl = uint32_t(pay_bytes(g) / 32);
+                so = g == 0 ? osc0 + 4u * blk : g == 1 ? osc1 + 4u * blk : kOut;
+                nl = uint32_t(pay_bytes(g) / 32);   // 16-byte pieces of this half
             }
         }
-        if (!has) po = io = so = 0;
-        q.p[0] = *reinterpret_cast<const uint4 *>(base + po);
 #pragma unroll
-        for (uint32_t j = 1; j < 8; ++j)
-            q.p[j] = j < nl ? *reinterpret_cast<const uint4 *>(base + (po + 16u * j)) : make_uint4(0, 0, 0, 0);
-        q.id2 = *reinterpret_cast<const uint32_t *>(base + io);
+        for (uint32_t j = 0; j < 8; ++j) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, j < nl ? po + 16u * j : kOut, 0, 0);
+            q.p[j] = make_uint4(v.x, v.y, v.z, v.w);
+        }
+        q.id2 = __builtin_amdgcn_raw_buffer_load_b32(rs, io, 0, 0);
         q.hi16 = blk & 1u;
-        q.sc = *reinterpret_cast<const float *>(base + so);
+        q.sc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, so, 0, 0));
+        q.f = int(f);
         return q;
     };
 
@@ -406,6 +417,7 @@ ht_status run_bwd_gemm(const ht_packed_weight *w, const float *dy, int64_t M, in
     a.KT = uint32_t((w->K + kBgBK - 1) / kBgBK);
     a.TPS = bg_tps(w, M);
     a.vec = (lddy % 4 == 0) ? 1u : 0u;
+    a.nbytes = uint32_t(w->bytes);
     const uint32_t S = bg_splits(w, M);
     a.dx = S > 1 ? nullptr : dx;
     a.partial = S > 1 ? static_cast<float *>(ws) : nullptr;

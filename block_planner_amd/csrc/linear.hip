@@ -343,7 +343,7 @@ extern "C" ht_status ht_linear_backward_workspace(const ht_packed_weight *w, int
     if (!bytes || !desc_ok(w)) return HT_EINVAL;
     if (M <= 0) return HT_ESHAPE;
     if (!bwd_ok(w)) return HT_EINVAL;
-    *bytes = M >= kBwdGemmMinM ? bwd_gemm_ws(w, M) : bwd_ws(w, M);
+    *bytes = bwd_gemm_takes(w, M) ? bwd_gemm_ws(w, M) : bwd_ws(w, M);
     return HT_OK;
 }
 
@@ -353,7 +353,7 @@ extern "C" ht_status ht_linear_backward_data(const ht_packed_weight *w, const fl
     if (!bwd_ok(w)) return HT_EINVAL;
     if (M <= 0 || lddy < w->N || lddx < w->K) return HT_ESHAPE;
     if (!al16(dy) || !al16(dx) || !al16(w->base)) return HT_EALIGN;
-    const bool mfma = M >= kBwdGemmMinM;
+    const bool mfma = bwd_gemm_takes(w, M);
     const size_t need = mfma ? bwd_gemm_ws(w, M) : bwd_ws(w, M);
     if (need && (!ws || ws_bytes < need)) return HT_ESMALL;
     if (ws && !al16(ws)) return HT_EALIGN;

@@ -88,8 +88,12 @@ ht_status run_bwd(const ht_packed_weight *w, const float *dy, int64_t M, int64_t
                   void *ws, hipStream_t s);
 
 // The input gradient on the matrix cores (row tile 16), for M >= 16 rows of
-// dY: its workspace bytes (per-split partial tiles) and one call.
+// dY and a packed buffer below 4 GiB (32-bit buffer offsets): whether it
+// takes the call, its workspace bytes (per-split partial tiles) and one call.
 constexpr int64_t kBwdGemmMinM = 16;
+inline bool bwd_gemm_takes(const ht_packed_weight *w, int64_t M) {
+    return M >= kBwdGemmMinM && w->bytes < 0xFFFFFF00ull;
+}
 size_t bwd_gemm_ws(const ht_packed_weight *w, int64_t M);
 ht_status run_bwd_gemm(const ht_packed_weight *w, const float *dy, int64_t M, int64_t lddy, float *dx,
                        int64_t lddx, void *ws, hipStream_t s);
