@@ -357,7 +357,7 @@ extern "C" ht_status ht_linear_backward_weight(const float *dy, int64_t M, int64
     if ((M > 0 && (lddy < N || ldx < K || ldx % 4)) || lddw < K || lddw % 4) return HT_ESHAPE;
     if (4 * ((N + kDwRows - 1) / kDwRows) > 65535) return HT_ESHAPE;
     if (!al16(dw) || (M > 0 && (!al16(dy) || !al16(x)))) return HT_EALIGN;
-    if (M >= kDwGemmMinM)
+    if (M >= kDwGemmMinM && K < (int64_t(1) << 30))   // x rows below 2 GiB: 32-bit buffer offsets
         return run_dw_gemm(dy, M, lddy, x, ldx, N, K, dw, lddw, accumulate ? 1 : 0,
                            reinterpret_cast<hipStream_t>(stream));
     const dim3 grid(uint32_t((K + kDwCols - 1) / kDwCols), 4u * uint32_t((N + kDwRows - 1) / kDwRows));

@@ -458,7 +458,8 @@ struct DgArgs {
     float *dw;
     int64_t lddw;
     uint32_t M, N, K, KT;
-    uint32_t vec;        // lddy % 2 == 0: dY read as float2
+    uint32_t nby, kby;   // bytes of a row of dY (4 N) and of x (2 K)
+    uint32_t vec;        // lddy and N even: dY read as float2 (a pair is all in or all out)
     int accumulate;
 };
 
@@ -477,33 +478,35 @@ __global__ __launch_bounds__(kDgThreads) void dw_gemm_kernel(DgArgs a) {
     const uint32_t lr = lane & 15, lq = lane >> 4;
 
     // thread -> columns 2 cp, 2 cp + 1 of the tile (cp = tid % 64; n for dY,
-    // k for x) and rows [16 rg, +16) of the step (rg = tid / 64): 16 loads of
+    // k for x) and rows [16 rg, +16) of the step (rg = the wave): 16 loads of
     // two adjacent columns each (a wave covers 512 / 256 contiguous bytes of
-    // a row), written per column as two 8-row runs (16-byte LDS writes)
-    const uint32_t cp = tid & 63u, rg = tid >> 6;
+    // a row), written per column as two 8-row runs (16-byte LDS writes).
+    // Each row is a buffer of its own (N fp32 of dY, K bf16 of x; none past
+    // M), so columns and rows out of range read zeros with no branch.
+    const uint32_t cp = lane, rg = c;
     struct Regs {
         float2 d[16];
         uint32_t xv[16];
     };
     auto load = [&](uint32_t t, Regs &R) {
-        const uint32_t n = n0 + 2u * cp, k = k0 + 2u * cp;
+        const uint32_t vn = 8u * cp, vk = 4u * cp;   // byte offsets of the lane's pair in its row
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const uint32_t m = 64u * t + 16u * rg + uint32_t(r);
-            float2 dv = make_float2(0.f, 0.f);
-            uint32_t xq = 0u;
-            if (m < a.M && t < nsteps) {
-                const float *p = a.dy + int64_t(m) * a.lddy + n;
-                if (a.vec && n + 1u < a.N) {
-                    dv = *reinterpret_cast<const float2 *>(p);
-                } else {
-                    dv.x = n < a.N ? p[0] : 0.f;
-                    dv.y = n + 1u < a.N ? p[1] : 0.f;
-                }
-                if (k < a.K) xq = *reinterpret_cast<const uint32_t *>(a.x + int64_t(m) * a.ldx + k);   // K % 4 == 0
+            const bool in = m < a.M;
+            const int64_t mr = in ? int64_t(m) : 0;
+            const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(a.dy + mr * a.lddy + n0), 0, in ? int(a.nby - 4u * n0) : 0, 0x00020000);
+            const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(a.x + mr * a.ldx + k0), 0, in ? int(a.kby - 2u * k0) : 0, 0x00020000);
+            if (a.vec) {
+                const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rd, vn, 0, 0);
+                R.d[r] = make_float2(__uint_as_float(v.x), __uint_as_float(v.y));
+            } else {
+                R.d[r] = make_float2(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, vn, 0, 0)),
+                                     __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, vn + 4u, 0, 0)));
             }
-            R.d[r] = dv;
-            R.xv[r] = xq;
+            R.xv[r] = __builtin_amdgcn_raw_buffer_load_b32(rx, vk, 0, 0);   // K % 4 == 0: a pair is all in or all out
         }
     };
     auto store = [&](const Regs &R, DgStage &s) {
@@ -609,7 +612,9 @@ ht_status run_dw_gemm(const float *dy, int64_t M, int64_t lddy, const uint16_t *
     a.N = uint32_t(N);
     a.K = uint32_t(K);
     a.KT = uint32_t((K + kDgTile - 1) / kDgTile);
-    a.vec = (lddy % 2 == 0) ? 1u : 0u;
+    a.nby = uint32_t(4 * N);
+    a.kby = uint32_t(2 * K);
+    a.vec = (lddy % 2 == 0 && N % 2 == 0) ? 1u : 0u;
     a.accumulate = accumulate;
     const uint64_t grid = uint64_t((N + kDgTile - 1) / kDgTile) * a.KT;
     if (grid > 0x7FFFFFFFull) return HT_ESHAPE;

@@ -146,10 +146,12 @@ def _dw_case(M, N, K, seed, lddy=None, ldx=None):
     return dy, xb
 
 
-@pytest.mark.parametrize("M,N,K", [(63, 64, 64), (64, 200, 192), (100, 130, 1028), (257, 300, 512)])
+@pytest.mark.parametrize("M,N,K", [(63, 64, 64), (64, 200, 192), (100, 130, 1028), (257, 300, 512),
+                                   (65, 129, 132), (130, 77, 256)])
 def test_weight_grad_mfma_matches_oracle(orc, M, N, K):
     """Ragged M (steps of 64 rows), N and K (tiles of 128), K not a multiple
-    of 128; 63 rows (the vector path) beside 64 and more."""
+    of 128; 63 rows (the vector path) beside 64 and more; odd N (dY read one
+    float at a time, the last column alone)."""
     dy, xb = _dw_case(M, N, K, 270 + M)
     dw = torch.full((N, K), float("nan"), device=dev())
     B.ht_linear_backward_weight(gpu(dy), gpu(xb.view(np.int16)), dw)
