@@ -30,6 +30,7 @@ namespace ht {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr uint32_t kBgBK = 128;          // dX columns per workgroup (two K-blocks)
 constexpr uint32_t kBgThreads = 512;     // 4 MFMA waves + 4 producer waves

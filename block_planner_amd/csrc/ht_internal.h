@@ -49,7 +49,6 @@ __host__ __device__ inline uint32_t fastdiv(uint32_t n, FastDiv f) {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Streaming 16-byte loads: the data is read once, so hint the caches not to
 // keep it (nontemporal).
