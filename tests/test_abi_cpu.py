@@ -263,6 +263,28 @@ def test_backward_argument_checks():
     assert f(ctypes.byref(d), None, 3, 256, dx, 512, None, 0, None) == 1
 
 
+def test_packed_buffers_stay_below_4gib():
+    """The kernels address the packed buffer with 32-bit offsets (buffer
+    loads, whose out-of-range offset reads zeros), so the layout refuses a
+    buffer of 4 GiB or more: a 65536 x 65536 all-INT8 weight (about 4.8 GB
+    packed) is refused by every entry point that takes a descriptor, while
+    32768 x 65536 (2.4 GB) is accepted and a 4096 x 4096 weight at 2048
+    rows takes the matrix-core input gradient (no split, no workspace) and
+    the two-pass GEMM (33 KiB records per 128 x 64 weight tile)."""
+    lib = B.load()
+    big = _desc(N=65536, K=65536)
+    assert big.bytes >= 1 << 32
+    out = ctypes.c_size_t(7)
+    assert lib.ht_linear_backward_workspace(ctypes.byref(big), 2048, ctypes.byref(out)) == 1
+    with pytest.raises(B.HTError):
+        B.ht_linear_workspace(big, 2048, B.HT_PATH_GEMM)
+    assert lib.ht_linear_backward_workspace(ctypes.byref(_desc(N=32768, K=65536)), 1, ctypes.byref(out)) == 0
+    small = _desc(N=4096, K=4096)
+    assert lib.ht_linear_backward_workspace(ctypes.byref(small), 2048, ctypes.byref(out)) == 0
+    assert out.value == 0
+    assert B.ht_linear_workspace(small, 2048, B.HT_PATH_GEMM) == 32 * 64 * 33 * 1024
+
+
 def test_backward_weight_argument_checks():
     """Argument checks of ht_linear_backward_weight (return before any GPU
     call): 1 EINVAL, 2 ESHAPE, 3 EALIGN."""
